@@ -1,0 +1,221 @@
+"""Benchmark of the TurboQuant packed-key attention hot path on one MI355X.
+
+Default workload (one decode step at 32K context): batch 32 x 8 KV heads x
+32768 tokens x d=128 bf16 keys with 4 outlier channels per head (x10), 32 query
+heads (GQA group 4), 3-bit TurboQuant (2-bit Lloyd-Max codes + 1-bit QJL).
+The packed cache for tokens 0..T-2 is built before timing; one step then
+  1. quantizes the new token's key of every (batch, KV head) stream straight
+     into cache slot T-1 (tq_quantize, record stride T),
+  2. scores all T packed keys against the fp32 queries (tq_scores),
+  3. takes the fp32 softmax of logits / sqrt(d) over the T tokens (tq_softmax).
+The metric is logits per second over the whole step; the scores call is timed
+separately with HIP events on the launch stream for the roofline figure.
+
+Also reported (separate timed loops, not part of `value`): streaming quantize
+throughput on 2^20 anisotropic bf16 vectors at b = 2, 3, 4.
+
+Usage: python bench.py [--steps K] [--warmup W] [--bits 3] [--no-cpu] [--no-extra]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(bits, budget_s=12.0):
+    """Time the oracle's estimator on a bounded sample of the same workload."""
+    import oracle as O
+    from oblivious_kv_cache_amd import workloads as wl
+    d, T, qpg = 128, 32768, 4
+    p = O.make_params(d, bits, 0)
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        blas_threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    cores = len(os.sched_getaffinity(0))
+    # one (batch, KV head) stream of the workload, quantized by the oracle (untimed)
+    K, _ = wl.outlier_keys_np(1, 1, T, d, seed=2)
+    X = wl.bf16_round(K.reshape(T, d))
+    rec = O.quantize(p, X)
+    Q = wl.gaussian((qpg, d), 7, np.float64)
+    n_groups, elapsed = 0, 0.0
+    t0 = time.perf_counter()
+    while elapsed < budget_s:
+        O.scores(p, Q, rec["codes"], rec["signs"], rec["norms"], rec["rnorms"])
+        n_groups += 1
+        elapsed = time.perf_counter() - t0
+    logits = n_groups * qpg * T
+    return {"value": logits / elapsed, "unit": "logits/s", "cores": min(cores, blas_threads) or 1,
+            "kind": "oracle",
+            "sample": f"{n_groups} (batch, KV-head) streams x {T} tokens x {qpg} query heads "
+                      f"(fp64 NumPy oracle, {elapsed:.1f} s; host cores {cores}, BLAS threads {blas_threads})"}
+
+
+def cpu_quantize_baseline(bits, n=16384):
+    import oracle as O
+    from oblivious_kv_cache_amd import workloads as wl
+    p = O.make_params(128, bits, 0)
+    X = wl.bf16_round(wl.power_law(n, 128, seed=3))
+    t0 = time.perf_counter()
+    O.quantize(p, X)
+    return n / (time.perf_counter() - t0)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--bits", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is described in DESIGN.md but not run", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from oblivious_kv_cache_amd import binding as tq
+    from oblivious_kv_cache_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, Hkv, T, d, Hq = 32, 8, 32768, 128, 32
+    qpg, G = Hq // Hkv, B * Hkv
+    bits = args.bits
+
+    log(f"setup: keys [{B},{Hkv},{T},{d}] bf16, b={bits}")
+    ctx = tq.Context(d, bits, seed=0)
+    K, _ = wl.outlier_keys_torch(B, Hkv, T, d, seed=2, device=dev)
+    cache = ctx.empty_records(G * T, dev)
+    tq.tq_quantize(ctx, K.view(G * T, d), out=cache)          # prefill (untimed)
+    del K
+    new_k, _ = wl.outlier_keys_torch(B, Hkv, 1, d, seed=102, device=dev)
+    new_k = new_k.view(G, d)
+    slot = {k: v[T - 1:] for k, v in cache.items()}
+    q = wl.gaussian_torch((B, Hq, d), 7, dev).view(G, qpg, d).contiguous()
+    logits = torch.empty((G, qpg, T), dtype=torch.float32, device=dev)
+    probs = torch.empty_like(logits)
+    ws = ctx.workspace(tq.TQ_OP_SCORES, G, qpg, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i=None):
+        tq.tq_quantize(ctx, new_k, out=slot, ldr=T)
+        if i is not None:
+            ev[i][0].record()
+        tq.tq_scores(ctx, q, cache, T=T, ldk=T, logits=logits, ws=ws)
+        if i is not None:
+            ev[i][1].record()
+        tq.tq_softmax(logits, scale, probs=probs)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1000.0 * wall / args.steps
+    score_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    n_logits = G * qpg * T
+    value = n_logits / (ms_step / 1000.0)
+
+    cb, sb = ctx.code_bytes, ctx.sign_bytes
+    key_bytes = G * T * (cb + sb + 8)
+    scores_bytes = key_bytes + n_logits * 4 + G * qpg * d * 4
+    achieved = scores_bytes / (score_ms / 1000.0) / 1e9
+    log(f"step {ms_step:.3f} ms; scores call {score_ms:.4f} ms = {achieved:.0f} GB/s algorithmic")
+
+    extra = {"scores_ms": score_ms, "scores_bytes_per_launch": scores_bytes,
+             "key_bytes_per_token": cb + sb + 8, "logits_per_step": n_logits}
+
+    if not args.no_extra:
+        log("quantize throughput: 2^20 x 128 bf16, power-law spectrum")
+        X = wl.power_law_torch(1 << 20, d, seed=3, device=dev)
+        qz = {}
+        for b in (2, 3, 4):
+            c2 = tq.Context(d, b, seed=0)
+            out = c2.empty_records(1 << 20, dev)
+            for _ in range(3):
+                tq.tq_quantize(c2, X, out=out)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            reps = 10
+            for _ in range(reps):
+                tq.tq_quantize(c2, X, out=out)
+            e.record()
+            torch.cuda.synchronize()
+            ms = s.elapsed_time(e) / reps
+            vps = (1 << 20) / (ms / 1000.0)
+            alg_tflops = vps * 4 * d * d / 1e12
+            hw_tflops = vps * (2 + 3) * 2 * d * d / 1e12
+            io_gbs = (1 << 20) * (2 * d + c2.code_bytes + c2.sign_bytes + 8) / (ms / 1000.0) / 1e9
+            qz[f"b{b}"] = {"ms": ms, "vec_per_s": vps, "alg_tflops": alg_tflops,
+                           "alg_frac_bf16_peak": alg_tflops / BF16_PEAK_TFLOPS,
+                           "mfma_tflops_split": hw_tflops,
+                           "mfma_frac_bf16_peak": hw_tflops / BF16_PEAK_TFLOPS,
+                           "io_gbs": io_gbs}
+            log(f"  b={b}: {ms:.3f} ms, {vps:.3e} vec/s, alg {alg_tflops:.0f} TF/s, "
+                f"MFMA {hw_tflops:.0f} TF/s, io {io_gbs:.0f} GB/s")
+            c2.close()
+            del out
+        extra["quantize_2p20"] = qz
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline: oracle estimator on a bounded sample")
+        cpu = cpu_baseline(bits)
+        extra["cpu_oracle_quantize_vec_per_s"] = cpu_quantize_baseline(bits)
+
+    line = {
+        "metric": "packed-key attention logits/s (d=128, 3-bit, decode 32K)",
+        "value": value,
+        "unit": "logits/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8-mfma/f32",
+        "data": "synthetic",
+        "config": {"workload": f"decode step: batch {B} x {Hkv} KV heads x {T} tokens x d={d} bf16 "
+                               f"keys (4 outlier channels/head x10), {Hq} query heads (GQA 4), "
+                               f"b={bits}; append 1 token/stream + scores + softmax",
+                   "global_batch": B, "seq_len": T, "bits": bits, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "tq_scores (prep_kernel + scores_kernel)"},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+/*
+ * tq.h -- C ABI of the MI355X (gfx950) TurboQuant hot path.
+ *
+ * TurboQuant compresses KV-cache keys in two stages and scores them against an
+ * uncompressed query:
+ *   stage 1: keep the vector length, rotate the unit vector by a seeded random
+ *            orthogonal matrix Pi, code each rotated coordinate with a
+ *            Max-Lloyd scalar codebook built for N(0, 1/d)
+ *            (suzuke blog "turboquant-compressing-ai-consciousness",
+ *             section 技術上怎麼做到的, 第一步 and 第二步; xujun.org note 189244,
+ *             section 第一步：PolarQuant);
+ *   stage 2: project the stage-1 residual with a Gaussian JL matrix S and keep
+ *            one sign bit per row (xujun.org note 189244, section 第二步：QJL;
+ *            hao.cnyes.com "TurboQuant", heading 1 bit 掃尾);
+ *   score:   l = nu * (<Pi q, c[idx]> + alpha * gamma * <S q, 2 bits - 1>),
+ *            alpha = sqrt(pi/2) / m, which is unbiased in expectation
+ *            (xujun.org note 189244, 第二步：QJL; suzuke blog, 第三步).
+ * Nothing is calibrated on data: a context is fixed by (d, bits, seed) alone
+ * (xujun.org note 189244, 常见问题 -- data-oblivious).
+ *
+ * Conventions for every call:
+ *   - Returns TQ_OK (0) or a negative TQ_E* code.  Arguments are validated
+ *     before anything is launched; on an error no output is touched.
+ *     Asynchronous kernel faults surface at the caller's next synchronisation
+ *     of `stream`.  No call aborts the process or throws across the ABI.
+ *   - Array pointers marked [device] are device memory owned by the caller;
+ *     base pointers must be 16-byte aligned.  The library keeps no pointer
+ *     after a call returns.  A context owns its device constants until
+ *     tq_free().  A context is immutable after init, so concurrent calls on
+ *     different streams are safe.
+ *   - Compute calls are stream-ordered and asynchronous on `stream` (NULL =
+ *     the default stream of the current device), and never allocate: calls
+ *     that need scratch memory take a caller workspace sized by
+ *     tq_workspace_size().
+ *
+ * Packed record layout (structure-of-arrays, one record per vector):
+ *   codes [n][code_bytes]  code i of a vector sits in bits [i*w, (i+1)*w) of its
+ *                          record, little-endian, LSB first; code k selects the
+ *                          k-th smallest centroid;
+ *   signs [n][sign_bytes]  sign bit j is bit (j & 7) of byte (j >> 3); 1 = +1
+ *                          (prod mode only);
+ *   norms [n]   float32    nu = |x|_2;
+ *   rnorms[n]   float32    gamma = |stage-1 residual of x/nu|_2 (prod only).
+ *   code_bytes = roundup16(ceil(d*w/8)), sign_bytes = roundup16(ceil(m/8)),
+ *   padding bytes are zero.  A zero vector is stored as zero codes, zero signs,
+ *   nu = 0, gamma = 0.  Appending = writing at a record offset.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TQ_OK        0
+#define TQ_EINVAL   (-1)   /* bad dimension, bit width, size, pointer, alignment or mode */
+#define TQ_ENOTSUP  (-2)   /* valid request this build does not implement */
+#define TQ_ENOMEM   (-3)   /* host or device allocation failed (init only) */
+#define TQ_EHIP     (-4)   /* a HIP runtime call or kernel launch failed */
+
+/* input element types for tq_quantize */
+#define TQ_F32   0
+#define TQ_BF16  1
+
+/* modes */
+#define TQ_MODE_PROD 0     /* (bits-1)-bit codes + 1-bit QJL sketch, m = d */
+#define TQ_MODE_MSE  1     /* bits-bit codes only (no sketch)              */
+
+/* ops for tq_workspace_size */
+#define TQ_OP_SCORES  1
+#define TQ_OP_ATTEND  2
+#define TQ_OP_TOPK    3
+
+/* limits of this build */
+#define TQ_MAX_D       256   /* d in [8, 256], d % 8 == 0 */
+#define TQ_MAX_TOPK    64
+
+typedef struct tq_ctx tq_ctx;
+
+typedef struct {
+  int d;           /* vector dimension                                  */
+  int m;           /* JL rows (= d in prod mode, 0 in mse mode)         */
+  int bits;        /* total bits per coordinate requested at init       */
+  int code_bits;   /* w: bits per scalar code (bits-1 prod, bits mse)   */
+  int levels;      /* 2^w codebook entries                              */
+  int code_bytes;  /* bytes per code record                             */
+  int sign_bytes;  /* bytes per sign record (0 in mse mode)             */
+  int mode;        /* TQ_MODE_PROD or TQ_MODE_MSE                       */
+} tq_layout_t;
+
+/* Build a prod-mode context: Pi = Haar(d) as Q diag(sign R_ii) of the QR
+ * factorisation of a d x d Gaussian matrix (SplitMix64 sub-stream 0 + Box-
+ * Muller), S = m x d Gaussian (sub-stream 1), m = d, and the Lloyd-Max codebook
+ * with 2^(bits-1) levels for N(0, 1/d) (suzuke blog, 第一步/第二步; xujun.org
+ * note 189244, 第二步：QJL).  d in [8, TQ_MAX_D] with d % 8 == 0; bits in
+ * {2,3,4}.  Synchronous; uploads constants to the current device.  *out is
+ * written only on success. */
+int tq_init(int d, int bits, uint64_t seed, tq_ctx **out);
+
+/* Same, MSE-only mode: 2^bits levels, no sketch; bits in {1,2,3,4}. */
+int tq_init_mse(int d, int bits, uint64_t seed, tq_ctx **out);
+
+/* Release a context (NULL is a no-op). */
+void tq_free(tq_ctx *ctx);
+
+/* Record sizes and code parameters of a context. */
+int tq_layout(const tq_ctx *ctx, tq_layout_t *out);
+
+/* Host-only: compute the float64 parameters a context would hold, without a
+ * GPU.  Pi [d*d] row-major, S [m*d] row-major (prod mode), c [2^w] ascending
+ * centroids, t [2^w - 1] ascending thresholds (already scaled by 1/sqrt(d)).
+ * Any output pointer may be NULL.  mode = TQ_MODE_PROD or TQ_MODE_MSE. */
+int tq_host_params(int d, int bits, uint64_t seed, int mode,
+                   double *Pi, double *S, double *c, double *t);
+
+/* Host copies of a context's float64 parameters (any pointer may be NULL). */
+int tq_get_params(const tq_ctx *ctx, double *Pi, double *S, double *c, double *t);
+
+/* Quantize n vectors (online append: any n >= 0).
+ *   x      [device] n rows of d elements, row stride ldx elements (ldx >= d;
+ *          ldx % 8 == 0 for TQ_BF16, ldx % 4 == 0 for TQ_F32);
+ *   dtype  TQ_F32 or TQ_BF16;
+ *   ldr    record stride (>= 1): vector i is written to record i * ldr, so a
+ *          decode step can append one token to each of n caches laid out
+ *          [n][ldr] by passing the record pointers of slot t;
+ *   codes  [device] records of code_bytes;  signs [device] records of
+ *          sign_bytes (prod), must be NULL in mse mode;  norms [device]
+ *          floats;  rnorms [device] floats (prod), NULL in mse mode.
+ * Steps per vector: nu = |x|; y = Pi x / nu; idx_i = #{k : t_k < y_i};
+ * r = y - c[idx]; gamma = |r|; bit_j = [ (S Pi^T r)_j >= 0 ]
+ * (xujun.org note 189244, 第一步 and 第二步; suzuke blog, 第二步 and 第三步). */
+int tq_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t ldx,
+                int64_t ldr, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
+                hipStream_t stream);
+
+/* Workspace bytes needed by an op:
+ *   TQ_OP_SCORES: a = G, b = qpg;  TQ_OP_ATTEND: a = G, b = qpg, c = T;
+ *   TQ_OP_TOPK:   a = nq, b = n, c = k. */
+int tq_workspace_size(const tq_ctx *ctx, int op, int64_t a, int64_t b, int64_t c,
+                      size_t *bytes);
+
+/* Asymmetric estimator (hao.cnyes.com "TurboQuant", 1 bit 掃尾: uncompressed
+ * query against compressed keys; suzuke blog, 第三步: approximation + residual
+ * correction).  GQA: G key groups, qpg query heads per group.
+ *   q      [device] float [G][qpg][d];
+ *   keys   records [G][ldk] (group g, token t at record g*ldk + t), t < T;
+ *   logits [device] float [G][qpg][T]: raw inner-product estimates (no
+ *          1/sqrt(d) scaling);
+ *   ws     [device] >= tq_workspace_size(TQ_OP_SCORES, G, qpg) bytes.
+ * Requires a prod-mode context; T >= 0, ldk >= T, 1 <= qpg <= 64. */
+int tq_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,
+              const uint8_t *codes, const uint8_t *signs, const float *norms,
+              const float *rnorms, float *logits, void *ws, size_t ws_bytes,
+              hipStream_t stream);
+
+/* Row softmax of scale * logits: probs[r][t] = exp(s l - max_r) / sum.
+ * logits, probs [device] float [rows][T]; probs == logits is allowed. */
+int tq_softmax(const float *logits, int64_t rows, int64_t T, float scale, float *probs,
+               hipStream_t stream);
+
+/* One fused decode-attention step over a packed KV cache: keys in a prod-mode
+ * context kctx, values in an MSE-mode context vctx with the same d
+ * (xujun.org note 189244, KV 缓存: both K and V are cached).
+ *   out[g][h] = sum_t softmax_t(scale * l[g][h][t]) * vhat[g][t],
+ *   vhat = nu_v Pi_v^T c_v[idx_v]  (computed in Pi_v coordinates, rotated
+ *   back once per head).
+ *   q [device] float [G][qpg][d]; key records [G][ldk]; value records [G][ldk];
+ *   logits, probs: optional [device] float [G][qpg][T] outputs (NULL = skip);
+ *   out [device] float [G][qpg][d];
+ *   ws [device] >= tq_workspace_size(TQ_OP_ATTEND, G, qpg, T). */
+int tq_attend(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G, int qpg,
+              int64_t T, int64_t ldk,
+              const uint8_t *kcodes, const uint8_t *ksigns, const float *knorms,
+              const float *krnorms, const uint8_t *vcodes, const float *vnorms,
+              float scale, float *logits, float *probs, float *out,
+              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Reconstruct n vectors: prod x_hat = nu (Pi^T c[idx] + alpha gamma S^T (2 bits - 1)),
+ * mse x_hat = nu Pi^T c[idx] (suzuke blog, 第三步).  out [device] float [n][d].
+ * signs/rnorms are ignored (may be NULL) in mse mode. */
+int tq_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs,
+               const float *norms, const float *rnorms, int64_t n, float *out,
+               hipStream_t stream);
+
+/* Inner-product top-k search over n packed database vectors (xujun.org note
+ * 189244, 常见问题: vector search, recall 1@k).
+ *   q [device] float [nq][d]; database records [n];
+ *   ids [device] int64 [nq][k], scores [device] float [nq][k], ordered by
+ *   (score descending, id ascending);  1 <= k <= min(n, TQ_MAX_TOPK);
+ *   ws [device] >= tq_workspace_size(TQ_OP_TOPK, nq, n, k). */
+int tq_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n,
+            const uint8_t *codes, const uint8_t *signs, const float *norms,
+            const float *rnorms, int k, int64_t *ids, float *scores,
+            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static string for a status code. */
+const char *tq_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

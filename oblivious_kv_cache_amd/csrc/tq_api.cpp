@@ -1,0 +1,346 @@
+// C ABI entry points: argument validation, context construction and upload.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "tq_internal.h"
+
+namespace {
+
+using tq::Frag;
+
+uint16_t bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)(u >> 16);   // inf / nan
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+float bf16_to_f(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// hi/lo bf16 split of a float64 value: hi = bf16(x), lo = bf16(x - hi).
+void split_bf16(double x, uint16_t &hi, uint16_t &lo) {
+  hi = bf16_rne((float)x);
+  lo = bf16_rne((float)(x - (double)bf16_to_f(hi)));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int current_device_matches(const tq_ctx *ctx) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TQ_EHIP;
+  return dev == ctx->device ? TQ_OK : TQ_EINVAL;
+}
+
+// Operand fragments of the quantize kernel (see tq_quantize.hip).  For output
+// tile u, k-block k, lane l (row r = l % 16, k-group g = l / 16), element e:
+//   GEMM 1: A = Pi[sigma(u, r)][32 k + 8 g + e]
+//   GEMM 2: A = S'[sigma(u, r)][g * P + 8 k + e]      (S' = S Pi^T, P = dpad/4)
+// with the row permutation sigma(u, r) = (r / 4) * P + 4 u + (r % 4), which
+// hands lane group g the coordinates [g P, (g+1) P).
+void build_frags(const tq::HostParams &hp, int dpad, const double *M, int rows, int cols,
+                 bool gemm2, Frag *hi, Frag *lo) {
+  const int NT = dpad / 16, NK = dpad / 32, P = dpad / 4;
+  for (int u = 0; u < NT; ++u)
+    for (int k = 0; k < NK; ++k)
+      for (int l = 0; l < 64; ++l) {
+        const int r = l % 16, g = l / 16;
+        const int row = (r / 4) * P + 4 * u + (r % 4);
+        uint16_t h8[8], l8[8];
+        for (int e = 0; e < 8; ++e) {
+          const int c = gemm2 ? g * P + 8 * k + e : 32 * k + 8 * g + e;
+          double v = 0.0;
+          if (row < rows && c < cols) v = M[(size_t)row * cols + c];
+          split_bf16(v, h8[e], l8[e]);
+        }
+        Frag fh, fl;
+        for (int i = 0; i < 4; ++i) {
+          fh.v[i] = (uint32_t)h8[2 * i] | ((uint32_t)h8[2 * i + 1] << 16);
+          fl.v[i] = (uint32_t)l8[2 * i] | ((uint32_t)l8[2 * i + 1] << 16);
+        }
+        const size_t idx = ((size_t)u * NK + k) * 64 + l;
+        hi[idx] = fh;
+        lo[idx] = fl;
+      }
+  (void)hp;
+}
+
+int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
+  if (!out) return TQ_EINVAL;
+  tq_ctx *ctx = new (std::nothrow) tq_ctx;
+  if (!ctx) return TQ_ENOMEM;
+  int st = tq::build_host_params(d, bits, seed, mode, ctx->hp);
+  if (st != TQ_OK) {
+    delete ctx;
+    return st;
+  }
+  const tq::HostParams &hp = ctx->hp;
+  const int m = hp.m, w = hp.w, L = hp.levels;
+  ctx->dpad = d <= 32 ? 32 : d <= 64 ? 64 : d <= 128 ? 128 : 256;
+  ctx->code_bytes = ((d * w + 7) / 8 + 15) / 16 * 16;
+  ctx->sign_bytes = m ? ((m + 7) / 8 + 15) / 16 * 16 : 0;
+  ctx->alpha = m ? (float)(std::sqrt(M_PI / 2.0) / m) : 0.f;
+  for (int k = 0; k < L; ++k) ctx->cf[k] = (float)hp.c[k];
+  for (int j = 0; j < L / 2; ++j) ctx->cpos[j] = (float)hp.c[L / 2 + j];
+  for (int j = 0; j + 1 < L / 2; ++j) ctx->tpos[j] = (float)hp.t[L / 2 + j];
+  // odd multilinear coefficients of the antisymmetric codebook in the sign
+  // variables s_p = 2 bit_p - 1 (p = 0..w-1) and, for w = 3, s0 s1 s2
+  for (int p = 0; p < 4; ++p) {
+    double acc = 0.0;
+    for (int idx = 0; idx < L; ++idx) {
+      double s;
+      if (p < w && p < 3) {
+        s = ((idx >> p) & 1) ? 1.0 : -1.0;
+      } else if (p == 3 && w == 3) {
+        s = 1.0;
+        for (int b = 0; b < 3; ++b) s *= ((idx >> b) & 1) ? 1.0 : -1.0;
+      } else {
+        s = 0.0;
+      }
+      acc += hp.c[idx] * s;
+    }
+    ctx->basis[p] = (float)(acc / L);
+  }
+
+  if (hipGetDevice(&ctx->device) != hipSuccess) {
+    delete ctx;
+    return TQ_EHIP;
+  }
+  const int dpad = ctx->dpad;
+  const size_t nfr = (size_t)(dpad / 16) * (dpad / 32) * 64;
+  const size_t bytes_f32 = sizeof(float) * ((size_t)2 * d * d + (size_t)2 * m * d);
+  const size_t bytes_fr = sizeof(Frag) * nfr * (m ? 4 : 2);
+  const size_t total = (bytes_f32 + 255) / 256 * 256 + bytes_fr;
+  std::vector<uint8_t> host(total, 0);
+  float *Pi32 = reinterpret_cast<float *>(host.data());
+  float *PiT32 = Pi32 + (size_t)d * d;
+  float *S32 = PiT32 + (size_t)d * d;
+  float *ST32 = S32 + (size_t)m * d;
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      Pi32[(size_t)i * d + j] = (float)hp.Pi[(size_t)i * d + j];
+      PiT32[(size_t)j * d + i] = (float)hp.Pi[(size_t)i * d + j];
+    }
+  for (int i = 0; i < m; ++i)
+    for (int j = 0; j < d; ++j) {
+      S32[(size_t)i * d + j] = (float)hp.S[(size_t)i * d + j];
+      ST32[(size_t)j * m + i] = (float)hp.S[(size_t)i * d + j];
+    }
+  Frag *fr = reinterpret_cast<Frag *>(host.data() + (bytes_f32 + 255) / 256 * 256);
+  build_frags(hp, dpad, hp.Pi.data(), d, d, false, fr, fr + nfr);
+  if (m) {
+    std::vector<double> Sp((size_t)m * d, 0.0);   // S' = S Pi^T
+    for (int i = 0; i < m; ++i)
+      for (int k = 0; k < d; ++k) {
+        double acc = 0.0;
+        for (int j = 0; j < d; ++j) acc += hp.S[(size_t)i * d + j] * hp.Pi[(size_t)k * d + j];
+        Sp[(size_t)i * d + k] = acc;
+      }
+    build_frags(hp, dpad, Sp.data(), m, d, true, fr + 2 * nfr, fr + 3 * nfr);
+  }
+  if (hipMalloc(&ctx->dmem, total) != hipSuccess) {
+    (void)hipGetLastError();
+    delete ctx;
+    return TQ_ENOMEM;
+  }
+  if (hipMemcpy(ctx->dmem, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(ctx->dmem);
+    delete ctx;
+    return TQ_EHIP;
+  }
+  uint8_t *base = reinterpret_cast<uint8_t *>(ctx->dmem);
+  ctx->Pi32 = reinterpret_cast<float *>(base);
+  ctx->PiT32 = ctx->Pi32 + (size_t)d * d;
+  ctx->S32 = ctx->PiT32 + (size_t)d * d;
+  ctx->ST32 = ctx->S32 + (size_t)m * d;
+  Frag *dfr = reinterpret_cast<Frag *>(base + (bytes_f32 + 255) / 256 * 256);
+  ctx->PiA_hi = dfr;
+  ctx->PiA_lo = dfr + nfr;
+  if (m) {
+    ctx->S2A_hi = dfr + 2 * nfr;
+    ctx->S2A_lo = dfr + 3 * nfr;
+  }
+  *out = ctx;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_init(int d, int bits, uint64_t seed, tq_ctx **out) {
+  return make_ctx(d, bits, seed, TQ_MODE_PROD, out);
+}
+
+int tq_init_mse(int d, int bits, uint64_t seed, tq_ctx **out) {
+  return make_ctx(d, bits, seed, TQ_MODE_MSE, out);
+}
+
+void tq_free(tq_ctx *ctx) {
+  if (!ctx) return;
+  if (ctx->dmem) (void)hipFree(ctx->dmem);
+  delete ctx;
+}
+
+int tq_layout(const tq_ctx *ctx, tq_layout_t *out) {
+  if (!ctx || !out) return TQ_EINVAL;
+  out->d = ctx->hp.d;
+  out->m = ctx->hp.m;
+  out->bits = ctx->hp.bits;
+  out->code_bits = ctx->hp.w;
+  out->levels = ctx->hp.levels;
+  out->code_bytes = ctx->code_bytes;
+  out->sign_bytes = ctx->sign_bytes;
+  out->mode = ctx->hp.mode;
+  return TQ_OK;
+}
+
+int tq_get_params(const tq_ctx *ctx, double *Pi, double *S, double *c, double *t) {
+  if (!ctx) return TQ_EINVAL;
+  const tq::HostParams &hp = ctx->hp;
+  if (Pi) std::memcpy(Pi, hp.Pi.data(), hp.Pi.size() * sizeof(double));
+  if (S && hp.m) std::memcpy(S, hp.S.data(), hp.S.size() * sizeof(double));
+  if (c) std::memcpy(c, hp.c.data(), hp.c.size() * sizeof(double));
+  if (t) std::memcpy(t, hp.t.data(), hp.t.size() * sizeof(double));
+  return TQ_OK;
+}
+
+int tq_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t ldx,
+                int64_t ldr, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
+                hipStream_t stream) {
+  if (!ctx || n < 0 || ldr < 1) return TQ_EINVAL;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EINVAL;
+  const bool prod = ctx->hp.mode == TQ_MODE_PROD;
+  if (n == 0) return TQ_OK;
+  if (!x || !codes || !norms) return TQ_EINVAL;
+  if (prod ? (!signs || !rnorms) : (signs || rnorms)) return TQ_EINVAL;
+  if (ldx < ctx->hp.d) return TQ_EINVAL;
+  if (dtype == TQ_BF16 ? (ldx % 8) : (ldx % 4)) return TQ_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || (signs && !aligned(signs, 16)) ||
+      !aligned(norms, 4) || (rnorms && !aligned(rnorms, 4)))
+    return TQ_EINVAL;
+  const int st = current_device_matches(ctx);
+  if (st != TQ_OK) return st;
+  return tq::launch_quantize(ctx, x, dtype, n, ldx, ldr, codes, signs, norms, rnorms, stream);
+}
+
+int tq_workspace_size(const tq_ctx *ctx, int op, int64_t a, int64_t b, int64_t c, size_t *bytes) {
+  if (!ctx || !bytes || a < 0 || b < 0 || c < 0) return TQ_EINVAL;
+  switch (op) {
+    case TQ_OP_SCORES:
+      if (ctx->hp.mode != TQ_MODE_PROD || b < 1 || b > 64) return TQ_EINVAL;
+      *bytes = tq::scores_ws_bytes(ctx, a, (int)b);
+      return TQ_OK;
+    case TQ_OP_ATTEND:
+      if (ctx->hp.mode != TQ_MODE_PROD || b < 1 || b > 64) return TQ_EINVAL;
+      *bytes = tq::attend_ws_bytes(ctx, a, (int)b, c);
+      return TQ_OK;
+    case TQ_OP_TOPK:
+      if (ctx->hp.mode != TQ_MODE_PROD || c < 1 || c > TQ_MAX_TOPK) return TQ_EINVAL;
+      *bytes = tq::topk_ws_bytes(ctx, a, b, (int)c);
+      return TQ_OK;
+    default:
+      return TQ_EINVAL;
+  }
+}
+
+int tq_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,
+              const uint8_t *codes, const uint8_t *signs, const float *norms,
+              const float *rnorms, float *logits, void *ws, size_t ws_bytes,
+              hipStream_t stream) {
+  if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
+  if (G < 0 || T < 0 || ldk < T || qpg < 1 || qpg > 64) return TQ_EINVAL;
+  if (G == 0 || T == 0) return TQ_OK;
+  if (!q || !codes || !signs || !norms || !rnorms || !logits || !ws) return TQ_EINVAL;
+  if (!aligned(codes, 16) || !aligned(signs, 16) || !aligned(norms, 4) || !aligned(rnorms, 4) ||
+      !aligned(q, 4) || !aligned(logits, 4) || !aligned(ws, 16))
+    return TQ_EINVAL;
+  if (ws_bytes < tq::scores_ws_bytes(ctx, G, qpg)) return TQ_EINVAL;
+  const int st = current_device_matches(ctx);
+  if (st != TQ_OK) return st;
+  return tq::launch_scores(ctx, q, G, qpg, T, ldk, codes, signs, norms, rnorms, logits, ws, stream);
+}
+
+int tq_softmax(const float *logits, int64_t rows, int64_t T, float scale, float *probs,
+               hipStream_t stream) {
+  if (rows < 0 || T < 0) return TQ_EINVAL;
+  if (rows == 0 || T == 0) return TQ_OK;
+  if (!logits || !probs || !aligned(logits, 4) || !aligned(probs, 4)) return TQ_EINVAL;
+  if (!std::isfinite(scale)) return TQ_EINVAL;
+  return tq::launch_softmax(logits, rows, T, scale, probs, stream);
+}
+
+int tq_attend(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G, int qpg,
+              int64_t T, int64_t ldk, const uint8_t *kcodes, const uint8_t *ksigns,
+              const float *knorms, const float *krnorms, const uint8_t *vcodes,
+              const float *vnorms, float scale, float *logits, float *probs, float *out,
+              void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!kctx || !vctx || kctx->hp.mode != TQ_MODE_PROD || vctx->hp.mode != TQ_MODE_MSE)
+    return TQ_EINVAL;
+  if (kctx->hp.d != vctx->hp.d) return TQ_EINVAL;
+  if (G < 0 || T < 1 || ldk < T || qpg < 1 || qpg > 64) return TQ_EINVAL;
+  if (G == 0) return TQ_OK;
+  if (!q || !kcodes || !ksigns || !knorms || !krnorms || !vcodes || !vnorms || !out || !ws)
+    return TQ_EINVAL;
+  if (!aligned(kcodes, 16) || !aligned(ksigns, 16) || !aligned(vcodes, 16) || !aligned(ws, 16) ||
+      !aligned(knorms, 4) || !aligned(krnorms, 4) || !aligned(vnorms, 4) || !aligned(q, 4) ||
+      !aligned(out, 4) || (logits && !aligned(logits, 4)) || (probs && !aligned(probs, 4)))
+    return TQ_EINVAL;
+  if (!std::isfinite(scale)) return TQ_EINVAL;
+  if (ws_bytes < tq::attend_ws_bytes(kctx, G, qpg, T)) return TQ_EINVAL;
+  const int st = current_device_matches(kctx);
+  if (st != TQ_OK) return st;
+  if (vctx->device != kctx->device) return TQ_EINVAL;
+  return tq::launch_attend(kctx, vctx, q, G, qpg, T, ldk, kcodes, ksigns, knorms, krnorms, vcodes,
+                           vnorms, scale, logits, probs, out, ws, stream);
+}
+
+int tq_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs, const float *norms,
+               const float *rnorms, int64_t n, float *out, hipStream_t stream) {
+  if (!ctx || n < 0) return TQ_EINVAL;
+  if (n == 0) return TQ_OK;
+  const bool prod = ctx->hp.mode == TQ_MODE_PROD;
+  if (!codes || !norms || !out || (prod && (!signs || !rnorms))) return TQ_EINVAL;
+  if (!aligned(codes, 16) || (prod && !aligned(signs, 16)) || !aligned(norms, 4) || !aligned(out, 4))
+    return TQ_EINVAL;
+  const int st = current_device_matches(ctx);
+  if (st != TQ_OK) return st;
+  return tq::launch_dequant(ctx, codes, prod ? signs : nullptr, norms, prod ? rnorms : nullptr, n,
+                            out, stream);
+}
+
+int tq_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const uint8_t *codes,
+            const uint8_t *signs, const float *norms, const float *rnorms, int k, int64_t *ids,
+            float *scores, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
+  if (nq < 0 || n < 1 || k < 1 || k > TQ_MAX_TOPK || k > n) return TQ_EINVAL;
+  if (nq == 0) return TQ_OK;
+  if (!q || !codes || !signs || !norms || !rnorms || !ids || !scores || !ws) return TQ_EINVAL;
+  if (!aligned(codes, 16) || !aligned(signs, 16) || !aligned(ws, 16) || !aligned(ids, 8) ||
+      !aligned(scores, 4) || !aligned(q, 4) || !aligned(norms, 4) || !aligned(rnorms, 4))
+    return TQ_EINVAL;
+  if (ws_bytes < tq::topk_ws_bytes(ctx, nq, n, k)) return TQ_EINVAL;
+  const int st = current_device_matches(ctx);
+  if (st != TQ_OK) return st;
+  return tq::launch_topk(ctx, q, nq, n, codes, signs, norms, rnorms, k, ids, scores, ws, stream);
+}
+
+const char *tq_strerror(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_EINVAL: return "invalid argument";
+    case TQ_ENOTSUP: return "not supported";
+    case TQ_ENOMEM: return "out of memory";
+    case TQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

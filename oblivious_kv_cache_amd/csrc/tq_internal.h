@@ -1,0 +1,82 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+struct HostParams {
+  int d = 0, m = 0, bits = 0, w = 0, levels = 0, mode = 0;
+  uint64_t seed = 0;
+  std::vector<double> Pi;  // [d][d] row-major
+  std::vector<double> S;   // [m][d] row-major
+  std::vector<double> c;   // [levels] ascending, for N(0, 1/d)
+  std::vector<double> t;   // [levels-1] ascending
+};
+
+int build_host_params(int d, int bits, uint64_t seed, int mode, HostParams &hp);
+void lloyd_max_unit_gaussian(int L, std::vector<double> &c, std::vector<double> &t);
+
+// 16-byte MFMA operand fragment (8 x bf16 or 16 x int8 per lane).
+struct alignas(16) Frag {
+  uint32_t v[4];
+};
+
+}  // namespace tq
+
+// The context.  Immutable after tq_init.
+struct tq_ctx {
+  tq::HostParams hp;
+  int device = 0;
+  int dpad = 0;        // d rounded up to the quantize kernel's tile (32/64/128/256)
+  int code_bytes = 0;
+  int sign_bytes = 0;
+  float alpha = 0.f;   // sqrt(pi/2) / m
+  float cpos[8] = {};  // positive centroids c_{L/2 + j}
+  float tpos[8] = {};  // positive thresholds t_{L/2 + j}
+  float cf[16] = {};   // all centroids, fp32
+  float basis[4] = {}; // odd-basis coefficients of the codebook (see tq_scores.hip)
+  // device constants (one allocation owned by the context)
+  void *dmem = nullptr;
+  float *Pi32 = nullptr;    // [d][d] row-major
+  float *PiT32 = nullptr;   // [d][d] = Pi^T row-major
+  float *S32 = nullptr;     // [m][d]
+  float *ST32 = nullptr;    // [d][m] = S^T
+  tq::Frag *PiA_hi = nullptr, *PiA_lo = nullptr;   // quantize GEMM-1 operand fragments
+  tq::Frag *S2A_hi = nullptr, *S2A_lo = nullptr;   // quantize GEMM-2 operand fragments
+};
+
+namespace tq {
+
+// kernel launchers (return TQ_OK / TQ_EHIP / TQ_ENOTSUP)
+int launch_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t ldx,
+                    int64_t ldr, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
+                    hipStream_t stream);
+size_t scores_ws_bytes(const tq_ctx *ctx, int64_t G, int qpg);
+int launch_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,
+                  const uint8_t *codes, const uint8_t *signs, const float *norms,
+                  const float *rnorms, float *logits, void *ws, hipStream_t stream);
+int launch_softmax(const float *logits, int64_t rows, int64_t T, float scale, float *probs,
+                   hipStream_t stream);
+int launch_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs,
+                   const float *norms, const float *rnorms, int64_t n, float *out,
+                   hipStream_t stream);
+size_t attend_ws_bytes(const tq_ctx *k, int64_t G, int qpg, int64_t T);
+int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G, int qpg,
+                  int64_t T, int64_t ldk, const uint8_t *kcodes, const uint8_t *ksigns,
+                  const float *knorms, const float *krnorms, const uint8_t *vcodes,
+                  const float *vnorms, float scale, float *logits, float *probs, float *out,
+                  void *ws, hipStream_t stream);
+size_t topk_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int k);
+int launch_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const uint8_t *codes,
+                const uint8_t *signs, const float *norms, const float *rnorms, int k,
+                int64_t *ids, float *scores, void *ws, hipStream_t stream);
+
+inline int hip_status() { return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP; }
+
+}  // namespace tq

@@ -47,6 +47,7 @@ from .quant import (
     unpack_bits,
     quantize_one,
     quantize,
+    stage2_from_codes,
     dequant,
 )
 from .estimate import (
@@ -64,6 +65,6 @@ __all__ = [
     "splitmix64_stream", "gaussian_stream", "haar_rotation", "jl_matrix",
     "lloyd_max_gaussian", "gaussian_distortion", "codebook", "TQParams",
     "make_params", "record_sizes", "pack_bits", "unpack_bits", "quantize_one",
-    "quantize", "dequant", "prep_query", "scores_one", "scores", "softmax",
+    "quantize", "stage2_from_codes", "dequant", "prep_query", "scores_one", "scores", "softmax",
     "attend", "topk", "exact_top1", "recall_at_k",
 ]

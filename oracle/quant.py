@@ -77,6 +77,23 @@ def quantize_one(p, x):
     return idx, bits, np.float32(nu), np.float32(gamma)
 
 
+def stage2_from_codes(p, x, idx):
+    """Residual norm and sign bits of one vector for a given stage-1 code choice.
+
+    Used where two stage-1 codes are both valid (a coordinate on a threshold
+    within rounding): the QJL stage is then evaluated for the given codes.
+    Returns (gamma float64, z [m] float64, bits [m] int).
+    """
+    x = np.asarray(x, np.float64)
+    nu = float(np.sqrt(np.sum(x * x)))
+    u = x / nu
+    y = p.Pi @ u
+    r = y - p.c[np.asarray(idx)]
+    gamma = float(np.sqrt(np.sum(r * r)))
+    z = p.S @ (u - p.Pi.T @ p.c[np.asarray(idx)])
+    return gamma, z, (z >= 0.0).astype(np.int64)
+
+
 def quantize(p, X, chunk=65536, return_unpacked=False):
     """Batched form of :func:`quantize_one` (same arithmetic, BLAS GEMMs).
 

@@ -1,0 +1,87 @@
+"""Comparison rules shared by the GPU parity tests.
+
+Acceptance (the precision contract of the hot path):
+  * codes and sign bits are bit-exact, except a code whose oracle coordinate
+    y_i lies within 1e-5 of a codebook threshold, or a sign whose oracle
+    sketch value |z_j| < 1e-5 (unit-vector scale); such boundary mismatches
+    must also stay below 1e-4 of all codes (signs counted separately);
+  * norms nu: within 1 float32 ulp of the float64 length;
+  * residual norms gamma (vectors whose codes all match): |diff| <= 2e-5 +
+    1e-5 * gamma (the GPU's rotated coordinates carry ~1e-6 absolute error per
+    coordinate, and |d gamma| <= |d y|_2);
+  * floating-point outputs (logits, probabilities, reconstructions):
+    |gpu - oracle| <= 1e-4 + 1e-3 * |oracle|, with the oracle evaluated on the
+    same inputs the GPU consumed (oracle-made records or generator data).
+"""
+
+import numpy as np
+
+import oracle as O
+
+BAND = 1e-5
+MAX_FRAC = 1e-4
+ATOL, RTOL = 1e-4, 1e-3
+
+
+def assert_close(got, want, atol=ATOL, rtol=RTOL, what="values"):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    excess = np.abs(got - want) - (atol + rtol * np.abs(want))
+    bad = excess > 0
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst excess "
+                           f"{excess.max():.3e} at {np.unravel_index(np.argmax(excess), excess.shape)}")
+
+
+def check_quantized(p, gpu, ref, X=None, allow_frac=MAX_FRAC):
+    """Compare GPU records with the oracle's (``ref`` from quantize(return_unpacked=True)).
+
+    A vector whose code differs inside the band has two valid encodings; its
+    sign bits and gamma are then checked against the oracle's stage-2 result
+    for the other valid code choice (needs the input rows ``X``).
+    """
+    g_idx = O.unpack_bits(gpu["codes"], p.w, p.d)
+    r_idx = ref["idx"]
+    assert np.array_equal(gpu["codes"].shape, ref["codes"].shape)
+    # norms: within one float32 ulp of the float64 length
+    gn, rn = gpu["norms"].astype(np.float32), ref["norms"].astype(np.float32)
+    assert (np.abs(gn.astype(np.float64) - rn) <= np.spacing(np.maximum(np.abs(rn), 1e-30))).all()
+    # codes
+    diff = g_idx != r_idx
+    if diff.any():
+        y = ref["y"][diff]
+        dist = np.min(np.abs(y[:, None] - p.t[None, :]), axis=1)
+        assert (dist < BAND).all(), f"code mismatch outside the band: min dist {dist.max():.3e}"
+        # the GPU's code must be the neighbour across that threshold
+        assert (np.abs(g_idx[diff] - r_idx[diff]) == 1).all()
+    assert diff.sum() <= allow_frac * diff.size, f"{diff.sum()} code mismatches of {diff.size}"
+    bits = np.unpackbits(gpu["codes"], axis=1, bitorder="little")
+    assert not bits[:, p.w * p.d:].any(), "nonzero code padding"
+    stats = {"code_mismatch": int(diff.sum())}
+    if p.mode == "prod":
+        g_s = O.unpack_bits(gpu["signs"], 1, p.m)
+        z_ref = ref["z"].copy()
+        s_ref = ref["sbits"].copy()
+        g_ref = ref["rnorms"].astype(np.float64).copy()
+        for v in np.nonzero(diff.any(axis=1))[0]:
+            assert X is not None, "input rows needed to check a vector with a boundary code"
+            alt = r_idx[v].copy()
+            alt[diff[v]] = g_idx[v][diff[v]]          # the other valid side of each tied coordinate
+            gam, z, sb = O.stage2_from_codes(p, X[v], alt)
+            z_ref[v], s_ref[v], g_ref[v] = z, sb, gam
+        sdiff = g_s != s_ref
+        if sdiff.any():
+            z = np.abs(z_ref[sdiff])
+            assert (z < BAND).all(), f"sign mismatch outside the band: |z| {z.max():.3e}"
+        assert sdiff.sum() <= allow_frac * sdiff.size, f"{sdiff.sum()} sign mismatches"
+        sb = np.unpackbits(gpu["signs"], axis=1, bitorder="little")
+        assert not sb[:, p.m:].any(), "nonzero sign padding"
+        stats["sign_mismatch"] = int(sdiff.sum())
+        gg = gpu["rnorms"].astype(np.float64)
+        assert (np.abs(gg - g_ref) <= 2e-5 + 1e-5 * g_ref).all(), np.abs(gg - g_ref).max()
+    zero = ref["norms"] == 0
+    if zero.any():
+        assert not gpu["codes"][zero].any()
+        if p.mode == "prod":
+            assert not gpu["signs"][zero].any() and (gpu["rnorms"][zero] == 0).all()
+    return stats

@@ -1,0 +1,175 @@
+"""GPU parity: tq_quantize (and tq_dequant) against the oracle."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oblivious_kv_cache_amd import workloads as wl
+from parity import assert_close, check_quantized
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from oblivious_kv_cache_amd import binding
+    return binding
+
+
+def _run(tq, d, bits, X, mode="prod", seed=0, dtype=torch.float32):
+    dev = torch.device("cuda")
+    ctx = tq.Context(d, bits, seed, tq.TQ_MODE_PROD if mode == "prod" else tq.TQ_MODE_MSE)
+    xt = torch.from_numpy(np.ascontiguousarray(X)).to(dev).to(dtype)
+    rec = tq.tq_quantize(ctx, xt)
+    torch.cuda.synchronize()
+    out = {k: (v.cpu().numpy() if v is not None else None) for k, v in rec.items()}
+    xin = xt.float().cpu().numpy()           # exactly what the GPU consumed
+    return ctx, out, xin
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_tiny_fp32_config(tq, bits):
+    # 4096 x 128 fp32 N(0,1) keys, seed 0 (the small oracle case), b = 2, 3, 4
+    K, _ = wl.tiny_case(seed=0)
+    print(f"quantize tiny fp32 n=4096 d=128 b={bits}", flush=True)
+    ctx, g, xin = _run(tq, 128, bits, K)
+    p = O.make_params(128, bits, 0)
+    st = check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
+    print(st)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_bf16_outlier_keys(tq, bits):
+    K, _ = wl.outlier_keys_np(1, 2, 1500, 128, seed=2)
+    X = wl.bf16_round(K.reshape(-1, 128))
+    print(f"quantize bf16 outlier keys n=3000 d=128 b={bits}", flush=True)
+    ctx, g, xin = _run(tq, 128, bits, X, dtype=torch.bfloat16)
+    assert np.array_equal(xin, X)
+    p = O.make_params(128, bits, 0)
+    check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_quantize_mse_mode(tq, bits):
+    X = wl.bf16_round(wl.gaussian((777, 128), 4))
+    print(f"quantize mse bf16 n=777 d=128 b={bits}", flush=True)
+    ctx, g, xin = _run(tq, 128, bits, X, mode="mse", seed=1, dtype=torch.bfloat16)
+    p = O.make_params(128, bits, 1, "mse")
+    check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
+    assert g["signs"] is None
+
+
+@pytest.mark.parametrize("d,bits,n", [(200, 2, 2000), (200, 4, 1500), (64, 3, 1001), (32, 2, 300),
+                                      (96, 4, 515), (8, 3, 100), (40, 2, 97), (256, 3, 700),
+                                      (136, 2, 333)])
+def test_quantize_dimensions(tq, d, bits, n):
+    X = wl.power_law(n, d, seed=5, unit=True)
+    print(f"quantize fp32 power-law n={n} d={d} b={bits}", flush=True)
+    ctx, g, xin = _run(tq, d, bits, X)
+    p = O.make_params(d, bits, 0)
+    check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
+
+
+def test_quantize_zero_rows_ragged_and_strided(tq):
+    dev = torch.device("cuda")
+    d, bits = 128, 3
+    X = wl.gaussian((45, 160), 9)           # row stride 160 > d
+    X[[0, 7, 44], :] = 0.0
+    ctx = tq.Context(d, bits, 0)
+    xt = torch.from_numpy(X).to(dev)[:, :d]
+    print("quantize strided ldx=160 n=45 with zero rows", flush=True)
+    rec = tq.tq_quantize(ctx, xt)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in rec.items()}
+    p = O.make_params(d, bits, 0)
+    check_quantized(p, g, O.quantize(p, X[:, :d], return_unpacked=True), X[:, :d])
+    assert (g["norms"][[0, 7, 44]] == 0).all()
+
+
+def test_quantize_append_at_offset_leaves_other_records(tq):
+    dev = torch.device("cuda")
+    d, bits = 128, 3
+    ctx = tq.Context(d, bits, 0)
+    big = ctx.empty_records(100, dev)
+    for v in big.values():
+        v.fill_(7)
+    X = wl.gaussian((5, d), 11)
+    view = {k: v[40:45] for k, v in big.items()}
+    print("quantize append 5 records at offset 40", flush=True)
+    tq.tq_quantize(ctx, torch.from_numpy(X).to(dev), out=view)
+    torch.cuda.synchronize()
+    for k, v in big.items():
+        a = v.cpu().numpy()
+        assert (a[:40] == 7).all() and (a[45:] == 7).all(), k
+    p = O.make_params(d, bits, 0)
+    g = {k: v[40:45].cpu().numpy() for k, v in big.items()}
+    check_quantized(p, g, O.quantize(p, X, return_unpacked=True), X)
+
+
+def test_quantize_empty_and_errors(tq):
+    dev = torch.device("cuda")
+    ctx = tq.Context(128, 3, 0)
+    rec = tq.tq_quantize(ctx, torch.zeros((0, 128), device=dev))
+    assert rec["codes"].shape == (0, 32)
+    with pytest.raises(tq.TQError):
+        tq.tq_quantize(ctx, torch.zeros((4, 130), device=dev)[:, :128])   # row stride 130: not 16-B aligned rows
+    mse = tq.Context(128, 3, 1, tq.TQ_MODE_MSE)
+    r = ctx.empty_records(4, dev)
+    import ctypes
+    st = tq.LIB.tq_quantize(mse.handle, ctypes.c_void_p(torch.zeros((4, 128), device=dev).data_ptr()),
+                            tq.TQ_F32, 4, 128, 1, ctypes.c_void_p(r["codes"].data_ptr()),
+                            ctypes.c_void_p(r["signs"].data_ptr()), ctypes.c_void_p(r["norms"].data_ptr()),
+                            ctypes.c_void_p(r["rnorms"].data_ptr()), None)
+    assert st == tq.TQ_EINVAL          # sketch buffers given to an MSE-only context
+
+
+def test_quantize_is_deterministic(tq):
+    X = wl.bf16_round(wl.gaussian((3000, 128), 12))
+    _, a, _ = _run(tq, 128, 3, X, dtype=torch.bfloat16)
+    _, b, _ = _run(tq, 128, 3, X, dtype=torch.bfloat16)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("mode,bits,d", [("prod", 3, 128), ("prod", 2, 200), ("mse", 3, 128),
+                                         ("prod", 4, 64)])
+def test_dequant_matches_oracle(tq, mode, bits, d):
+    dev = torch.device("cuda")
+    p = O.make_params(d, bits, 3, mode)
+    X = wl.gaussian((300, d), 13, np.float64)
+    ref = O.quantize(p, X)
+    ctx = tq.Context(d, bits, 3, tq.TQ_MODE_PROD if mode == "prod" else tq.TQ_MODE_MSE)
+    rec = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in ref.items()
+           if not (mode == "mse" and k in ("signs", "rnorms"))}
+    print(f"dequant {mode} b={bits} d={d}", flush=True)
+    out = tq.tq_dequant(ctx, rec).cpu().numpy()
+    want = O.dequant(p, ref["codes"], ref["signs"], ref["norms"], ref["rnorms"])
+    scale = np.linalg.norm(want, axis=1, keepdims=True)
+    assert (np.abs(out - want) <= 1e-5 * scale + 1e-6).all()
+
+
+def test_quantize_strided_records_decode_append(tq):
+    # one new token per stream written at slot t of caches laid out [G][T]
+    dev = torch.device("cuda")
+    d, bits, G, T, slot = 128, 3, 6, 50, 37
+    ctx = tq.Context(d, bits, 0)
+    cache = ctx.empty_records(G * T, dev)
+    for v in cache.values():
+        v.fill_(3)
+    X = wl.bf16_round(wl.gaussian((G, d), 31))
+    view = {k: v[slot:] for k, v in cache.items()}
+    tq.tq_quantize(ctx, torch.from_numpy(X).to(dev).to(torch.bfloat16), out=view, ldr=T)
+    torch.cuda.synchronize()
+    rows = [g * T + slot for g in range(G)]
+    host = {k: v.cpu().numpy() for k, v in cache.items()}
+    mask = np.ones(G * T, bool)
+    mask[rows] = False
+    for k, v in host.items():
+        assert (v[mask] == 3).all(), k
+    p = O.make_params(d, bits, 0)
+    g = {k: v[rows] for k, v in host.items()}
+    check_quantized(p, g, O.quantize(p, X, return_unpacked=True), X)

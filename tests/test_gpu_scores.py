@@ -1,0 +1,124 @@
+"""GPU parity: tq_scores and tq_softmax against the oracle.
+
+The GPU scores the oracle's own packed records (or generator-made random
+records), so both sides evaluate the estimator on identical inputs.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oblivious_kv_cache_amd import workloads as wl
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from oblivious_kv_cache_amd import binding
+    return binding
+
+
+def _dev(rec):
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in rec.items()}
+
+
+def _score(tq, ctx, Q, rec, G, T, ldk):
+    q = torch.from_numpy(np.ascontiguousarray(Q, dtype=np.float32)).cuda()
+    out = tq.tq_scores(ctx, q, _dev(rec), T=T, ldk=ldk)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _oracle_grouped(p, Q, rec, G, T, ldk):
+    out = np.zeros((G, Q.shape[1], T))
+    for g in range(G):
+        sl = slice(g * ldk, g * ldk + T)
+        out[g] = O.scores(p, Q[g].astype(np.float64), rec["codes"][sl], rec["signs"][sl],
+                          rec["norms"][sl], rec["rnorms"][sl])
+    return out
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_scores_tiny_config_on_oracle_records(tq, bits):
+    # 4096 keys, 16 fp32 queries, d=128: G=1, qpg=16 (4 head groups)
+    K, Q = wl.tiny_case(seed=0)
+    p = O.make_params(128, bits, 0)
+    rec = O.quantize(p, K)
+    ctx = tq.Context(128, bits, 0)
+    print(f"scores tiny b={bits} T=4096 qpg=16", flush=True)
+    got = _score(tq, ctx, Q[None], rec, 1, 4096, 4096)
+    want = O.scores(p, Q.astype(np.float64), rec["codes"], rec["signs"], rec["norms"], rec["rnorms"])
+    assert_close(got[0], want, what="logits")
+
+
+@pytest.mark.parametrize("d,bits,G,qpg,T,ldk", [
+    (128, 3, 3, 4, 1000, 1100), (128, 2, 2, 1, 65, 65), (128, 4, 2, 5, 130, 131),
+    (128, 3, 1, 8, 1, 1), (200, 2, 2, 4, 777, 777), (200, 4, 1, 4, 500, 512),
+    (64, 3, 4, 4, 300, 300), (96, 4, 2, 3, 257, 260), (256, 3, 1, 2, 129, 129), (40, 2, 1, 4, 63, 63),
+])
+def test_scores_random_records(tq, d, bits, G, qpg, T, ldk):
+    ctx = tq.Context(d, bits, 0)
+    p = O.make_params(d, bits, 0)
+    codes, signs, norms, rnorms = wl.random_records(G * ldk, ctx.code_bytes, ctx.sign_bytes, seed=d + bits)
+    rec = {"codes": codes, "signs": signs, "norms": norms, "rnorms": rnorms}
+    Q = wl.gaussian((G, qpg, d), 21)
+    print(f"scores random d={d} b={bits} G={G} qpg={qpg} T={T} ldk={ldk}", flush=True)
+    got = _score(tq, ctx, Q, rec, G, T, ldk)
+    assert_close(got, _oracle_grouped(p, Q, rec, G, T, ldk), what="logits")
+
+
+def test_scores_zero_norm_keys_and_large_queries(tq):
+    d, bits = 128, 3
+    ctx = tq.Context(d, bits, 0)
+    p = O.make_params(d, bits, 0)
+    K = wl.gaussian((300, d), 22, np.float64) * 50.0
+    K[::7] = 0.0
+    rec = O.quantize(p, K)
+    Q = wl.gaussian((1, 4, d), 23) * 30.0
+    got = _score(tq, ctx, Q, rec, 1, 300, 300)
+    want = _oracle_grouped(p, Q, rec, 1, 300, 300)
+    assert_close(got, want, what="logits")
+    assert (got[0][:, ::7] == 0).all()
+
+
+def test_scores_deterministic(tq):
+    d, bits = 128, 3
+    ctx = tq.Context(d, bits, 0)
+    codes, signs, norms, rnorms = wl.random_records(4 * 2048, ctx.code_bytes, ctx.sign_bytes, seed=3)
+    rec = {"codes": codes, "signs": signs, "norms": norms, "rnorms": rnorms}
+    Q = wl.gaussian((4, 4, d), 24)
+    a = _score(tq, ctx, Q, rec, 4, 2048, 2048)
+    b = _score(tq, ctx, Q, rec, 4, 2048, 2048)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("rows,T,scale", [(5, 1000, 0.125), (3, 33, 1.0), (2, 1, 0.5), (1, 70000, 0.088)])
+def test_softmax_matches_oracle(tq, rows, T, scale):
+    L = wl.gaussian((rows, T), 25 + T) * 30.0
+    lt = torch.from_numpy(L).cuda()
+    print(f"softmax rows={rows} T={T}", flush=True)
+    got = tq.tq_softmax(lt, scale).cpu().numpy()
+    want = O.softmax(L.astype(np.float64), scale)
+    assert_close(got, want, atol=1e-6, rtol=1e-4, what="probs")
+    inplace = tq.tq_softmax(lt, scale, probs=lt).cpu().numpy()
+    assert np.array_equal(inplace, got)
+
+
+def test_scores_errors(tq):
+    ctx = tq.Context(128, 3, 0)
+    mse = tq.Context(128, 3, 1, tq.TQ_MODE_MSE)
+    rec = ctx.empty_records(10)
+    q = torch.zeros((1, 4, 128), device="cuda")
+    with pytest.raises(tq.TQError):
+        tq.tq_scores(mse, q, rec, T=10, ldk=10)
+    with pytest.raises(tq.TQError):
+        tq.tq_scores(ctx, q, rec, T=10, ldk=9)          # ldk < T
+    ws = ctx.workspace(tq.TQ_OP_SCORES, 1, 4)
+    with pytest.raises(tq.TQError):
+        tq.tq_scores(ctx, q, rec, T=10, ldk=10, ws=ws[:16])   # workspace too small

@@ -1,0 +1,82 @@
+"""CPU tests of the C-ABI library: exports, host-side parameters, validation.
+
+No compute call is made here (no GPU in this environment): only host logic.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "oblivious_kv_cache_amd", "lib", "libtq.so")
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libtq.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert "tq_init" in names and "tq_scores" in names and "tq_topk" in names
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    from oblivious_kv_cache_amd import binding
+    assert sorted(binding.EXPORTS) == names
+
+
+@pytest.mark.parametrize("d,bits,mode,seed", [
+    (128, 3, "prod", 0), (128, 2, "prod", 1), (128, 4, "prod", 7), (200, 2, "prod", 0),
+    (200, 4, "prod", 0), (64, 3, "mse", 1), (8, 1, "mse", 3), (256, 4, "mse", 5), (96, 3, "prod", 11),
+])
+def test_host_params_match_oracle(d, bits, mode, seed):
+    from oblivious_kv_cache_amd import binding as tq
+    Pi, S, c, t = tq.tq_host_params(d, bits, seed, tq.TQ_MODE_PROD if mode == "prod" else tq.TQ_MODE_MSE)
+    p = O.make_params(d, bits, seed, mode)
+    assert np.abs(Pi - p.Pi).max() < 1e-12
+    assert S.shape == p.S.shape and (S.size == 0 or np.abs(S - p.S).max() < 1e-12)
+    assert np.abs(c - p.c).max() < 1e-13 and np.abs(t - p.t).max() < 1e-13
+    assert np.array_equal(c, -c[::-1])
+
+
+def test_host_params_validation():
+    from oblivious_kv_cache_amd import binding as tq
+    for d, bits, mode in [(7, 3, 0), (0, 3, 0), (264, 3, 0), (128, 1, 0), (128, 5, 0), (128, 0, 1),
+                          (128, 5, 1), (128, 3, 2)]:
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_host_params(d, bits, 0, mode)
+        assert e.value.status == tq.TQ_EINVAL
+
+
+def test_argument_validation_before_any_device_work():
+    from oblivious_kv_cache_amd import binding as tq
+    L = tq.LIB
+    h = ctypes.c_void_p()
+    assert L.tq_init(7, 3, 0, ctypes.byref(h)) == tq.TQ_EINVAL
+    assert L.tq_init(128, 5, 0, ctypes.byref(h)) == tq.TQ_EINVAL
+    assert L.tq_init_mse(128, 0, 0, ctypes.byref(h)) == tq.TQ_EINVAL
+    assert h.value is None                    # *out untouched on error
+    assert L.tq_init(128, 3, 0, None) == tq.TQ_EINVAL
+    assert L.tq_quantize(None, None, 0, 1, 128, 1, None, None, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_scores(None, None, 1, 4, 1, 1, None, None, None, None, None, None, 0, None) == tq.TQ_EINVAL
+    assert L.tq_softmax(None, -1, 4, 1.0, None, None) == tq.TQ_EINVAL
+    assert L.tq_softmax(None, 0, 4, 1.0, None, None) == tq.TQ_OK          # empty: nothing to do
+    assert L.tq_dequant(None, None, None, None, None, 1, None, None) == tq.TQ_EINVAL
+    assert L.tq_topk(None, None, 1, 1, None, None, None, None, 1, None, None, None, 0, None) == tq.TQ_EINVAL
+    assert L.tq_attend(None, None, None, 1, 4, 1, 1, None, None, None, None, None, None, 1.0,
+                       None, None, None, None, 0, None) == tq.TQ_EINVAL
+    n = ctypes.c_size_t()
+    assert L.tq_workspace_size(None, tq.TQ_OP_SCORES, 1, 4, 0, ctypes.byref(n)) == tq.TQ_EINVAL
+    L.tq_free(None)                           # null-safe
+    assert tq.tq_strerror(tq.TQ_EINVAL) == "invalid argument"
+    assert tq.tq_strerror(12345) == "unknown status"

@@ -308,3 +308,20 @@ def test_planted_wrong_tie_rule_is_caught():
     wrong = np.searchsorted(t, y, side="right")
     nearest = np.argmin(np.abs(y[:, None] - c[None, :]), axis=1)
     assert np.array_equal(right, nearest) and not np.array_equal(wrong, nearest)
+
+
+def test_stage2_from_codes_reproduces_quantize():
+    p = O.make_params(64, 3, 4)
+    X = np.random.default_rng(12).standard_normal((20, 64))
+    r = O.quantize(p, X, return_unpacked=True)
+    for i in range(20):
+        g, z, sb = O.stage2_from_codes(p, X[i], r["idx"][i])
+        assert abs(g - r["rnorms"][i]) < 1e-6 * max(g, 1e-3)
+        assert np.abs(z - r["z"][i]).max() < 1e-12 and np.array_equal(sb, r["sbits"][i])
+    # a different (neighbouring) code choice changes the residual by the centroid gap
+    alt = r["idx"][0].copy()
+    alt[0] = alt[0] + 1 if alt[0] < 3 else alt[0] - 1
+    g2, _, _ = O.stage2_from_codes(p, X[0], alt)
+    y0 = (p.Pi @ (X[0] / np.linalg.norm(X[0])))[0]
+    want = np.sqrt(r["rnorms"][0] ** 2 - (y0 - p.c[r["idx"][0][0]]) ** 2 + (y0 - p.c[alt[0]]) ** 2)
+    assert abs(g2 - want) < 1e-6
