@@ -80,17 +80,4 @@ int launch_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs
   return hip_status();
 }
 
-// Not built yet: fused attention and top-k.
-size_t attend_ws_bytes(const tq_ctx *, int64_t, int, int64_t) { return 0; }
-int launch_attend(const tq_ctx *, const tq_ctx *, const float *, int64_t, int, int64_t, int64_t,
-                  const uint8_t *, const uint8_t *, const float *, const float *, const uint8_t *,
-                  const float *, float, float *, float *, float *, void *, hipStream_t) {
-  return TQ_ENOTSUP;
-}
-size_t topk_ws_bytes(const tq_ctx *, int64_t, int64_t, int) { return 0; }
-int launch_topk(const tq_ctx *, const float *, int64_t, int64_t, const uint8_t *, const uint8_t *,
-                const float *, const float *, int, int64_t *, float *, void *, hipStream_t) {
-  return TQ_ENOTSUP;
-}
-
 }  // namespace tq

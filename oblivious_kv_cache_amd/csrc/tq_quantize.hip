@@ -80,11 +80,25 @@ __global__ void __launch_bounds__(USE_LDS ? 512 : 256) quantize_kernel(QArgs a) 
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
 
   if constexpr (USE_LDS) {
-    const int nfr = (a.prod ? 4 : 2) * FR * 64;
-    for (int i = threadIdx.x; i < nfr; i += blockDim.x) {
-      const int which = i / (FR * 64), off = i - which * (FR * 64);
-      const Frag *src = which == 0 ? a.PiA_hi : which == 1 ? a.PiA_lo : which == 2 ? a.S2A_hi : a.S2A_lo;
-      lds[i] = src[off];
+    // Fill LDS with batches of independent 16-byte loads per thread, one
+    // operand matrix at a time (the matrix pointer stays a scalar; choosing it
+    // with a runtime index would re-load it from the kernel arguments).
+    constexpr int NF = FR * 64;
+    constexpr int ITER = (NF + 511) / 512;        // USE_LDS launches 512 threads
+    auto fill = [&](const Frag *src, int which) {
+      Frag tmp[ITER];
+      // Clamped indices: no branch, so all loads are issued before the first
+      // wait; a duplicate store of the last element rewrites the same value.
+#pragma unroll
+      for (int b = 0; b < ITER; ++b) tmp[b] = src[min(b * 512 + (int)threadIdx.x, NF - 1)];
+#pragma unroll
+      for (int b = 0; b < ITER; ++b) lds[which * NF + min(b * 512 + (int)threadIdx.x, NF - 1)] = tmp[b];
+    };
+    fill(a.PiA_hi, 0);
+    fill(a.PiA_lo, 1);
+    if (a.prod) {
+      fill(a.S2A_hi, 2);
+      fill(a.S2A_lo, 3);
     }
     __syncthreads();
   }
@@ -92,11 +106,12 @@ __global__ void __launch_bounds__(USE_LDS ? 512 : 256) quantize_kernel(QArgs a) 
   // opaque in every tile iteration so that address arithmetic for all
   // fragments is not hoisted out of the loop into registers.
   int lofs = lane;
+  const Frag *const PiH = a.PiA_hi, *const PiL = a.PiA_lo, *const S2H = a.S2A_hi, *const S2L = a.S2A_lo;
   auto frag = [&](int which, int f) -> bf16x8 {
     if constexpr (USE_LDS) {
       return as_bf(lds[(which * FR + f) * 64 + lofs]);
     } else {
-      const Frag *src = which == 0 ? a.PiA_hi : which == 1 ? a.PiA_lo : which == 2 ? a.S2A_hi : a.S2A_lo;
+      const Frag *src = which == 0 ? PiH : which == 1 ? PiL : which == 2 ? S2H : S2L;
       return as_bf(src[f * 64 + lofs]);
     }
   };

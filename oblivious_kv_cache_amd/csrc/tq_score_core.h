@@ -1,0 +1,116 @@
+// Shared pieces of the int8-MFMA estimator (see tq_scores.hip for the math):
+// the query-prep interface and the per-16-key tile computation used by the
+// scores, top-k and attention kernels.
+#pragma once
+
+#include "tq_internal.h"
+
+namespace tq {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// MFMAs per 16-key tile: two per 32-bit record word (bit planes 0-3, 4-7),
+// over code words, parity words (3-bit codes) and sign words.
+__host__ __device__ inline int mfma_count(int cb16, int sb16, int w) {
+  return 2 * cb16 + (w == 3 ? 2 * cb16 : 0) + 2 * sb16;
+}
+
+// bytes of prepared query state per (query group of 4 heads): NM fragments of
+// 64 lanes x 16 B, then 4 heads x {1/S_P, 1/S_Q, K_P, K_Q}
+__host__ __device__ inline int64_t prep_stride(int nm) {
+  return ((int64_t)nm * 1024 + 64 + 255) / 256 * 256;
+}
+
+// Build the A fragments for `groups` query groups.  Group i covers queries
+// q[(i / hg) * qpg + (i % hg) * 4 + hh], hh < 4, of which those with head
+// index < qpg and flat index < nq_total are real (the rest are zero).
+int launch_prep(const tq_ctx *ctx, const float *q, int64_t groups, int qpg, int hg,
+                int64_t nq_total, uint8_t *ws, hipStream_t stream);
+
+// Record words a lane (column n, lane group g) holds for one key.
+template <int CB16, int SB16, int W>
+struct KeyWords {
+  static constexpr int XW = (W == 3) ? 1 : 0;
+  uint32_t cw[CB16 + XW];
+  uint32_t sw[SB16];
+};
+
+template <int CB16, int SB16, int W>
+__device__ __forceinline__ void load_key_words(KeyWords<CB16, SB16, W> &k, const uint8_t *crec,
+                                               const uint8_t *srec, int grp) {
+  const uint32_t *cp = reinterpret_cast<const uint32_t *>(crec + grp * (CB16 * 4));
+#pragma unroll
+  for (int i = 0; i < CB16; ++i) k.cw[i] = cp[i];
+  if constexpr (W == 3) {   // first word of the next lane group's chunk (none for the last group)
+    const uint32_t nxt = cp[grp < 3 ? CB16 : CB16 - 1];
+    k.cw[CB16] = grp < 3 ? nxt : 0u;
+  }
+  const uint32_t *sp = reinterpret_cast<const uint32_t *>(srec + grp * (SB16 * 4));
+#pragma unroll
+  for (int i = 0; i < SB16; ++i) k.sw[i] = sp[i];
+}
+
+__device__ __forceinline__ i32x4 mfma8(const i32x4 &a, const i32x4 &b, const i32x4 &c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// bit planes 4*half .. 4*half+3 of each byte of w, as int8 values 2^j (-128 for j = 7)
+__device__ __forceinline__ i32x4 planes(uint32_t w, int half) {
+  const int s = 4 * half;
+  return i32x4{(int)(w & (0x01010101u << s)), (int)(w & (0x01010101u << (s + 1))),
+               (int)(w & (0x01010101u << (s + 2))), (int)(w & (0x01010101u << (s + 3)))};
+}
+
+struct HeadConsts {
+  float invSP, invSQ, KP, KQ;
+};
+
+template <int CB16, int SB16, int W>
+struct ScoreShape {
+  static constexpr int NMC = 2 * CB16, NMP = (W == 3) ? 2 * CB16 : 0, NMS = 2 * SB16;
+  static constexpr int NM = NMC + NMP + NMS;
+};
+
+// Logit of head (lane / 16) of this query group for key (lane % 16) of the tile:
+//   nu * (P + alpha * gamma * Q), P and Q recombined from four int32 digit rows.
+template <int CB16, int SB16, int W>
+__device__ __forceinline__ float tile_logit(const i32x4 *A, const KeyWords<CB16, SB16, W> &k, float nu,
+                                            float gamma, float alpha, const HeadConsts &hc) {
+  using Sh = ScoreShape<CB16, SB16, W>;
+  i32x4 accP = {0, 0, 0, 0}, accQ = {0, 0, 0, 0};
+#pragma unroll
+  for (int p = 0; p < CB16; ++p) {
+    accP = mfma8(A[2 * p], planes(k.cw[p], 0), accP);
+    accP = mfma8(A[2 * p + 1], planes(k.cw[p], 1), accP);
+  }
+  if constexpr (W == 3) {
+#pragma unroll
+    for (int p = 0; p < CB16; ++p) {
+      const uint32_t lo = k.cw[p], hi = k.cw[p + 1];
+      const uint32_t par = lo ^ __builtin_amdgcn_alignbit(hi, lo, 1) ^ __builtin_amdgcn_alignbit(hi, lo, 2);
+      accP = mfma8(A[Sh::NMC + 2 * p], planes(par, 0), accP);
+      accP = mfma8(A[Sh::NMC + 2 * p + 1], planes(par, 1), accP);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < SB16; ++p) {
+    accQ = mfma8(A[Sh::NMC + Sh::NMP + 2 * p], planes(k.sw[p], 0), accQ);
+    accQ = mfma8(A[Sh::NMC + Sh::NMP + 2 * p + 1], planes(k.sw[p], 1), accQ);
+  }
+  const float P = fmaf((float)accP[3], 0x1.0p-21f,
+                       fmaf((float)accP[2], 0x1.0p-14f, fmaf((float)accP[1], 0x1.0p-7f, (float)accP[0]))) *
+                      hc.invSP - hc.KP;
+  const float Q = fmaf((float)accQ[3], 0x1.0p-21f,
+                       fmaf((float)accQ[2], 0x1.0p-14f, fmaf((float)accQ[1], 0x1.0p-7f, (float)accQ[0]))) *
+                      hc.invSQ - hc.KQ;
+  return nu * fmaf(alpha * gamma, Q, P);
+}
+
+// Expands a dispatch over the record geometries d <= 256 can produce:
+// (code words per lane group, sign words per lane group, code bits).
+#define TQ_FOR_EACH_GEOMETRY(X)                                              \
+  X(1, 1, 1) X(2, 2, 1)                                           \
+  X(1, 1, 2) X(2, 1, 2) X(3, 2, 2) X(4, 2, 2)                                \
+  X(1, 1, 3) X(2, 1, 3) X(3, 1, 3) X(4, 2, 3) X(5, 2, 3) X(6, 2, 3)
+
+}  // namespace tq

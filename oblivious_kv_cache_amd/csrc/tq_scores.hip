@@ -25,95 +25,148 @@
 // recombined in fp32.  Four digits keep the coefficient error below ~2.5e-7 of
 // the largest coefficient.  A query-prep kernel builds these A fragments once
 // per (KV group, head group) into the caller's workspace.
-#include "tq_internal.h"
+#include "tq_score_core.h"
 
 namespace tq {
 namespace {
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int PREP_THREADS = 256;
 
-struct ScoreGeom {
-  int CB16, SB16, w, nm;   // code words/lane, sign words/lane, code bits, MFMAs per key tile
-};
-
-__host__ __device__ inline int mfma_count(int cb16, int sb16, int w) {
-  return 2 * cb16 + (w == 3 ? 2 * cb16 : 0) + 2 * sb16;
-}
-
-// bytes of prepared query state per (KV group, head group)
-__host__ __device__ inline int64_t prep_stride(int nm) {
-  return ((int64_t)nm * 1024 + 64 + 255) / 256 * 256;
-}
+#ifndef TQ_SCORES_PREFETCH
+#define TQ_SCORES_PREFETCH 0
+#endif
+#ifndef TQ_SCORES_WAVES
+#define TQ_SCORES_WAVES 16384
+#endif
 
 struct PrepArgs {
   const float *q;      // [G][qpg][d]
   const float *PiT;    // [d][d]
   const float *ST;     // [d][m]
   uint8_t *ws;
+  int64_t nq_total;    // queries beyond this flat index are zero
   int d, m, w, qpg, hg, cb, sb, nm;
   float basis[4];
 };
 
 // Build the int8 A fragments and per-head constants for one (group, head group).
+// Pi^T and S^T are staged through LDS in row chunks with 16-byte cooperative
+// loads, so the query products do not wait on one global load at a time.
+constexpr int PREP_STAGE_FLOATS = 8192;   // 32 KB staging buffer
+
+__device__ inline float block_sum(float v, float *red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < PREP_THREADS / 64; ++i) t += red[i];
+  return t;
+}
+
+__device__ inline float block_max(float v, float *red) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < PREP_THREADS / 64; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+// out[hh][i] = sum_j MT[j][i] * qv[hh][j]  for i < cols (MT row-major [d][cols])
+__device__ inline void apply_T(const float *MT, int d, int cols, const float (*qv)[TQ_MAX_D],
+                               float (*out)[TQ_MAX_D], float *stage) {
+  const int tid = threadIdx.x;
+  const int rows_per = PREP_STAGE_FLOATS / cols;           // rows of MT per chunk
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < d; j0 += rows_per) {
+    const int nr = min(rows_per, d - j0);
+    const int n4 = nr * cols / 4;                           // cols % 8 == 0
+    const float4 *src = reinterpret_cast<const float4 *>(MT + (int64_t)j0 * cols);
+    __syncthreads();
+    for (int base = 0; base < n4; base += 8 * PREP_THREADS) {   // 8 loads in flight per thread
+      float4 tmp[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {     // branch-free: clamped index
+        tmp[b] = src[min(base + b * PREP_THREADS + tid, n4 - 1)];
+      }
+#pragma unroll
+      for (int b = 0; b < 8; ++b)       // duplicate stores at the clamp rewrite one value
+        reinterpret_cast<float4 *>(stage)[min(base + b * PREP_THREADS + tid, n4 - 1)] = tmp[b];
+    }
+    __syncthreads();
+    if (tid < cols) {
+#pragma unroll 8
+      for (int j = 0; j < nr; ++j) {
+        const float m = stage[j * cols + tid];
+        acc[0] = fmaf(m, qv[0][j0 + j], acc[0]);
+        acc[1] = fmaf(m, qv[1][j0 + j], acc[1]);
+        acc[2] = fmaf(m, qv[2][j0 + j], acc[2]);
+        acc[3] = fmaf(m, qv[3][j0 + j], acc[3]);
+      }
+    }
+  }
+  if (tid < cols)
+    for (int hh = 0; hh < 4; ++hh) out[hh][tid] = acc[hh];
+}
+
 __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
   __shared__ float qv[4][TQ_MAX_D];
   __shared__ float qr[4][TQ_MAX_D];
   __shared__ float qs[4][TQ_MAX_D];
   __shared__ float vP[4][2 * 96 * 8];     // code-bit + parity-bit coefficients
   __shared__ float vQ[4][32 * 8];         // sign-bit coefficients
-  __shared__ float red[4][2][PREP_THREADS / 64];
+  __shared__ __align__(16) float stage[PREP_STAGE_FLOATS];
+  __shared__ float red[PREP_THREADS / 64];
   __shared__ float scal[4][2];
+  __shared__ float sums[4][2];
+  __shared__ float basis[4];
 
   const int gidx = blockIdx.x;           // = group * hg + head group
   const int grp = gidx / a.hg, hgi = gidx - grp * a.hg;
   const int tid = threadIdx.x;
   const int d = a.d, m = a.m;
   const int ncb = a.cb * 8, nsb = a.sb * 8;
+  // Kernel-argument fields are copied to LDS / scalars once: indexing them
+  // with a runtime value makes the compiler re-load them from the kernarg
+  // segment (a full memory round trip) on every use.
+  if (tid < 4) basis[tid] = tid == 0 ? a.basis[0] : tid == 1 ? a.basis[1] : tid == 2 ? a.basis[2] : a.basis[3];
+  const int w = a.w, cwpl = a.cb / 16, swpl = a.sb / 16;
 
   for (int i = tid; i < 4 * d; i += PREP_THREADS) {
     const int hh = i / d, j = i - hh * d;
     const int h = hgi * 4 + hh;
-    qv[hh][j] = h < a.qpg ? a.q[((int64_t)grp * a.qpg + h) * d + j] : 0.f;
+    const int64_t flat = (int64_t)grp * a.qpg + h;
+    qv[hh][j] = (h < a.qpg && flat < a.nq_total) ? a.q[flat * d + j] : 0.f;
   }
   __syncthreads();
-  // q_rot = Pi q, q_s = S q  (PiT[j][i] = Pi[i][j]; ST[j][i] = S[i][j])
-  if (tid < d) {
-    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-    for (int j = 0; j < d; ++j) {
-      const float p = a.PiT[(int64_t)j * d + tid];
-      r0 = fmaf(p, qv[0][j], r0);
-      r1 = fmaf(p, qv[1][j], r1);
-      r2 = fmaf(p, qv[2][j], r2);
-      r3 = fmaf(p, qv[3][j], r3);
-    }
-    qr[0][tid] = r0; qr[1][tid] = r1; qr[2][tid] = r2; qr[3][tid] = r3;
-  }
-  if (tid < m) {
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    for (int j = 0; j < d; ++j) {
-      const float p = a.ST[(int64_t)j * m + tid];
-      s0 = fmaf(p, qv[0][j], s0);
-      s1 = fmaf(p, qv[1][j], s1);
-      s2 = fmaf(p, qv[2][j], s2);
-      s3 = fmaf(p, qv[3][j], s3);
-    }
-    qs[0][tid] = s0; qs[1][tid] = s1; qs[2][tid] = s2; qs[3][tid] = s3;
-  }
+  // q_rot = Pi q (PiT[j][i] = Pi[i][j]), q_s = S q (ST[j][i] = S[i][j])
+  apply_T(a.PiT, d, d, qv, qr, stage);
+  apply_T(a.ST, d, m, qv, qs, stage);
   __syncthreads();
 
+  // per-head sums of q_rot and q_s (for the +-1 -> bit conversion)
+  for (int hh = 0; hh < 4; ++hh) {
+    const float s1 = block_sum(tid < d ? qr[hh][tid] : 0.f, red);
+    const float s2 = block_sum(tid < m ? qs[hh][tid] : 0.f, red);
+    if (tid == 0) {
+      sums[hh][0] = s1;
+      sums[hh][1] = s2;
+    }
+  }
+
   // coefficients of every bit position
-  const int npar = a.w == 3 ? ncb : 0;
+  const int npar = w == 3 ? ncb : 0;
   for (int i = tid; i < 4 * (ncb + npar); i += PREP_THREADS) {
     const int hh = i / (ncb + npar), k = i - hh * (ncb + npar);
     float v = 0.f;
     if (k < ncb) {
-      const int coord = k / a.w, plane = k - coord * a.w;
-      if (coord < d) v = 2.f * a.basis[plane] * qr[hh][coord];
+      const int coord = k / w, plane = k - coord * w;
+      if (coord < d) v = 2.f * basis[plane] * qr[hh][coord];
     } else {
       const int kk = k - ncb;
-      if (kk % 3 == 0 && kk / 3 < d) v = 2.f * a.basis[3] * qr[hh][kk / 3];
+      if (kk % 3 == 0 && kk / 3 < d) v = 2.f * basis[3] * qr[hh][kk / 3];
     }
     vP[hh][k] = v;
   }
@@ -123,58 +176,42 @@ __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
   }
   __syncthreads();
 
-  // per (head, chain) maxima of |v| 2^-j
-  float mx[4][2];
+  // per (head, chain) maxima of |v| 2^-j -> digit scale 127 / max
   for (int hh = 0; hh < 4; ++hh) {
     float mp = 0.f, mq = 0.f;
     for (int k = tid; k < ncb + npar; k += PREP_THREADS) mp = fmaxf(mp, ldexpf(fabsf(vP[hh][k]), -(k & 7)));
     for (int k = tid; k < nsb; k += PREP_THREADS) mq = fmaxf(mq, ldexpf(fabsf(vQ[hh][k]), -(k & 7)));
-    for (int o = 32; o > 0; o >>= 1) {
-      mp = fmaxf(mp, __shfl_xor(mp, o));
-      mq = fmaxf(mq, __shfl_xor(mq, o));
+    mp = block_max(mp, red);
+    mq = block_max(mq, red);
+    if (tid == 0) {
+      scal[hh][0] = mp > 0.f ? 127.f / mp : 1.f;
+      scal[hh][1] = mq > 0.f ? 127.f / mq : 1.f;
     }
-    mx[hh][0] = mp;
-    mx[hh][1] = mq;
-  }
-  if ((tid & 63) == 0)
-    for (int hh = 0; hh < 4; ++hh) {
-      red[hh][0][tid >> 6] = mx[hh][0];
-      red[hh][1][tid >> 6] = mx[hh][1];
-    }
-  __syncthreads();
-  if (tid < 8) {
-    const int hh = tid >> 1, ch = tid & 1;
-    float v = 0.f;
-    for (int i = 0; i < PREP_THREADS / 64; ++i) v = fmaxf(v, red[hh][ch][i]);
-    scal[hh][ch] = v > 0.f ? 127.f / v : 1.f;
   }
   __syncthreads();
 
   uint8_t *out = a.ws + (int64_t)gidx * prep_stride(a.nm);
   // A fragments: dword index = (mu * 64 + lane) * 4 + e
   const int ndw = a.nm * 64 * 4;
-  const int nmc = 2 * (a.cb / 16), nmp = a.w == 3 ? nmc : 0;
+  const int nmc = 2 * cwpl, nmp = w == 3 ? nmc : 0;
   for (int i = tid; i < ndw; i += PREP_THREADS) {
     const int mu = i >> 8, lane = (i >> 2) & 63, e = i & 3;
     const int row = lane & 15, g = lane >> 4;
     const int hh = row >> 2, digit = row & 3;
-    int chain, mloc, wpl, base;
+    int chain, mloc, wpl;
     const float *vv;
     if (mu < nmc + nmp) {
       chain = 0;
       const bool par = mu >= nmc;
       mloc = par ? mu - nmc : mu;
-      wpl = a.cb / 16;
+      wpl = cwpl;
       vv = vP[hh] + (par ? ncb : 0);
-      base = 0;
     } else {
       chain = 1;
       mloc = mu - nmc - nmp;
-      wpl = a.sb / 16;
+      wpl = swpl;
       vv = vQ[hh];
-      base = 0;
     }
-    (void)base;
     const int pair = mloc >> 1, half = mloc & 1;
     const int word = g * wpl + pair;
     const int j = 4 * half + e;
@@ -197,15 +234,12 @@ __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
   // constants per head: invS_P, invS_Q, K_P, K_Q
   if (tid < 4) {
     const int hh = tid;
-    float sq = 0.f, ss = 0.f;
-    for (int i = 0; i < d; ++i) sq += qr[hh][i];
-    for (int i = 0; i < m; ++i) ss += qs[hh][i];
-    float bsum = a.basis[0] + (a.w >= 2 ? a.basis[1] : 0.f) + (a.w >= 3 ? a.basis[2] + a.basis[3] : 0.f);
+    const float bsum = basis[0] + (w >= 2 ? basis[1] : 0.f) + (w >= 3 ? basis[2] + basis[3] : 0.f);
     float *cst = reinterpret_cast<float *>(out + (int64_t)a.nm * 1024);
     cst[hh * 4 + 0] = 1.f / scal[hh][0];
     cst[hh * 4 + 1] = 1.f / scal[hh][1];
-    cst[hh * 4 + 2] = bsum * sq;
-    cst[hh * 4 + 3] = ss;
+    cst[hh * 4 + 2] = bsum * sums[hh][0];
+    cst[hh * 4 + 3] = sums[hh][1];
   }
 }
 
@@ -219,21 +253,9 @@ struct ScoreArgs {
   float alpha;
 };
 
-__device__ __forceinline__ i32x4 mfma8(const i32x4 &a, const i32x4 &b, const i32x4 &c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ i32x4 planes(uint32_t w, int half) {
-  const int s = 4 * half;
-  return i32x4{(int)(w & (0x01010101u << s)), (int)(w & (0x01010101u << (s + 1))),
-               (int)(w & (0x01010101u << (s + 2))), (int)(w & (0x01010101u << (s + 3)))};
-}
-
 template <int CB16, int SB16, int W>
 __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
-  constexpr int NMC = 2 * CB16, NMP = (W == 3) ? 2 * CB16 : 0, NMS = 2 * SB16;
-  constexpr int NM = NMC + NMP + NMS;
-  constexpr int XW = (W == 3) ? 1 : 0;   // extra word for parity straddling
+  constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   const int wv = threadIdx.x >> 6;
   const int64_t gidx = blockIdx.y;       // key group * hg + head group
@@ -245,91 +267,95 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
 #pragma unroll
   for (int mu = 0; mu < NM; ++mu) A[mu] = reinterpret_cast<const i32x4 *>(prep)[mu * 64 + lane];
   const float *cst = reinterpret_cast<const float *>(prep + NM * 1024) + grp * 4;
-  const float invSP = cst[0], invSQ = cst[1], KP = cst[2], KQ = cst[3];
+  const HeadConsts hc{cst[0], cst[1], cst[2], cst[3]};
   const int head = hgi * 4 + grp;
   const bool head_ok = head < a.qpg;
-  float *lrow = a.logits + ((int64_t)kg * a.qpg + head) * a.T;
+  float *lrow = a.logits + ((int64_t)kg * a.qpg + (head_ok ? head : 0)) * a.T;
 
-  const uint8_t *cbase = a.codes + (int64_t)kg * a.ldk * a.cb + grp * (CB16 * 4);
-  const uint8_t *sbase = a.signs + (int64_t)kg * a.ldk * a.sb + grp * (SB16 * 4);
+  const uint8_t *cbase = a.codes + (int64_t)kg * a.ldk * a.cb;
+  const uint8_t *sbase = a.signs + (int64_t)kg * a.ldk * a.sb;
   const float *nbase = a.norms + (int64_t)kg * a.ldk;
   const float *rbase = a.rnorms + (int64_t)kg * a.ldk;
 
   const int64_t tile0 = ((int64_t)blockIdx.x * 4 + wv) * a.tiles_per_wave;
-  for (int it = 0; it < a.tiles_per_wave; ++it) {
-    const int64_t t0 = (tile0 + it) * 64;
-    if (t0 >= a.T) break;
-    uint32_t cw[4][CB16 + XW], sw[4][SB16];
-    float nu[4], ga[4];
-    int64_t tk[4];
+  int64_t ntile = a.tiles_per_wave;
+  const int64_t last = (a.T + 63) / 64;
+  if (tile0 + ntile > last) ntile = last - tile0;
+  auto load_tile = [&](KeyWords<CB16, SB16, W> (&kw)[4], float (&nu)[4], float (&ga)[4], int64_t t0) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       int64_t t = t0 + 16 * s + col;
-      tk[s] = t;
       if (t >= a.T) t = a.T - 1;
-      const uint32_t *cp = reinterpret_cast<const uint32_t *>(cbase + t * a.cb);
-#pragma unroll
-      for (int i = 0; i < CB16; ++i) cw[s][i] = cp[i];
-      if constexpr (XW) cw[s][CB16] = grp < 3 ? cp[CB16] : 0u;
-      const uint32_t *sp = reinterpret_cast<const uint32_t *>(sbase + t * a.sb);
-#pragma unroll
-      for (int i = 0; i < SB16; ++i) sw[s][i] = sp[i];
+      load_key_words(kw[s], cbase + t * a.cb, sbase + t * a.sb, grp);
       nu[s] = nbase[t];
       ga[s] = rbase[t];
     }
+  };
+  auto score_tile = [&](const KeyWords<CB16, SB16, W> (&kw)[4], const float (&nu)[4], const float (&ga)[4],
+                        int64_t t0) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      i32x4 accP = {0, 0, 0, 0}, accQ = {0, 0, 0, 0};
-#pragma unroll
-      for (int p = 0; p < CB16; ++p) {
-        accP = mfma8(A[2 * p], planes(cw[s][p], 0), accP);
-        accP = mfma8(A[2 * p + 1], planes(cw[s][p], 1), accP);
-      }
-      if constexpr (W == 3) {
-#pragma unroll
-        for (int p = 0; p < CB16; ++p) {
-          const uint32_t lo = cw[s][p], hi = cw[s][p + 1];
-          const uint32_t par = lo ^ __builtin_amdgcn_alignbit(hi, lo, 1) ^ __builtin_amdgcn_alignbit(hi, lo, 2);
-          accP = mfma8(A[NMC + 2 * p], planes(par, 0), accP);
-          accP = mfma8(A[NMC + 2 * p + 1], planes(par, 1), accP);
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < SB16; ++p) {
-        accQ = mfma8(A[NMC + NMP + 2 * p], planes(sw[s][p], 0), accQ);
-        accQ = mfma8(A[NMC + NMP + 2 * p + 1], planes(sw[s][p], 1), accQ);
-      }
-      const float P = fmaf((float)accP[3], 0x1.0p-21f,
-                           fmaf((float)accP[2], 0x1.0p-14f, fmaf((float)accP[1], 0x1.0p-7f, (float)accP[0]))) *
-                          invSP - KP;
-      const float Q = fmaf((float)accQ[3], 0x1.0p-21f,
-                           fmaf((float)accQ[2], 0x1.0p-14f, fmaf((float)accQ[1], 0x1.0p-7f, (float)accQ[0]))) *
-                          invSQ - KQ;
-      const float l = nu[s] * fmaf(a.alpha * ga[s], Q, P);
-      if (head_ok && tk[s] < a.T) lrow[tk[s]] = l;
+      const int64_t t = t0 + 16 * s + col;
+      const float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
+      if (head_ok && t < a.T) lrow[t] = l;
     }
+  };
+#if TQ_SCORES_PREFETCH
+  // two named register sets: the next tile's words load while this one is scored
+  KeyWords<CB16, SB16, W> k0[4], k1[4];
+  float n0[4], g0[4], n1[4], g1[4];
+  if (ntile > 0) load_tile(k0, n0, g0, tile0 * 64);
+  for (int64_t it = 0; it < ntile; it += 2) {
+    if (it + 1 < ntile) load_tile(k1, n1, g1, (tile0 + it + 1) * 64);
+    score_tile(k0, n0, g0, (tile0 + it) * 64);
+    if (it + 1 >= ntile) break;
+    if (it + 2 < ntile) load_tile(k0, n0, g0, (tile0 + it + 2) * 64);
+    score_tile(k1, n1, g1, (tile0 + it + 1) * 64);
   }
-}
-
-template <int CB16, int SB16, int W>
-void launch_one(const ScoreArgs &a, dim3 grid, hipStream_t s) {
-  scores_kernel<CB16, SB16, W><<<grid, 256, 0, s>>>(a);
+#else
+  for (int64_t it = 0; it < ntile; ++it) {
+    KeyWords<CB16, SB16, W> kw[4];
+    float nu[4], ga[4];
+    load_tile(kw, nu, ga, (tile0 + it) * 64);
+    score_tile(kw, nu, ga, (tile0 + it) * 64);
+  }
+#endif
 }
 
 int dispatch(const ScoreArgs &a, dim3 grid, int cb16, int sb16, int w, hipStream_t s) {
-#define TQ_CASE(C, S, W_)                                   \
-  if (cb16 == C && sb16 == S && w == W_) {                  \
-    launch_one<C, S, W_>(a, grid, s);                       \
-    return hip_status();                                    \
+#define TQ_CASE(C, S, W_)                                        \
+  if (cb16 == C && sb16 == S && w == W_) {                       \
+    scores_kernel<C, S, W_><<<grid, 256, 0, s>>>(a);             \
+    return hip_status();                                         \
   }
-  TQ_CASE(1, 1, 1) TQ_CASE(2, 2, 1) TQ_CASE(1, 2, 1)
-  TQ_CASE(1, 1, 2) TQ_CASE(2, 1, 2) TQ_CASE(3, 2, 2) TQ_CASE(4, 2, 2)
-  TQ_CASE(1, 1, 3) TQ_CASE(2, 1, 3) TQ_CASE(3, 1, 3) TQ_CASE(4, 2, 3) TQ_CASE(5, 2, 3) TQ_CASE(6, 2, 3)
+  TQ_FOR_EACH_GEOMETRY(TQ_CASE)
 #undef TQ_CASE
   return TQ_ENOTSUP;
 }
 
 }  // namespace
+
+int launch_prep(const tq_ctx *ctx, const float *q, int64_t groups, int qpg, int hg, int64_t nq_total,
+                uint8_t *ws, hipStream_t stream) {
+  PrepArgs pa{};
+  pa.q = q;
+  pa.PiT = ctx->PiT32;
+  pa.ST = ctx->ST32;
+  pa.ws = ws;
+  pa.nq_total = nq_total;
+  pa.d = ctx->hp.d;
+  pa.m = ctx->hp.m;
+  pa.w = ctx->hp.w;
+  pa.qpg = qpg;
+  pa.hg = hg;
+  pa.cb = ctx->code_bytes;
+  pa.sb = ctx->sign_bytes;
+  pa.nm = mfma_count(ctx->code_bytes / 16, ctx->sign_bytes / 16, ctx->hp.w);
+  for (int i = 0; i < 4; ++i) pa.basis[i] = ctx->basis[i];
+  if (groups > 0x7fffffff) return TQ_ENOTSUP;
+  prep_kernel<<<dim3((unsigned)groups), PREP_THREADS, 0, stream>>>(pa);
+  return hip_status();
+}
 
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t G, int qpg) {
   const int hg = (qpg + 3) / 4;
@@ -343,24 +369,10 @@ int launch_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t
   if (G == 0 || T == 0) return TQ_OK;
   const int hg = (qpg + 3) / 4;
   const int cb16 = ctx->code_bytes / 16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
-  const int nm = mfma_count(cb16, sb16, w);
-
-  PrepArgs pa{};
-  pa.q = q;
-  pa.PiT = ctx->PiT32;
-  pa.ST = ctx->ST32;
-  pa.ws = reinterpret_cast<uint8_t *>(ws);
-  pa.d = ctx->hp.d;
-  pa.m = ctx->hp.m;
-  pa.w = w;
-  pa.qpg = qpg;
-  pa.hg = hg;
-  pa.cb = ctx->code_bytes;
-  pa.sb = ctx->sign_bytes;
-  pa.nm = nm;
-  for (int i = 0; i < 4; ++i) pa.basis[i] = ctx->basis[i];
-  prep_kernel<<<dim3((unsigned)(G * hg)), PREP_THREADS, 0, stream>>>(pa);
-  if (hip_status() != TQ_OK) return TQ_EHIP;
+  const int64_t groups = G * hg;
+  if (groups > 65535) return TQ_ENOTSUP;
+  int st = launch_prep(ctx, q, groups, qpg, hg, G * qpg, reinterpret_cast<uint8_t *>(ws), stream);
+  if (st != TQ_OK) return st;
 
   ScoreArgs sa{};
   sa.codes = codes;
@@ -376,54 +388,109 @@ int launch_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t
   sa.cb = ctx->code_bytes;
   sa.sb = ctx->sign_bytes;
   sa.alpha = ctx->alpha;
-  // key tiles of 64 per wave iteration; aim for >= ~4096 waves in flight overall
+  // key tiles of 64 per wave iteration; aim for ~TQ_SCORES_WAVES waves overall
   const int64_t tiles = (T + 63) / 64;
-  const int64_t groups = G * hg;
-  int64_t tpw = (tiles * groups + 16383) / 16384;
+  int64_t tpw = (tiles * groups + TQ_SCORES_WAVES - 1) / TQ_SCORES_WAVES;
   if (tpw < 1) tpw = 1;
   if (tpw > 64) tpw = 64;
   const int64_t chunks = (tiles + 4 * tpw - 1) / (4 * tpw);
   sa.tiles_per_wave = (int)tpw;
-  if (groups > 65535) return TQ_ENOTSUP;
   return dispatch(sa, dim3((unsigned)chunks, (unsigned)groups), cb16, sb16, w, stream);
 }
 
 // ------------------------------------------------------------------ softmax
+// Row softmax of scale * logits.  A row of up to NT * 4 * VPT floats is held in
+// registers (one HBM read, one write, 16-byte accesses); longer rows and rows
+// whose length is not a multiple of 4 take a streaming two-pass kernel.
 namespace {
 
-__global__ void __launch_bounds__(256) softmax_kernel(const float *in, float *out, int64_t T,
-                                                      float scale) {
-  __shared__ float sm[4], ssum[4];
-  const int64_t row = blockIdx.x;
-  const float *x = in + row * T;
-  float *y = out + row * T;
-  float m = -INFINITY, s = 0.f;
-  for (int64_t i = threadIdx.x; i < T; i += 256) {
-    const float z = scale * x[i];
-    if (z > m) {
-      s = s * expf(m - z) + 1.f;
-      m = z;
-    } else {
-      s += expf(z - m);
-    }
-  }
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int NT>
+__device__ inline void block_max_sum(float &m, float &s) {
+  __shared__ float sm[NT / 64], ss[NT / 64];
   for (int o = 32; o > 0; o >>= 1) {
     const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
     const float mm = fmaxf(m, m2);
-    s = (m == -INFINITY ? 0.f : s * expf(m - mm)) + (m2 == -INFINITY ? 0.f : s2 * expf(m2 - mm));
+    s = (m == -INFINITY ? 0.f : s * exp2f((m - mm) * kLog2e)) +
+        (m2 == -INFINITY ? 0.f : s2 * exp2f((m2 - mm) * kLog2e));
     m = mm;
   }
   if ((threadIdx.x & 63) == 0) {
     sm[threadIdx.x >> 6] = m;
-    ssum[threadIdx.x >> 6] = s;
+    ss[threadIdx.x >> 6] = s;
   }
   __syncthreads();
   float M = sm[0];
-  for (int i = 1; i < 4; ++i) M = fmaxf(M, sm[i]);
+  for (int i = 1; i < NT / 64; ++i) M = fmaxf(M, sm[i]);
   float S = 0.f;
-  for (int i = 0; i < 4; ++i) S += sm[i] == -INFINITY ? 0.f : ssum[i] * expf(sm[i] - M);
-  const float inv = 1.f / S;
-  for (int64_t i = threadIdx.x; i < T; i += 256) y[i] = expf(scale * x[i] - M) * inv;
+  for (int i = 0; i < NT / 64; ++i) S += sm[i] == -INFINITY ? 0.f : ss[i] * exp2f((sm[i] - M) * kLog2e);
+  m = M;
+  s = S;
+}
+
+template <int NT, int VPT>
+__global__ void __launch_bounds__(NT) softmax_reg_kernel(const float *in, float *out, int64_t T,
+                                                          float scale) {
+  const int64_t row = blockIdx.x;
+  const float4 *x = reinterpret_cast<const float4 *>(in + row * T);
+  float4 *y = reinterpret_cast<float4 *>(out + row * T);
+  const int n4 = (int)(T >> 2);
+  float4 v[VPT];
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i < n4) {
+      v[k] = x[i];
+      v[k].x *= scale; v[k].y *= scale; v[k].z *= scale; v[k].w *= scale;
+      m = fmaxf(m, fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w)));
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i < n4) {
+      v[k].x = exp2f((v[k].x - m) * kLog2e);
+      v[k].y = exp2f((v[k].y - m) * kLog2e);
+      v[k].z = exp2f((v[k].z - m) * kLog2e);
+      v[k].w = exp2f((v[k].w - m) * kLog2e);
+      s += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+    }
+  }
+  const float mloc = m;
+  block_max_sum<NT>(m, s);
+  const float f = (mloc == -INFINITY ? 0.f : exp2f((mloc - m) * kLog2e)) / s;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i < n4) {
+      float4 o = v[k];
+      o.x *= f; o.y *= f; o.z *= f; o.w *= f;
+      y[i] = o;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(1024) softmax_stream_kernel(const float *in, float *out, int64_t T,
+                                                              float scale) {
+  const int64_t row = blockIdx.x;
+  const float *x = in + row * T;
+  float *y = out + row * T;
+  float m = -INFINITY, s = 0.f;
+  for (int64_t i = threadIdx.x; i < T; i += 1024) {
+    const float z = scale * x[i];
+    if (z > m) {
+      s = (m == -INFINITY ? 0.f : s * exp2f((m - z) * kLog2e)) + 1.f;
+      m = z;
+    } else {
+      s += exp2f((z - m) * kLog2e);
+    }
+  }
+  block_max_sum<1024>(m, s);
+  const float inv = 1.f / s;
+  for (int64_t i = threadIdx.x; i < T; i += 1024) y[i] = exp2f((scale * x[i] - m) * kLog2e) * inv;
 }
 
 }  // namespace
@@ -432,7 +499,17 @@ int launch_softmax(const float *logits, int64_t rows, int64_t T, float scale, fl
                    hipStream_t stream) {
   if (rows == 0 || T == 0) return TQ_OK;
   if (rows > 0x7fffffff) return TQ_ENOTSUP;
-  softmax_kernel<<<(unsigned)rows, 256, 0, stream>>>(logits, probs, T, scale);
+  const bool vec = (T % 4 == 0) && ((uintptr_t)logits % 16 == 0) && ((uintptr_t)probs % 16 == 0);
+  const unsigned g = (unsigned)rows;
+  if (vec && T <= 256 * 4 * 4) {
+    softmax_reg_kernel<256, 4><<<g, 256, 0, stream>>>(logits, probs, T, scale);
+  } else if (vec && T <= 256 * 4 * 32) {
+    softmax_reg_kernel<256, 32><<<g, 256, 0, stream>>>(logits, probs, T, scale);
+  } else if (vec && T <= 1024 * 4 * 16) {
+    softmax_reg_kernel<1024, 16><<<g, 1024, 0, stream>>>(logits, probs, T, scale);
+  } else {
+    softmax_stream_kernel<<<g, 1024, 0, stream>>>(logits, probs, T, scale);
+  }
   return hip_status();
 }
 

@@ -98,7 +98,8 @@ def test_scores_deterministic(tq):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("rows,T,scale", [(5, 1000, 0.125), (3, 33, 1.0), (2, 1, 0.5), (1, 70000, 0.088)])
+@pytest.mark.parametrize("rows,T,scale", [(5, 1000, 0.125), (3, 33, 1.0), (2, 1, 0.5), (1, 70000, 0.088),
+                                         (4, 32768, 0.088), (2, 40000, 0.088), (3, 4096, 0.2)])
 def test_softmax_matches_oracle(tq, rows, T, scale):
     L = wl.gaussian((rows, T), 25 + T) * 30.0
     lt = torch.from_numpy(L).cuda()

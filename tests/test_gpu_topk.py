@@ -1,0 +1,108 @@
+"""GPU parity: tq_topk (fused estimator + top-k) against the oracle.
+
+Acceptance with ties (several correct lists exist when scores tie within the
+tolerance): at every rank r the oracle score of the GPU's id is within
+tolerance of the oracle's r-th score, and the GPU and oracle id sets differ
+only in ids whose oracle scores are within tolerance of the k-th score.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oblivious_kv_cache_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+ATOL, RTOL = 1e-4, 1e-3
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from oblivious_kv_cache_amd import binding
+    return binding
+
+
+def check_topk(gpu_ids, gpu_scores, oracle_scores, k):
+    """oracle_scores: [nq, n] float64 oracle estimator scores."""
+    ref_ids, ref_vals = O.topk(oracle_scores, k)
+    for qi in range(len(gpu_ids)):
+        g = gpu_ids[qi]
+        assert len(set(g.tolist())) == k, "duplicate ids"
+        sc = oracle_scores[qi]
+        tol = ATOL + RTOL * np.abs(ref_vals[qi])
+        assert (np.abs(sc[g] - ref_vals[qi]) <= tol).all(), (qi, sc[g] - ref_vals[qi])
+        assert (np.abs(gpu_scores[qi] - sc[g]) <= ATOL + RTOL * np.abs(sc[g])).all()
+        kth = ref_vals[qi][-1]
+        for i in set(g.tolist()) ^ set(ref_ids[qi].tolist()):
+            assert abs(sc[i] - kth) <= ATOL + RTOL * abs(kth), (qi, i, sc[i], kth)
+
+
+def _setup(tq, d, bits, nq, n, seed, records="oracle"):
+    p = O.make_params(d, bits, 0)
+    ctx = tq.Context(d, bits, 0)
+    if records == "oracle":
+        X = wl.power_law(n, d, seed=seed, unit=True)
+        rec = O.quantize(p, X)
+    else:
+        c, s, nu, g = wl.random_records(n, ctx.code_bytes, ctx.sign_bytes, seed)
+        rec = {"codes": c, "signs": s, "norms": nu, "rnorms": g}
+    Q = wl.power_law(nq, d, seed=seed + 1, unit=True)
+    return p, ctx, rec, Q
+
+
+def _run(tq, ctx, Q, rec, k):
+    dev = torch.device("cuda")
+    drec = {key: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for key, v in rec.items()}
+    ids, sc = tq.tq_topk(ctx, torch.from_numpy(Q).to(dev), drec, k)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), sc.cpu().numpy()
+
+
+@pytest.mark.parametrize("d,bits,nq,n,k", [
+    (200, 2, 7, 1000, 10), (200, 4, 9, 1500, 10), (128, 3, 4, 777, 1), (128, 3, 5, 3000, 16),
+    (200, 2, 3, 2000, 17), (64, 3, 6, 500, 64), (128, 2, 2, 64, 64), (200, 4, 1, 65, 10),
+])
+def test_topk_matches_oracle(tq, d, bits, nq, n, k):
+    p, ctx, rec, Q = _setup(tq, d, bits, nq, n, seed=d + n)
+    print(f"topk d={d} b={bits} nq={nq} n={n} k={k}", flush=True)
+    ids, sc = _run(tq, ctx, Q, rec, k)
+    want = O.scores(p, Q.astype(np.float64), rec["codes"], rec["signs"], rec["norms"], rec["rnorms"])
+    check_topk(ids, sc, want, k)
+
+
+def test_topk_exact_ties_order_by_id(tq):
+    d, bits = 128, 3
+    p, ctx, rec, Q = _setup(tq, d, bits, 3, 200, seed=5)
+    for key in rec:                       # rows 150..199 repeat rows 0..49: exact score ties
+        rec[key] = rec[key].copy()
+        rec[key][150:200] = rec[key][0:50]
+    ids, sc = _run(tq, ctx, Q, rec, 20)
+    for qi in range(3):
+        for r in range(19):
+            assert sc[qi, r] > sc[qi, r + 1] or (sc[qi, r] == sc[qi, r + 1] and ids[qi, r] < ids[qi, r + 1])
+    want = O.scores(p, Q.astype(np.float64), rec["codes"], rec["signs"], rec["norms"], rec["rnorms"])
+    check_topk(ids, sc, want, 20)
+
+
+def test_topk_random_records_large_db(tq):
+    d, bits, nq, n, k = 200, 2, 12, 200000, 10
+    p, ctx, rec, Q = _setup(tq, d, bits, nq, n, seed=77, records="random")
+    ids, sc = _run(tq, ctx, Q, rec, k)
+    want = np.concatenate([O.scores(p, Q.astype(np.float64), rec["codes"][s:s + 50000], rec["signs"][s:s + 50000],
+                                    rec["norms"][s:s + 50000], rec["rnorms"][s:s + 50000])
+                           for s in range(0, n, 50000)], axis=1)
+    check_topk(ids, sc, want, k)
+
+
+def test_topk_errors(tq):
+    ctx = tq.Context(128, 3, 0)
+    rec = ctx.empty_records(10)
+    q = torch.zeros((2, 128), device="cuda")
+    with pytest.raises(tq.TQError):
+        tq.tq_topk(ctx, q, rec, 11)          # k > n
+    with pytest.raises(tq.TQError):
+        tq.tq_topk(ctx, q, rec, 65)          # k > TQ_MAX_TOPK
