@@ -12,7 +12,9 @@ The metric is logits per second over the whole step; the scores call is timed
 separately with HIP events on the launch stream for the roofline figure.
 
 Also reported (separate timed loops, not part of `value`): streaming quantize
-throughput on 2^20 anisotropic bf16 vectors at b = 2, 3, 4.
+throughput on 2^20 anisotropic bf16 vectors at b = 2, 3, 4; fused decode
+attention at 128K (keys 3-bit TurboQuant, values 3-bit MSE-only); top-10 vector
+search over 10^6 packed d=200 vectors for 10^4 queries with recall 1@k.
 
 Usage: python bench.py [--steps K] [--warmup W] [--bits 3] [--no-cpu] [--no-extra]
 """
@@ -75,6 +77,75 @@ def cpu_quantize_baseline(bits, n=16384):
     t0 = time.perf_counter()
     O.quantize(p, X)
     return n / (time.perf_counter() - t0)
+
+
+def _time(torch, fn, reps):
+    for _ in range(2):
+        fn()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def bench_attend(tq, wl, dev):
+    """Long-context decode at 128K: 4 x 8 KV heads x 131072 tokens, d=128, keys
+    3-bit TurboQuant, values 3-bit MSE-only, 32 query heads, fused logits +
+    softmax + value sum."""
+    import torch
+    B, Hkv, T, d, Hq = 4, 8, 131072, 128, 32
+    G, qpg = B * Hkv, Hq // Hkv
+    log("attend 128K: setup")
+    kctx, vctx = tq.Context(d, 3, 0), tq.Context(d, 3, 1, tq.TQ_MODE_MSE)
+    K, _ = wl.outlier_keys_torch(B, Hkv, T, d, seed=4, device=dev)
+    krec = tq.tq_quantize(kctx, K.view(G * T, d))
+    del K
+    V = wl.gaussian_torch((G * T, d), 44, dev, torch.bfloat16)
+    vrec = tq.tq_quantize(vctx, V)
+    del V
+    q = wl.gaussian_torch((B, Hq, d), 45, dev).view(G, qpg, d).contiguous()
+    ws = kctx.workspace(tq.TQ_OP_ATTEND, G, qpg, T, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    ms = _time(torch, lambda: tq.tq_attend(kctx, vctx, q, krec, vrec, scale, ws=ws), 10)
+    kv_bytes = G * T * (kctx.code_bytes + kctx.sign_bytes + 8 + vctx.code_bytes + 4)
+    r = {"ms": ms, "tokens_per_s": G * T / (ms / 1e3), "logits_per_s": G * qpg * T / (ms / 1e3),
+         "kv_bytes": kv_bytes, "alg_gbs": kv_bytes / (ms / 1e3) / 1e9,
+         "hbm_frac": kv_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+    log(f"  attend: {ms:.3f} ms, {r['alg_gbs']:.0f} GB/s of packed K+V")
+    return r
+
+
+def bench_topk(tq, wl, dev, nq=10000, n=1000000, d=200, k=10):
+    """Vector search: 10^6 unit-norm d=200 power-law database vectors, 10^4
+    queries, top-10 by the estimator, recall of the exact fp32 top-1."""
+    import torch
+    log("topk 10^6 x 10^4: setup")
+    DB = wl.power_law_torch(n, d, seed=5, device=dev, dtype=torch.float32, unit=True)
+    Q = wl.power_law_torch(nq, d, seed=6, device=dev, dtype=torch.float32, unit=True)
+    top1 = torch.empty(nq, dtype=torch.int64, device=dev)
+    for s0 in range(0, nq, 256):                      # exact fp32 brute force
+        top1[s0:s0 + 256] = (Q[s0:s0 + 256] @ DB.T).argmax(dim=1)
+    out = {}
+    for bits in (2, 4):
+        ctx = tq.Context(d, bits, 0)
+        rec = tq.tq_quantize(ctx, DB)
+        ws = ctx.workspace(tq.TQ_OP_TOPK, nq, n, k, device=dev)
+        ms_q = _time(torch, lambda: tq.tq_quantize(ctx, DB, out=rec), 3)
+        res = {}
+        ms = _time(torch, lambda: res.__setitem__("r", tq.tq_topk(ctx, Q, rec, k, ws=ws)), 3)
+        ids = res["r"][0]
+        rec_k = {str(kk): float((ids[:, :kk] == top1[:, None]).any(dim=1).float().mean()) for kk in (1, 2, 4, 8, 10)}
+        db_bytes = n * (ctx.code_bytes + ctx.sign_bytes + 8)
+        out[f"b{bits}"] = {"ms": ms, "pairs_per_s": nq * n / (ms / 1e3), "queries_per_s": nq / (ms / 1e3),
+                           "db_bytes": db_bytes, "db_quantize_ms": ms_q, "recall_1_at_k": rec_k}
+        log(f"  b={bits}: topk {ms:.2f} ms ({nq * n / (ms / 1e3):.3e} pairs/s), "
+            f"db quantize {ms_q:.3f} ms, recall1@k {rec_k}")
+        del rec, ws
+    return out
 
 
 def main():
@@ -184,6 +255,8 @@ def main():
             c2.close()
             del out
         extra["quantize_2p20"] = qz
+        extra["attend_128k"] = bench_attend(tq, wl, dev)
+        extra["topk_1e6"] = bench_topk(tq, wl, dev)
 
     cpu = None
     if not args.no_cpu:
