@@ -53,7 +53,7 @@ __global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
   __shared__ float lut[16];
   __shared__ float red[4][NT / 64];
   __shared__ float stat[4][2];
-  __shared__ float accs[16][4][129];                // token-stream partials (d <= 128)
+  __shared__ float accs[NT / 64][4][128];          // per-wave partials (d <= 128)
 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4, wv = tid >> 6;
   const int64_t gidx = blockIdx.y, kg = gidx / a.hg;
@@ -89,7 +89,8 @@ __global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int tl = tile * 64 + 16 * s + col;
-        const float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
+        float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
+        __asm__ volatile("" : "+v"(l));     // keep the norm loads ahead of the guarded stores
         if (tl < nval) {
           zt[grp][tl] = a.scale * l;
           if (a.logits && head < a.qpg) a.logits[(kg * a.qpg + head) * a.T + tbeg + tl] = l;
@@ -112,6 +113,7 @@ __global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
   }
   for (int t = nval + tid; t < CH; t += NT)
     for (int h = 0; h < 4; ++h) zt[h][t] = -INFINITY;
+  for (int i = tid; i < (NT / 64) * 4 * 128; i += NT) (&accs[0][0][0])[i] = 0.f;
   __syncthreads();
 
   // ---- B: chunk softmax statistics, weights
@@ -181,19 +183,35 @@ __global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
     }
   }
   __syncthreads();
-  // ---- D: sum the token streams, write the chunk partial
-  if (active) {
+  // ---- D: sum the token streams (lane groups by shuffles, waves via LDS)
+  const bool by_group = (lpt == 16);          // d == 128: the 4 streams are the 4 lane groups
+  if (by_group) {
 #pragma unroll
     for (int h = 0; h < 4; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) accs[sid][h][8 * j + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) {
+        float v = acc[h][e];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[h][e] = v;
+      }
+  }
+  if (active && (!by_group || stream == 0)) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (by_group) accs[wv][h][8 * j + e] = acc[h][e];
+        else atomicAdd(&accs[wv][h][8 * j + e], acc[h][e]);
+      }
   }
   __syncthreads();
   float *out = a.part + (gidx * a.nchunk + chunk) * 4 * (d + 2);
   for (int i = tid; i < 4 * d; i += NT) {
     const int h = i / d, c = i - h * d;
     float v = 0.f;
-    for (int s = 0; s < nstreams; ++s) v += accs[s][h][c];
+#pragma unroll
+    for (int s = 0; s < NT / 64; ++s) v += accs[s][h][c];
     out[h * (d + 2) + c] = v;
   }
   if (tid < 4) {
@@ -211,40 +229,70 @@ struct CombArgs {
   int qpg, hg, nchunk, d;
 };
 
-__global__ void __launch_bounds__(256) attend_combine_kernel(CombArgs a) {
+// One block per (group, head): chunk weights exp(m_c - M) in LDS, then 1024
+// threads = (1024 / d) chunk lanes x d coordinates sum the rescaled partials.
+constexpr int CT = 1024;
+constexpr int MAXCH_LDS = 8192;     // chunk weights held in LDS (T <= 4M tokens)
+
+__global__ void __launch_bounds__(CT) attend_combine_kernel(CombArgs a) {
   __shared__ float y[TQ_MAX_D];
-  __shared__ float ML[2];
+  __shared__ float wts[MAXCH_LDS];
+  __shared__ float red[CT / 64];
+  __shared__ float part_acc[CT];
+  const int tid = threadIdx.x;
   const int64_t gq = blockIdx.x;             // (group, head)
   const int64_t kg = gq / a.qpg;
   const int h = (int)(gq - kg * a.qpg);
   const int hgi = h / 4, hh = h % 4;
   const int d = a.d;
-  const float *p = a.part + ((kg * a.hg + hgi) * a.nchunk) * 4 * (d + 2) + hh * (d + 2);
   const int64_t cstride = 4 * (d + 2);
-  if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    for (int c = 0; c < a.nchunk; ++c) M = fmaxf(M, p[c * cstride + d]);
-    float L = 0.f;
-    for (int c = 0; c < a.nchunk; ++c) L += p[c * cstride + d + 1] * __expf(p[c * cstride + d] - M);
-    ML[0] = M;
-    ML[1] = L;
+  const float *p = a.part + ((kg * a.hg + hgi) * a.nchunk) * cstride + hh * (d + 2);
+  // global max over chunks
+  float m = -INFINITY;
+  for (int c = tid; c < a.nchunk; c += CT) m = fmaxf(m, p[c * cstride + d]);
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  float M = red[0];
+  for (int i = 1; i < CT / 64; ++i) M = fmaxf(M, red[i]);
+  __syncthreads();
+  // chunk weights and the total
+  float l = 0.f;
+  for (int c = tid; c < a.nchunk; c += CT) {
+    const float wc = __expf(p[c * cstride + d] - M);
+    wts[c] = wc;
+    l += p[c * cstride + d + 1] * wc;
+  }
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+  if ((tid & 63) == 0) red[tid >> 6] = l;
+  __syncthreads();
+  float L = 0.f;
+  for (int i = 0; i < CT / 64; ++i) L += red[i];
+  // rescaled sum of the partial vectors
+  const int lanes_c = CT / d;                // chunk lanes
+  const int ci = tid / d, i = tid - ci * d;
+  float v = 0.f;
+  if (ci < lanes_c) {
+#pragma unroll 4
+    for (int c = ci; c < a.nchunk; c += lanes_c) v = fmaf(p[c * cstride + i], wts[c], v);
+  }
+  part_acc[tid] = v;
+  __syncthreads();
+  if (tid < d) {
+    float s = 0.f;
+    for (int k = 0; k < lanes_c; ++k) s += part_acc[k * d + tid];
+    y[tid] = s / L;
   }
   __syncthreads();
-  const float M = ML[0], invL = 1.f / ML[1];
-  for (int i = threadIdx.x; i < d; i += 256) {
-    float v = 0.f;
-    for (int c = 0; c < a.nchunk; ++c) v += p[c * cstride + i] * __expf(p[c * cstride + d] - M);
-    y[i] = v * invL;
+  for (int jx = tid; jx < d; jx += CT) {      // out = Pi_v^T y
+    float o = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < d; ++r) o = fmaf(a.Piv[(int64_t)r * d + jx], y[r], o);
+    a.out[gq * d + jx] = o;
   }
-  __syncthreads();
-  for (int jx = threadIdx.x; jx < d; jx += 256) {      // out = Pi_v^T y
-    float v = 0.f;
-    for (int i = 0; i < d; ++i) v = fmaf(a.Piv[(int64_t)i * d + jx], y[i], v);
-    a.out[gq * d + jx] = v;
-  }
-  if (a.mstat && threadIdx.x == 0) {
+  if (a.mstat && tid == 0) {
     a.mstat[2 * gq] = M;
-    a.mstat[2 * gq + 1] = ML[1];
+    a.mstat[2 * gq + 1] = L;
   }
 }
 
@@ -293,7 +341,7 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   const int nm = mfma_count(cb16, sb16, w);
   const int64_t nchunk = (T + CH - 1) / CH;
   const int64_t groups = G * hg;
-  if (groups > 65535 || nchunk > 0x7fffffff) return TQ_ENOTSUP;
+  if (groups > 65535 || nchunk > MAXCH_LDS || G * qpg > 0x7fffffff) return TQ_ENOTSUP;
   uint8_t *base = reinterpret_cast<uint8_t *>(ws);
   uint8_t *prep = base;
   float *part = reinterpret_cast<float *>(base + align256(groups * prep_stride(nm)));
@@ -336,7 +384,7 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   c.hg = hg;
   c.nchunk = (int)nchunk;
   c.d = d;
-  attend_combine_kernel<<<(unsigned)(G * qpg), 256, 0, stream>>>(c);
+  attend_combine_kernel<<<(unsigned)(G * qpg), CT, 0, stream>>>(c);
   if (hip_status() != TQ_OK) return TQ_EHIP;
   if (probs) {
     const int64_t rows = G * qpg;

@@ -33,10 +33,10 @@ namespace {
 constexpr int PREP_THREADS = 256;
 
 #ifndef TQ_SCORES_PREFETCH
-#define TQ_SCORES_PREFETCH 0
+#define TQ_SCORES_PREFETCH 1
 #endif
 #ifndef TQ_SCORES_WAVES
-#define TQ_SCORES_WAVES 16384
+#define TQ_SCORES_WAVES 32768
 #endif
 
 struct PrepArgs {
@@ -272,32 +272,38 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   const bool head_ok = head < a.qpg;
   float *lrow = a.logits + ((int64_t)kg * a.qpg + (head_ok ? head : 0)) * a.T;
 
-  const uint8_t *cbase = a.codes + (int64_t)kg * a.ldk * a.cb;
-  const uint8_t *sbase = a.signs + (int64_t)kg * a.ldk * a.sb;
+  // Record strides are compile-time (code_bytes = 16 CB16, sign_bytes = 16 SB16)
+  // and per-token offsets are 32-bit from per-group base pointers, which keeps
+  // address arithmetic to a few shifts per load.
+  const uint8_t *cbase = a.codes + (int64_t)kg * a.ldk * (CB16 * 16);
+  const uint8_t *sbase = a.signs + (int64_t)kg * a.ldk * (SB16 * 16);
   const float *nbase = a.norms + (int64_t)kg * a.ldk;
   const float *rbase = a.rnorms + (int64_t)kg * a.ldk;
+  const int T = (int)a.T;                  // T < 2^31 is checked on the host
 
-  const int64_t tile0 = ((int64_t)blockIdx.x * 4 + wv) * a.tiles_per_wave;
-  int64_t ntile = a.tiles_per_wave;
-  const int64_t last = (a.T + 63) / 64;
+  const int tile0 = (blockIdx.x * 4 + wv) * a.tiles_per_wave;
+  int ntile = a.tiles_per_wave;
+  const int last = (T + 63) / 64;
   if (tile0 + ntile > last) ntile = last - tile0;
-  auto load_tile = [&](KeyWords<CB16, SB16, W> (&kw)[4], float (&nu)[4], float (&ga)[4], int64_t t0) {
+  auto load_tile = [&](KeyWords<CB16, SB16, W> (&kw)[4], float (&nu)[4], float (&ga)[4], int t0) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      int64_t t = t0 + 16 * s + col;
-      if (t >= a.T) t = a.T - 1;
-      load_key_words(kw[s], cbase + t * a.cb, sbase + t * a.sb, grp);
+      const int t = min(t0 + 16 * s + col, T - 1);
+      load_key_words(kw[s], cbase + (uint32_t)t * (CB16 * 16), sbase + (uint32_t)t * (SB16 * 16), grp);
       nu[s] = nbase[t];
       ga[s] = rbase[t];
     }
   };
   auto score_tile = [&](const KeyWords<CB16, SB16, W> (&kw)[4], const float (&nu)[4], const float (&ga)[4],
-                        int64_t t0) {
+                        int t0) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int64_t t = t0 + 16 * s + col;
-      const float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
-      if (head_ok && t < a.T) lrow[t] = l;
+      const int t = t0 + 16 * s + col;
+      float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
+      // Materialise l here: otherwise the compiler sinks the norm loads into
+      // the guarded store and waits on each of them in turn.
+      __asm__ volatile("" : "+v"(l));
+      if (head_ok && t < T) lrow[t] = l;
     }
   };
 #if TQ_SCORES_PREFETCH
@@ -305,7 +311,7 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   KeyWords<CB16, SB16, W> k0[4], k1[4];
   float n0[4], g0[4], n1[4], g1[4];
   if (ntile > 0) load_tile(k0, n0, g0, tile0 * 64);
-  for (int64_t it = 0; it < ntile; it += 2) {
+  for (int it = 0; it < ntile; it += 2) {
     if (it + 1 < ntile) load_tile(k1, n1, g1, (tile0 + it + 1) * 64);
     score_tile(k0, n0, g0, (tile0 + it) * 64);
     if (it + 1 >= ntile) break;
@@ -313,7 +319,7 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
     score_tile(k1, n1, g1, (tile0 + it + 1) * 64);
   }
 #else
-  for (int64_t it = 0; it < ntile; ++it) {
+  for (int it = 0; it < ntile; ++it) {
     KeyWords<CB16, SB16, W> kw[4];
     float nu[4], ga[4];
     load_tile(kw, nu, ga, (tile0 + it) * 64);
@@ -370,7 +376,7 @@ int launch_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t
   const int hg = (qpg + 3) / 4;
   const int cb16 = ctx->code_bytes / 16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
   const int64_t groups = G * hg;
-  if (groups > 65535) return TQ_ENOTSUP;
+  if (groups > 65535 || T > 0x7fffffff - 64) return TQ_ENOTSUP;
   int st = launch_prep(ctx, q, groups, qpg, hg, G * qpg, reinterpret_cast<uint8_t *>(ws), stream);
   if (st != TQ_OK) return st;
 
