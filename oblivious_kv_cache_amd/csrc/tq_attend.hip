@@ -47,7 +47,7 @@ struct AttArgs {
 template <int CB16, int SB16, int W>
 __global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
   constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
-  __shared__ float zt[4][CH];                       // scaled logits, then weights
+  __shared__ __align__(16) float zt[CH][4];         // scaled logits, then weights, [token][head]
   __shared__ __align__(16) uint8_t vbytes[CH * VB_MAX + 16];
   __shared__ float vnu[CH];
   __shared__ float lut[16];
@@ -92,34 +92,44 @@ __global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
         float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
         __asm__ volatile("" : "+v"(l));     // keep the norm loads ahead of the guarded stores
         if (tl < nval) {
-          zt[grp][tl] = a.scale * l;
+          zt[tl][grp] = a.scale * l;
           if (a.logits && head < a.qpg) a.logits[(kg * a.qpg + head) * a.T + tbeg + tl] = l;
         }
       }
     }
   }
-  // stage value codes and norms of the chunk (16-byte loads, clamped rows)
+  // stage value codes and norms of the chunk: batches of independent 16-byte
+  // loads from clamped rows (rows past the cache end are never read back)
   {
-    const int n16 = CH * a.vcb / 16;
-    const uint8_t *src = a.vcodes + (kg * a.ldk + tbeg) * a.vcb;
-    const int lim = nval * a.vcb / 16;                 // valid 16-byte units
-    for (int i = tid; i < n16; i += NT) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (i < lim) v = reinterpret_cast<const uint4 *>(src)[i];
-      reinterpret_cast<uint4 *>(vbytes)[i] = v;
+    const int n16 = CH * a.vcb / 16;                    // multiple of NT (vcb % 16 == 0, CH = 2 NT)
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.vcodes + (kg * a.ldk + tbeg) * a.vcb);
+    const int lim = nval * a.vcb / 16 - 1;              // last valid 16-byte unit
+    for (int base = 0; base < n16; base += 4 * NT) {
+      uint4 v[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v[b] = src[min(base + b * NT + tid, lim)];
+      // unconditional stores: an index past the end rewrites the last unit
+      // with the value it already gets (both loads clamp to the same source)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) reinterpret_cast<uint4 *>(vbytes)[min(base + b * NT + tid, n16 - 1)] = v[b];
     }
-    for (int t = tid; t < CH; t += NT) vnu[t] = t < nval ? a.vnorms[kg * a.ldk + tbeg + t] : 0.f;
+    const float *vn = a.vnorms + kg * a.ldk + tbeg;
+    float nv[CH / NT];
+#pragma unroll
+    for (int b = 0; b < CH / NT; ++b) nv[b] = vn[min(b * NT + tid, nval - 1)];
+#pragma unroll
+    for (int b = 0; b < CH / NT; ++b) vnu[b * NT + tid] = (b * NT + tid < nval) ? nv[b] : 0.f;
     if (tid < 16) lut[tid] = a.vc[tid & 15];
   }
   for (int t = nval + tid; t < CH; t += NT)
-    for (int h = 0; h < 4; ++h) zt[h][t] = -INFINITY;
+    for (int h = 0; h < 4; ++h) zt[t][h] = -INFINITY;
   for (int i = tid; i < (NT / 64) * 4 * 128; i += NT) (&accs[0][0][0])[i] = 0.f;
   __syncthreads();
 
   // ---- B: chunk softmax statistics, weights
   float mloc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   for (int t = tid; t < nval; t += NT)
-    for (int h = 0; h < 4; ++h) mloc[h] = fmaxf(mloc[h], zt[h][t]);
+    for (int h = 0; h < 4; ++h) mloc[h] = fmaxf(mloc[h], zt[t][h]);
   for (int h = 0; h < 4; ++h) {
     float v = mloc[h];
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -135,9 +145,9 @@ __global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
   float sloc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int t = tid; t < CH; t += NT) {
     for (int h = 0; h < 4; ++h) {
-      const float p = t < nval ? __expf(zt[h][t] - stat[h][0]) : 0.f;
+      const float p = t < nval ? __expf(zt[t][h] - stat[h][0]) : 0.f;
       sloc[h] += p;
-      zt[h][t] = p * vnu[t];
+      zt[t][h] = p * vnu[t];
     }
   }
   for (int h = 0; h < 4; ++h) {
@@ -171,7 +181,8 @@ __global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
     for (int t = sid; t < nval; t += nstreams) {
       const uint32_t *rec = reinterpret_cast<const uint32_t *>(vbytes + t * a.vcb);
       const uint32_t bits = __builtin_amdgcn_alignbit(rec[dw0 + 1], rec[dw0], sh);
-      const float w0 = zt[0][t], w1 = zt[1][t], w2 = zt[2][t], w3 = zt[3][t];
+      const float4 wq = *reinterpret_cast<const float4 *>(&zt[t][0]);
+      const float w0 = wq.x, w1 = wq.y, w2 = wq.z, w3 = wq.w;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float c = lut[(bits >> (e * vw)) & mask];
