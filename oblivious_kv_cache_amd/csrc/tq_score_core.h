@@ -106,6 +106,39 @@ __device__ __forceinline__ float tile_logit(const i32x4 *A, const KeyWords<CB16,
   return nu * fmaf(alpha * gamma, Q, P);
 }
 
+// Wave-wide sum / max with DPP row permutes (quad swaps, half-row and row
+// mirrors make every lane of a 16-lane row hold the row result) and four
+// readlanes; much shorter latency than a chain of ds_bpermute shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp_f<0xb1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4e>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);   // row_half_mirror
+  v += dpp_f<0x140>(v);   // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp_f<0xb1>(v));
+  v = fmaxf(v, dpp_f<0x4e>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row_max(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
 // Expands a dispatch over the record geometries d <= 256 can produce:
 // (code words per lane group, sign words per lane group, code bits).
 #define TQ_FOR_EACH_GEOMETRY(X)                                              \

@@ -54,26 +54,6 @@ struct PrepArgs {
 // loads, so the query products do not wait on one global load at a time.
 constexpr int PREP_STAGE_FLOATS = 8192;   // 32 KB staging buffer
 
-__device__ inline float block_sum(float v, float *red) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float t = 0.f;
-  for (int i = 0; i < PREP_THREADS / 64; ++i) t += red[i];
-  return t;
-}
-
-__device__ inline float block_max(float v, float *red) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float t = 0.f;
-  for (int i = 0; i < PREP_THREADS / 64; ++i) t = fmaxf(t, red[i]);
-  return t;
-}
-
 // out[hh][i] = sum_j MT[j][i] * qv[hh][j]  for i < cols (MT row-major [d][cols])
 __device__ inline void apply_T(const float *MT, int d, int cols, const float (*qv)[TQ_MAX_D],
                                float (*out)[TQ_MAX_D], float *stage) {
@@ -107,25 +87,54 @@ __device__ inline void apply_T(const float *MT, int d, int cols, const float (*q
       }
     }
   }
-  if (tid < cols)
-    for (int hh = 0; hh < 4; ++hh) out[hh][tid] = acc[hh];
+  if (tid < cols) {
+    out[0][tid] = acc[0];
+    out[1][tid] = acc[1];
+    out[2][tid] = acc[2];
+    out[3][tid] = acc[3];
+  }
 }
 
+// out[hh][i] = sum_j MT[j][i] * qv[hh][j] with MT (row-major [d][cols]) already in LDS
+__device__ inline void project_lds(const float *MT, int d, int cols, const float (*qv)[TQ_MAX_D],
+                                   float (*out)[TQ_MAX_D]) {
+  const int tid = threadIdx.x;
+  if (tid < cols) {
+    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < d; ++j) {
+      const float m = MT[j * cols + tid];
+      acc0 = fmaf(m, qv[0][j], acc0);
+      acc1 = fmaf(m, qv[1][j], acc1);
+      acc2 = fmaf(m, qv[2][j], acc2);
+      acc3 = fmaf(m, qv[3][j], acc3);
+    }
+    out[0][tid] = acc0; out[1][tid] = acc1; out[2][tid] = acc2; out[3][tid] = acc3;
+  }
+}
+
+#ifndef TQ_PREP_WAVES_PER_EU
+#define TQ_PREP_WAVES_PER_EU 0
+#endif
+#if TQ_PREP_WAVES_PER_EU
+__global__ void __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) prep_kernel(PrepArgs a) {
+#else
 __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
+#endif
   __shared__ float qv[4][TQ_MAX_D];
   __shared__ float qr[4][TQ_MAX_D];
   __shared__ float qs[4][TQ_MAX_D];
   __shared__ float vP[4][2 * 96 * 8];     // code-bit + parity-bit coefficients
   __shared__ float vQ[4][32 * 8];         // sign-bit coefficients
-  __shared__ __align__(16) float stage[PREP_STAGE_FLOATS];
-  __shared__ float red[PREP_THREADS / 64];
+  __shared__ __align__(16) float stage[2 * PREP_STAGE_FLOATS];
+  __shared__ float red[PREP_THREADS / 64][16];
   __shared__ float scal[4][2];
   __shared__ float sums[4][2];
   __shared__ float basis[4];
 
   const int gidx = blockIdx.x;           // = group * hg + head group
   const int grp = gidx / a.hg, hgi = gidx - grp * a.hg;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int d = a.d, m = a.m;
   const int ncb = a.cb * 8, nsb = a.sb * 8;
   // Kernel-argument fields are copied to LDS / scalars once: indexing them
@@ -140,19 +149,60 @@ __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
     const int64_t flat = (int64_t)grp * a.qpg + h;
     qv[hh][j] = (h < a.qpg && flat < a.nq_total) ? a.q[flat * d + j] : 0.f;
   }
-  __syncthreads();
-  // q_rot = Pi q (PiT[j][i] = Pi[i][j]), q_s = S q (ST[j][i] = S[i][j])
-  apply_T(a.PiT, d, d, qv, qr, stage);
-  apply_T(a.ST, d, m, qv, qs, stage);
+  if (d <= 128) {
+    // Pi^T and S^T (64 KB each at d = 128) fetched in one batch of 16-byte
+    // loads per thread, then projected from LDS: one memory round trip.
+    constexpr int B4 = 2 * PREP_STAGE_FLOATS / 4 / PREP_THREADS;     // float4s per thread per matrix
+    const int n4p = d * d / 4, n4s = d * m / 4;
+    const float4 *sp = reinterpret_cast<const float4 *>(a.PiT);
+    const float4 *ss = reinterpret_cast<const float4 *>(a.ST);
+    float4 *st4 = reinterpret_cast<float4 *>(stage);
+    // unconditional clamped loads and stores: no branch, so every load of the
+    // batch is in flight before the first LDS store waits
+#pragma unroll
+    for (int b = 0; b < B4; ++b) {
+      const int i = min(b * PREP_THREADS + tid, n4p - 1);
+      st4[i] = sp[i];
+    }
+    __syncthreads();
+    project_lds(stage, d, d, qv, qr);
+    __syncthreads();
+    if (m) {
+#pragma unroll
+      for (int b = 0; b < B4; ++b) {
+        const int i = min(b * PREP_THREADS + tid, n4s - 1);
+        st4[i] = ss[i];
+      }
+      __syncthreads();
+      project_lds(stage, d, m, qv, qs);
+    }
+  } else {
+    __syncthreads();
+    apply_T(a.PiT, d, d, qv, qr, stage);
+    apply_T(a.ST, d, m, qv, qs, stage);
+  }
   __syncthreads();
 
-  // per-head sums of q_rot and q_s (for the +-1 -> bit conversion)
-  for (int hh = 0; hh < 4; ++hh) {
-    const float s1 = block_sum(tid < d ? qr[hh][tid] : 0.f, red);
-    const float s2 = block_sum(tid < m ? qs[hh][tid] : 0.f, red);
-    if (tid == 0) {
-      sums[hh][0] = s1;
-      sums[hh][1] = s2;
+  // per-head sums of q_rot and q_s (for the +-1 -> bit conversion), one pass
+  {
+    float v[8];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      v[2 * hh] = 0.f;
+      v[2 * hh + 1] = 0.f;
+      for (int i = tid; i < d; i += PREP_THREADS) v[2 * hh] += qr[hh][i];
+      for (int i = tid; i < m; i += PREP_THREADS) v[2 * hh + 1] += qs[hh][i];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float t = wave_sum(v[k]);
+      if (lane == 0) red[wv][k] = t;
+    }
+    __syncthreads();
+    if (tid < 8) {
+      float t = 0.f;
+      for (int i = 0; i < PREP_THREADS / 64; ++i) t += red[i][tid];
+      sums[tid >> 1][tid & 1] = t;
     }
   }
 
@@ -176,19 +226,30 @@ __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
   }
   __syncthreads();
 
-  // per (head, chain) maxima of |v| 2^-j -> digit scale 127 / max
-  for (int hh = 0; hh < 4; ++hh) {
-    float mp = 0.f, mq = 0.f;
-    for (int k = tid; k < ncb + npar; k += PREP_THREADS) mp = fmaxf(mp, ldexpf(fabsf(vP[hh][k]), -(k & 7)));
-    for (int k = tid; k < nsb; k += PREP_THREADS) mq = fmaxf(mq, ldexpf(fabsf(vQ[hh][k]), -(k & 7)));
-    mp = block_max(mp, red);
-    mq = block_max(mq, red);
-    if (tid == 0) {
-      scal[hh][0] = mp > 0.f ? 127.f / mp : 1.f;
-      scal[hh][1] = mq > 0.f ? 127.f / mq : 1.f;
+  // per (head, chain) maxima of |v| 2^-j -> digit scale 127 / max, one pass
+  {
+    float v[8];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      float mp = 0.f, mq = 0.f;
+      for (int k = tid; k < ncb + npar; k += PREP_THREADS) mp = fmaxf(mp, ldexpf(fabsf(vP[hh][k]), -(k & 7)));
+      for (int k = tid; k < nsb; k += PREP_THREADS) mq = fmaxf(mq, ldexpf(fabsf(vQ[hh][k]), -(k & 7)));
+      v[2 * hh] = mp;
+      v[2 * hh + 1] = mq;
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float t = wave_max(v[k]);
+      if (lane == 0) red[wv][8 + k] = t;
+    }
+    __syncthreads();
+    if (tid < 8) {
+      float t = 0.f;
+      for (int i = 0; i < PREP_THREADS / 64; ++i) t = fmaxf(t, red[i][8 + tid]);
+      scal[tid >> 1][tid & 1] = t > 0.f ? 127.f / t : 1.f;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   uint8_t *out = a.ws + (int64_t)gidx * prep_stride(a.nm);
   // A fragments: dword index = (mu * 64 + lane) * 4 + e
@@ -221,12 +282,15 @@ __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
       const int bitpos = 32 * word + 8 * b + j;
       float u = ldexpf(vv[bitpos] * S, -j);
       if (j == 7) u = -u;                 // B byte value is -128 for bit 7
-      int dig = 0;
-      for (int t = 0; t <= digit; ++t) {
-        const float r = rintf(u);
-        dig = (int)r;
-        u = (u - r) * 128.f;
-      }
+      // base-128 digits, all four computed and one selected (no per-lane loop)
+      const float r0 = rintf(u);
+      u = (u - r0) * 128.f;
+      const float r1 = rintf(u);
+      u = (u - r1) * 128.f;
+      const float r2 = rintf(u);
+      u = (u - r2) * 128.f;
+      const float r3 = rintf(u);
+      const int dig = (int)(digit == 0 ? r0 : digit == 1 ? r1 : digit == 2 ? r2 : r3);
       dw |= ((uint32_t)(uint8_t)(int8_t)dig) << (8 * b);
     }
     reinterpret_cast<uint32_t *>(out)[i] = dw;
@@ -412,25 +476,30 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// (max, sum-of-exp) pairs merged over the block: rows of 16 lanes by DPP
+// (rescaling each partner's sum to the larger max), then through LDS.
+__device__ inline void merge_ms(float &m, float &s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  s = (m == -INFINITY ? 0.f : s * exp2f((m - mm) * kLog2e)) + (m2 == -INFINITY ? 0.f : s2 * exp2f((m2 - mm) * kLog2e));
+  m = mm;
+}
+
 template <int NT>
 __device__ inline void block_max_sum(float &m, float &s) {
-  __shared__ float sm[NT / 64], ss[NT / 64];
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-    const float mm = fmaxf(m, m2);
-    s = (m == -INFINITY ? 0.f : s * exp2f((m - mm) * kLog2e)) +
-        (m2 == -INFINITY ? 0.f : s2 * exp2f((m2 - mm) * kLog2e));
-    m = mm;
-  }
-  if ((threadIdx.x & 63) == 0) {
-    sm[threadIdx.x >> 6] = m;
-    ss[threadIdx.x >> 6] = s;
+  __shared__ float sm[NT / 16], ss[NT / 16];
+  merge_ms(m, s, dpp_f<0xb1>(m), dpp_f<0xb1>(s));
+  merge_ms(m, s, dpp_f<0x4e>(m), dpp_f<0x4e>(s));
+  merge_ms(m, s, dpp_f<0x141>(m), dpp_f<0x141>(s));
+  merge_ms(m, s, dpp_f<0x140>(m), dpp_f<0x140>(s));
+  if ((threadIdx.x & 15) == 0) {
+    sm[threadIdx.x >> 4] = m;
+    ss[threadIdx.x >> 4] = s;
   }
   __syncthreads();
   float M = sm[0];
-  for (int i = 1; i < NT / 64; ++i) M = fmaxf(M, sm[i]);
+  for (int i = 1; i < NT / 16; ++i) M = fmaxf(M, sm[i]);
   float S = 0.f;
-  for (int i = 0; i < NT / 64; ++i) S += sm[i] == -INFINITY ? 0.f : ss[i] * exp2f((sm[i] - M) * kLog2e);
+  for (int i = 0; i < NT / 16; ++i) S += sm[i] == -INFINITY ? 0.f : ss[i] * exp2f((sm[i] - M) * kLog2e);
   m = M;
   s = S;
 }

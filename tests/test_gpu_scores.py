@@ -9,7 +9,7 @@ import pytest
 
 import oracle as O
 from oblivious_kv_cache_amd import workloads as wl
-from parity import assert_close
+from parity import ATOL, assert_close
 
 pytestmark = pytest.mark.gpu
 
@@ -83,7 +83,10 @@ def test_scores_zero_norm_keys_and_large_queries(tq):
     Q = wl.gaussian((1, 4, d), 23) * 30.0
     got = _score(tq, ctx, Q, rec, 1, 300, 300)
     want = _oracle_grouped(p, Q, rec, 1, 300, 300)
-    assert_close(got, want, what="logits")
+    # the logit is linear in the key norm and in the query, so scaling keys by
+    # 50 and queries by 30 scales the absolute tolerance (stated for unit-scale
+    # inputs) by 1500; the relative part is unchanged
+    assert_close(got, want, atol=ATOL * 50.0 * 30.0, what="logits")
     assert (got[0][:, ::7] == 0).all()
 
 
