@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
       for (int s = 0; s < 4; ++s) {
         int64_t t = tbeg + tile * 64 + 16 * s + col;
         if (t >= a.T) t = a.T - 1;
-        load_key_words(kw[s], cb + t * a.kcb, sb + t * a.ksb, grp);
+        load_key_words<true>(kw[s], cb + t * a.kcb, sb + t * a.ksb, grp);
         nu[s] = nb[t];
         ga[s] = rb[t];
       }
@@ -107,7 +107,11 @@ __global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
     for (int base = 0; base < n16; base += 4 * NT) {
       uint4 v[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) v[b] = src[min(base + b * NT + tid, lim)];
+      for (int b = 0; b < 4; ++b) {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src) + min(base + b * NT + tid, lim));
+        v[b] = make_uint4(t.x, t.y, t.z, t.w);
+      }
       // unconditional stores: an index past the end rewrites the last unit
       // with the value it already gets (both loads clamp to the same source)
 #pragma unroll

@@ -80,25 +80,33 @@ __global__ void __launch_bounds__(USE_LDS ? 512 : 256) quantize_kernel(QArgs a) 
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
 
   if constexpr (USE_LDS) {
-    // Fill LDS with batches of independent 16-byte loads per thread, one
-    // operand matrix at a time (the matrix pointer stays a scalar; choosing it
-    // with a runtime index would re-load it from the kernel arguments).
+    // Fill LDS with one batch of independent 16-byte loads per thread over
+    // all operand matrices (each matrix pointer stays a scalar; choosing it
+    // with a runtime index would re-load it from the kernel arguments), then
+    // store: one memory round trip.  Clamped indices keep the loads free of
+    // branches; a duplicate store of the last element rewrites the same value.
     constexpr int NF = FR * 64;
     constexpr int ITER = (NF + 511) / 512;        // USE_LDS launches 512 threads
-    auto fill = [&](const Frag *src, int which) {
-      Frag tmp[ITER];
-      // Clamped indices: no branch, so all loads are issued before the first
-      // wait; a duplicate store of the last element rewrites the same value.
+    // Without the sketch (MSE-only contexts) slots 2 and 3 receive a second
+    // copy of Pi's fragments, unused: the loads stay unconditional.
+    const Frag *const s0 = a.PiA_hi, *const s1 = a.PiA_lo;
+    const Frag *const s2 = a.prod ? a.S2A_hi : a.PiA_hi, *const s3 = a.prod ? a.S2A_lo : a.PiA_lo;
+    Frag t0[ITER], t1[ITER], t2[ITER], t3[ITER];
 #pragma unroll
-      for (int b = 0; b < ITER; ++b) tmp[b] = src[min(b * 512 + (int)threadIdx.x, NF - 1)];
+    for (int b = 0; b < ITER; ++b) {
+      const int i = min(b * 512 + (int)threadIdx.x, NF - 1);
+      t0[b] = s0[i];
+      t1[b] = s1[i];
+      t2[b] = s2[i];
+      t3[b] = s3[i];
+    }
 #pragma unroll
-      for (int b = 0; b < ITER; ++b) lds[which * NF + min(b * 512 + (int)threadIdx.x, NF - 1)] = tmp[b];
-    };
-    fill(a.PiA_hi, 0);
-    fill(a.PiA_lo, 1);
-    if (a.prod) {
-      fill(a.S2A_hi, 2);
-      fill(a.S2A_lo, 3);
+    for (int b = 0; b < ITER; ++b) {
+      const int i = min(b * 512 + (int)threadIdx.x, NF - 1);
+      lds[i] = t0[b];
+      lds[NF + i] = t1[b];
+      lds[2 * NF + i] = t2[b];
+      lds[3 * NF + i] = t3[b];
     }
     __syncthreads();
   }

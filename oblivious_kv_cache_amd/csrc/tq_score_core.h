@@ -35,19 +35,31 @@ struct KeyWords {
   uint32_t sw[SB16];
 };
 
-template <int CB16, int SB16, int W>
+// Streaming keys (scores, attention) are read once per call and are loaded
+// with the non-temporal hint: they then do not evict lines that are about to
+// be reused, such as the logits a following softmax reads.  A database that
+// many query blocks re-read (top-k) uses ordinary loads.
+template <bool NT>
+__device__ __forceinline__ uint32_t key_word(const uint32_t *p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+template <bool NT, int CB16, int SB16, int W>
 __device__ __forceinline__ void load_key_words(KeyWords<CB16, SB16, W> &k, const uint8_t *crec,
                                                const uint8_t *srec, int grp) {
   const uint32_t *cp = reinterpret_cast<const uint32_t *>(crec + grp * (CB16 * 4));
 #pragma unroll
-  for (int i = 0; i < CB16; ++i) k.cw[i] = cp[i];
+  for (int i = 0; i < CB16; ++i) k.cw[i] = key_word<NT>(cp + i);
   if constexpr (W == 3) {   // first word of the next lane group's chunk (none for the last group)
-    const uint32_t nxt = cp[grp < 3 ? CB16 : CB16 - 1];
+    const uint32_t nxt = key_word<NT>(cp + (grp < 3 ? CB16 : CB16 - 1));
     k.cw[CB16] = grp < 3 ? nxt : 0u;
   }
   const uint32_t *sp = reinterpret_cast<const uint32_t *>(srec + grp * (SB16 * 4));
 #pragma unroll
-  for (int i = 0; i < SB16; ++i) k.sw[i] = sp[i];
+  for (int i = 0; i < SB16; ++i) k.sw[i] = key_word<NT>(sp + i);
 }
 
 __device__ __forceinline__ i32x4 mfma8(const i32x4 &a, const i32x4 &b, const i32x4 &c) {

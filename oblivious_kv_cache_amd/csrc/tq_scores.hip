@@ -35,6 +35,12 @@ constexpr int PREP_THREADS = 256;
 #ifndef TQ_SCORES_PREFETCH
 #define TQ_SCORES_PREFETCH 1
 #endif
+#ifndef TQ_NT_LOGITS
+#define TQ_NT_LOGITS 0
+#endif
+#ifndef TQ_SOFTMAX_NT
+#define TQ_SOFTMAX_NT 512     // threads per row for rows of up to 32768 values
+#endif
 #ifndef TQ_SCORES_WAVES
 #define TQ_SCORES_WAVES 32768
 #endif
@@ -50,98 +56,45 @@ struct PrepArgs {
 };
 
 // Build the int8 A fragments and per-head constants for one (group, head group).
-// Pi^T and S^T are staged through LDS in row chunks with 16-byte cooperative
-// loads, so the query products do not wait on one global load at a time.
-constexpr int PREP_STAGE_FLOATS = 8192;   // 32 KB staging buffer
-
-// out[hh][i] = sum_j MT[j][i] * qv[hh][j]  for i < cols (MT row-major [d][cols])
-__device__ inline void apply_T(const float *MT, int d, int cols, const float (*qv)[TQ_MAX_D],
-                               float (*out)[TQ_MAX_D], float *stage) {
-  const int tid = threadIdx.x;
-  const int rows_per = PREP_STAGE_FLOATS / cols;           // rows of MT per chunk
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < d; j0 += rows_per) {
-    const int nr = min(rows_per, d - j0);
-    const int n4 = nr * cols / 4;                           // cols % 8 == 0
-    const float4 *src = reinterpret_cast<const float4 *>(MT + (int64_t)j0 * cols);
-    __syncthreads();
-    for (int base = 0; base < n4; base += 8 * PREP_THREADS) {   // 8 loads in flight per thread
-      float4 tmp[8];
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {     // branch-free: clamped index
-        tmp[b] = src[min(base + b * PREP_THREADS + tid, n4 - 1)];
-      }
-#pragma unroll
-      for (int b = 0; b < 8; ++b)       // duplicate stores at the clamp rewrite one value
-        reinterpret_cast<float4 *>(stage)[min(base + b * PREP_THREADS + tid, n4 - 1)] = tmp[b];
-    }
-    __syncthreads();
-    if (tid < cols) {
-#pragma unroll 8
-      for (int j = 0; j < nr; ++j) {
-        const float m = stage[j * cols + tid];
-        acc[0] = fmaf(m, qv[0][j0 + j], acc[0]);
-        acc[1] = fmaf(m, qv[1][j0 + j], acc[1]);
-        acc[2] = fmaf(m, qv[2][j0 + j], acc[2]);
-        acc[3] = fmaf(m, qv[3][j0 + j], acc[3]);
-      }
-    }
-  }
-  if (tid < cols) {
-    out[0][tid] = acc[0];
-    out[1][tid] = acc[1];
-    out[2][tid] = acc[2];
-    out[3][tid] = acc[3];
-  }
-}
-
-// out[hh][i] = sum_j MT[j][i] * qv[hh][j] with MT (row-major [d][cols]) already in LDS
-__device__ inline void project_lds(const float *MT, int d, int cols, const float (*qv)[TQ_MAX_D],
-                                   float (*out)[TQ_MAX_D]) {
-  const int tid = threadIdx.x;
-  if (tid < cols) {
-    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < d; ++j) {
-      const float m = MT[j * cols + tid];
-      acc0 = fmaf(m, qv[0][j], acc0);
-      acc1 = fmaf(m, qv[1][j], acc1);
-      acc2 = fmaf(m, qv[2][j], acc2);
-      acc3 = fmaf(m, qv[3][j], acc3);
-    }
-    out[0][tid] = acc0; out[1][tid] = acc1; out[2][tid] = acc2; out[3][tid] = acc3;
-  }
-}
-
-#ifndef TQ_PREP_WAVES_PER_EU
-#define TQ_PREP_WAVES_PER_EU 0
-#endif
-#if TQ_PREP_WAVES_PER_EU
-__global__ void __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) prep_kernel(PrepArgs a) {
-#else
+//
+// The kernel is latency-bound (one block per group, a few microseconds each),
+// so it is laid out for few round trips and few barriers:
+//   * every thread owns one output coordinate of one projection (Pi q or S q,
+//     all 4 heads) and loads that column of Pi^T / S^T straight into registers
+//     with one batch of coalesced loads, issued before the queries arrive;
+//   * the owner of a coordinate writes its bit coefficients and keeps the
+//     partial sums and scaled maxima; one DPP + LDS reduction serves both;
+//   * the fragments are written after the second (and last) barrier.
+// d <= 128: threads [0, 128) project with Pi, [128, 256) with S, at once, and
+// JC (>= d) is the column length; d > 128: both projections in turn, each in
+// row chunks of JC.
+template <int JC, bool SPLIT>
 __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
-#endif
-  __shared__ float qv[4][TQ_MAX_D];
-  __shared__ float qr[4][TQ_MAX_D];
-  __shared__ float qs[4][TQ_MAX_D];
+  __shared__ __align__(16) float qv[4][TQ_MAX_D];
   __shared__ float vP[4][2 * 96 * 8];     // code-bit + parity-bit coefficients
   __shared__ float vQ[4][32 * 8];         // sign-bit coefficients
-  __shared__ __align__(16) float stage[2 * PREP_STAGE_FLOATS];
   __shared__ float red[PREP_THREADS / 64][16];
-  __shared__ float scal[4][2];
-  __shared__ float sums[4][2];
-  __shared__ float basis[4];
 
   const int gidx = blockIdx.x;           // = group * hg + head group
   const int grp = gidx / a.hg, hgi = gidx - grp * a.hg;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int d = a.d, m = a.m;
+  const int d = a.d, m = a.m, w = a.w;
   const int ncb = a.cb * 8, nsb = a.sb * 8;
-  // Kernel-argument fields are copied to LDS / scalars once: indexing them
-  // with a runtime value makes the compiler re-load them from the kernarg
-  // segment (a full memory round trip) on every use.
-  if (tid < 4) basis[tid] = tid == 0 ? a.basis[0] : tid == 1 ? a.basis[1] : tid == 2 ? a.basis[2] : a.basis[3];
-  const int w = a.w, cwpl = a.cb / 16, swpl = a.sb / 16;
+  const int npar = w == 3 ? ncb : 0;
+  const int cwpl = a.cb / 16, swpl = a.sb / 16;
+
+  // column loads first (they do not depend on the queries)
+  const int mat0 = SPLIT ? (tid >> 7) : 0;
+  const int col = SPLIT ? (tid & 127) : tid;
+  float mc[JC];
+  auto load_col = [&](int mat, int j0) {
+    const float *MT = mat ? a.ST : a.PiT;
+    const int cols = mat ? m : d;
+    const int c = min(col, max(cols, 1) - 1);
+#pragma unroll
+    for (int j = 0; j < JC; ++j) mc[j] = MT[(int64_t)min(j0 + j, d - 1) * cols + c];
+  };
+  if (SPLIT && (mat0 == 0 || m > 0)) load_col(mat0, 0);
 
   for (int i = tid; i < 4 * d; i += PREP_THREADS) {
     const int hh = i / d, j = i - hh * d;
@@ -149,135 +102,112 @@ __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
     const int64_t flat = (int64_t)grp * a.qpg + h;
     qv[hh][j] = (h < a.qpg && flat < a.nq_total) ? a.q[flat * d + j] : 0.f;
   }
-  if (d <= 128) {
-    // Pi^T and S^T (64 KB each at d = 128) fetched in one batch of 16-byte
-    // loads per thread, then projected from LDS: one memory round trip.
-    constexpr int B4 = 2 * PREP_STAGE_FLOATS / 4 / PREP_THREADS;     // float4s per thread per matrix
-    const int n4p = d * d / 4, n4s = d * m / 4;
-    const float4 *sp = reinterpret_cast<const float4 *>(a.PiT);
-    const float4 *ss = reinterpret_cast<const float4 *>(a.ST);
-    float4 *st4 = reinterpret_cast<float4 *>(stage);
-    // unconditional clamped loads and stores: no branch, so every load of the
-    // batch is in flight before the first LDS store waits
+  for (int i = tid; i < 4 * (ncb + npar); i += PREP_THREADS) (&vP[0][0])[(i / (ncb + npar)) * (2 * 96 * 8) + i % (ncb + npar)] = 0.f;
+  for (int i = tid; i < 4 * nsb; i += PREP_THREADS) (&vQ[0][0])[(i / nsb) * (32 * 8) + i % nsb] = 0.f;
+  __syncthreads();
+
+  // per thread: sums (P: code chain, Q: sign chain) and maxima of |v| 2^-(bit & 7)
+  float sP[4] = {0.f, 0.f, 0.f, 0.f}, sQ[4] = {0.f, 0.f, 0.f, 0.f};
+  float mP[4] = {0.f, 0.f, 0.f, 0.f}, mQ[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int mat = mat0; mat < (SPLIT ? mat0 + 1 : 2); ++mat) {
+    const int cols = mat ? m : d;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < (SPLIT ? 1 : d); j0 += JC) {
+      if (!SPLIT) load_col(mat, j0);
 #pragma unroll
-    for (int b = 0; b < B4; ++b) {
-      const int i = min(b * PREP_THREADS + tid, n4p - 1);
-      st4[i] = sp[i];
-    }
-    __syncthreads();
-    project_lds(stage, d, d, qv, qr);
-    __syncthreads();
-    if (m) {
+      for (int j = 0; j < JC; j += 4) {
+        if (j0 + j < d) {               // d % 8 == 0; rows past d are skipped
 #pragma unroll
-      for (int b = 0; b < B4; ++b) {
-        const int i = min(b * PREP_THREADS + tid, n4s - 1);
-        st4[i] = ss[i];
+          for (int hh = 0; hh < 4; ++hh) {
+            const float4 qq = *reinterpret_cast<const float4 *>(&qv[hh][j0 + j]);
+            acc[hh] = fmaf(mc[j], qq.x, acc[hh]);
+            acc[hh] = fmaf(mc[j + 1], qq.y, acc[hh]);
+            acc[hh] = fmaf(mc[j + 2], qq.z, acc[hh]);
+            acc[hh] = fmaf(mc[j + 3], qq.w, acc[hh]);
+          }
+        }
       }
-      __syncthreads();
-      project_lds(stage, d, m, qv, qs);
     }
-  } else {
-    __syncthreads();
-    apply_T(a.PiT, d, d, qv, qr, stage);
-    apply_T(a.ST, d, m, qv, qs, stage);
+    if (col < cols) {
+      if (mat == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+          sP[hh] = acc[hh];
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            if (p < w) {
+              const int pos = col * w + p;
+              const float v = 2.f * a.basis[p] * acc[hh];
+              vP[hh][pos] = v;
+              mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(v), -(pos & 7)));
+            }
+          }
+          if (w == 3) {
+            const int pos = 3 * col;
+            const float v = 2.f * a.basis[3] * acc[hh];
+            vP[hh][ncb + pos] = v;
+            mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(v), -(pos & 7)));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+          sQ[hh] = acc[hh];
+          const float v = 2.f * acc[hh];
+          vQ[hh][col] = v;
+          mQ[hh] = ldexpf(fabsf(v), -(col & 7));
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    const float t0 = wave_sum(sP[hh]), t1 = wave_sum(sQ[hh]);
+    const float t2 = wave_max(mP[hh]), t3 = wave_max(mQ[hh]);
+    if (lane == 0) {
+      red[wv][2 * hh] = t0;
+      red[wv][2 * hh + 1] = t1;
+      red[wv][8 + 2 * hh] = t2;
+      red[wv][8 + 2 * hh + 1] = t3;
+    }
   }
   __syncthreads();
-
-  // per-head sums of q_rot and q_s (for the +-1 -> bit conversion), one pass
-  {
-    float v[8];
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      v[2 * hh] = 0.f;
-      v[2 * hh + 1] = 0.f;
-      for (int i = tid; i < d; i += PREP_THREADS) v[2 * hh] += qr[hh][i];
-      for (int i = tid; i < m; i += PREP_THREADS) v[2 * hh + 1] += qs[hh][i];
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float t = wave_sum(v[k]);
-      if (lane == 0) red[wv][k] = t;
-    }
-    __syncthreads();
-    if (tid < 8) {
-      float t = 0.f;
-      for (int i = 0; i < PREP_THREADS / 64; ++i) t += red[i][tid];
-      sums[tid >> 1][tid & 1] = t;
-    }
-  }
-
-  // coefficients of every bit position
-  const int npar = w == 3 ? ncb : 0;
-  for (int i = tid; i < 4 * (ncb + npar); i += PREP_THREADS) {
-    const int hh = i / (ncb + npar), k = i - hh * (ncb + npar);
-    float v = 0.f;
-    if (k < ncb) {
-      const int coord = k / w, plane = k - coord * w;
-      if (coord < d) v = 2.f * basis[plane] * qr[hh][coord];
-    } else {
-      const int kk = k - ncb;
-      if (kk % 3 == 0 && kk / 3 < d) v = 2.f * basis[3] * qr[hh][kk / 3];
-    }
-    vP[hh][k] = v;
-  }
-  for (int i = tid; i < 4 * nsb; i += PREP_THREADS) {
-    const int hh = i / nsb, k = i - hh * nsb;
-    vQ[hh][k] = k < m ? 2.f * qs[hh][k] : 0.f;
-  }
-  __syncthreads();
-
-  // per (head, chain) maxima of |v| 2^-j -> digit scale 127 / max, one pass
-  {
-    float v[8];
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      float mp = 0.f, mq = 0.f;
-      for (int k = tid; k < ncb + npar; k += PREP_THREADS) mp = fmaxf(mp, ldexpf(fabsf(vP[hh][k]), -(k & 7)));
-      for (int k = tid; k < nsb; k += PREP_THREADS) mq = fmaxf(mq, ldexpf(fabsf(vQ[hh][k]), -(k & 7)));
-      v[2 * hh] = mp;
-      v[2 * hh + 1] = mq;
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float t = wave_max(v[k]);
-      if (lane == 0) red[wv][8 + k] = t;
-    }
-    __syncthreads();
-    if (tid < 8) {
-      float t = 0.f;
-      for (int i = 0; i < PREP_THREADS / 64; ++i) t = fmaxf(t, red[i][8 + tid]);
-      scal[tid >> 1][tid & 1] = t > 0.f ? 127.f / t : 1.f;
-    }
-    __syncthreads();
-  }
 
   uint8_t *out = a.ws + (int64_t)gidx * prep_stride(a.nm);
-  // A fragments: dword index = (mu * 64 + lane) * 4 + e
-  const int ndw = a.nm * 64 * 4;
+  // A fragments: dword index i = (mu * 64 + lane) * 4 + e; thread tid writes
+  // dword tid of every mu, so its lane (row -> head, digit) and e are fixed
+  const int flane = tid >> 2, e = tid & 3;
+  const int row = flane & 15, g = flane >> 4;
+  const int hh = row >> 2, digit = row & 3;
+  float mx0 = 0.f, mx1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < PREP_THREADS / 64; ++i) {
+    mx0 = fmaxf(mx0, red[i][8 + 2 * hh]);
+    mx1 = fmaxf(mx1, red[i][8 + 2 * hh + 1]);
+  }
+  const float sc0 = mx0 > 0.f ? 127.f / mx0 : 1.f, sc1 = mx1 > 0.f ? 127.f / mx1 : 1.f;
   const int nmc = 2 * cwpl, nmp = w == 3 ? nmc : 0;
-  for (int i = tid; i < ndw; i += PREP_THREADS) {
-    const int mu = i >> 8, lane = (i >> 2) & 63, e = i & 3;
-    const int row = lane & 15, g = lane >> 4;
-    const int hh = row >> 2, digit = row & 3;
-    int chain, mloc, wpl;
+  for (int mu = 0; mu < a.nm; ++mu) {
+    int mloc, wpl;
     const float *vv;
+    float S;
     if (mu < nmc + nmp) {
-      chain = 0;
       const bool par = mu >= nmc;
       mloc = par ? mu - nmc : mu;
       wpl = cwpl;
       vv = vP[hh] + (par ? ncb : 0);
+      S = sc0;
     } else {
-      chain = 1;
       mloc = mu - nmc - nmp;
       wpl = swpl;
       vv = vQ[hh];
+      S = sc1;
     }
     const int pair = mloc >> 1, half = mloc & 1;
     const int word = g * wpl + pair;
     const int j = 4 * half + e;
-    const float S = scal[hh][chain];
     uint32_t dw = 0u;
+#pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int bitpos = 32 * word + 8 * b + j;
       float u = ldexpf(vv[bitpos] * S, -j);
@@ -293,17 +223,25 @@ __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
       const int dig = (int)(digit == 0 ? r0 : digit == 1 ? r1 : digit == 2 ? r2 : r3);
       dw |= ((uint32_t)(uint8_t)(int8_t)dig) << (8 * b);
     }
-    reinterpret_cast<uint32_t *>(out)[i] = dw;
+    reinterpret_cast<uint32_t *>(out)[mu * 256 + tid] = dw;
   }
   // constants per head: invS_P, invS_Q, K_P, K_Q
   if (tid < 4) {
-    const int hh = tid;
-    const float bsum = basis[0] + (w >= 2 ? basis[1] : 0.f) + (w >= 3 ? basis[2] + basis[3] : 0.f);
+    const int h4 = tid;
+    float s0 = 0.f, s1 = 0.f, x0 = 0.f, x1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < PREP_THREADS / 64; ++i) {
+      s0 += red[i][2 * h4];
+      s1 += red[i][2 * h4 + 1];
+      x0 = fmaxf(x0, red[i][8 + 2 * h4]);
+      x1 = fmaxf(x1, red[i][8 + 2 * h4 + 1]);
+    }
+    const float bsum = a.basis[0] + (w >= 2 ? a.basis[1] : 0.f) + (w >= 3 ? a.basis[2] + a.basis[3] : 0.f);
     float *cst = reinterpret_cast<float *>(out + (int64_t)a.nm * 1024);
-    cst[hh * 4 + 0] = 1.f / scal[hh][0];
-    cst[hh * 4 + 1] = 1.f / scal[hh][1];
-    cst[hh * 4 + 2] = bsum * sums[hh][0];
-    cst[hh * 4 + 3] = sums[hh][1];
+    cst[h4 * 4 + 0] = x0 > 0.f ? 1.f / (127.f / x0) : 1.f;
+    cst[h4 * 4 + 1] = x1 > 0.f ? 1.f / (127.f / x1) : 1.f;
+    cst[h4 * 4 + 2] = bsum * s0;
+    cst[h4 * 4 + 3] = s1;
   }
 }
 
@@ -353,7 +291,7 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int t = min(t0 + 16 * s + col, T - 1);
-      load_key_words(kw[s], cbase + (uint32_t)t * (CB16 * 16), sbase + (uint32_t)t * (SB16 * 16), grp);
+      load_key_words<true>(kw[s], cbase + (uint32_t)t * (CB16 * 16), sbase + (uint32_t)t * (SB16 * 16), grp);
       nu[s] = nbase[t];
       ga[s] = rbase[t];
     }
@@ -367,7 +305,11 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
       // Materialise l here: otherwise the compiler sinks the norm loads into
       // the guarded store and waits on each of them in turn.
       __asm__ volatile("" : "+v"(l));
+#if TQ_NT_LOGITS
+      if (head_ok && t < T) __builtin_nontemporal_store(l, lrow + t);
+#else
       if (head_ok && t < T) lrow[t] = l;
+#endif
     }
   };
 #if TQ_SCORES_PREFETCH
@@ -423,7 +365,15 @@ int launch_prep(const tq_ctx *ctx, const float *q, int64_t groups, int qpg, int 
   pa.nm = mfma_count(ctx->code_bytes / 16, ctx->sign_bytes / 16, ctx->hp.w);
   for (int i = 0; i < 4; ++i) pa.basis[i] = ctx->basis[i];
   if (groups > 0x7fffffff) return TQ_ENOTSUP;
-  prep_kernel<<<dim3((unsigned)groups), PREP_THREADS, 0, stream>>>(pa);
+  const dim3 grid((unsigned)groups);
+  if (pa.d <= 32)
+    prep_kernel<32, true><<<grid, PREP_THREADS, 0, stream>>>(pa);
+  else if (pa.d <= 64)
+    prep_kernel<64, true><<<grid, PREP_THREADS, 0, stream>>>(pa);
+  else if (pa.d <= 128)
+    prep_kernel<128, true><<<grid, PREP_THREADS, 0, stream>>>(pa);
+  else
+    prep_kernel<64, false><<<grid, PREP_THREADS, 0, stream>>>(pa);
   return hip_status();
 }
 
@@ -504,6 +454,9 @@ __device__ inline void block_max_sum(float &m, float &s) {
   s = S;
 }
 
+// Whole row in registers: one read, one write.  The loads are unconditional
+// (clamped index) so that all of them are in flight before the first use; the
+// elements past the row end are masked out of the max and the sum.
 template <int NT, int VPT>
 __global__ void __launch_bounds__(NT) softmax_reg_kernel(const float *in, float *out, int64_t T,
                                                           float scale) {
@@ -511,40 +464,35 @@ __global__ void __launch_bounds__(NT) softmax_reg_kernel(const float *in, float 
   const float4 *x = reinterpret_cast<const float4 *>(in + row * T);
   float4 *y = reinterpret_cast<float4 *>(out + row * T);
   const int n4 = (int)(T >> 2);
+  const int tid = threadIdx.x;
   float4 v[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) v[k] = x[min(tid + k * NT, n4 - 1)];
   float m = -INFINITY;
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    const int i = threadIdx.x + k * NT;
-    if (i < n4) {
-      v[k] = x[i];
-      v[k].x *= scale; v[k].y *= scale; v[k].z *= scale; v[k].w *= scale;
-      m = fmaxf(m, fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w)));
-    }
+    v[k].x *= scale; v[k].y *= scale; v[k].z *= scale; v[k].w *= scale;
+    const float mk = fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w));
+    m = tid + k * NT < n4 ? fmaxf(m, mk) : m;
   }
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    const int i = threadIdx.x + k * NT;
-    if (i < n4) {
-      v[k].x = exp2f((v[k].x - m) * kLog2e);
-      v[k].y = exp2f((v[k].y - m) * kLog2e);
-      v[k].z = exp2f((v[k].z - m) * kLog2e);
-      v[k].w = exp2f((v[k].w - m) * kLog2e);
-      s += (v[k].x + v[k].y) + (v[k].z + v[k].w);
-    }
+    v[k].x = exp2f((v[k].x - m) * kLog2e);
+    v[k].y = exp2f((v[k].y - m) * kLog2e);
+    v[k].z = exp2f((v[k].z - m) * kLog2e);
+    v[k].w = exp2f((v[k].w - m) * kLog2e);
+    const float sk = (v[k].x + v[k].y) + (v[k].z + v[k].w);
+    s += tid + k * NT < n4 ? sk : 0.f;
   }
   const float mloc = m;
   block_max_sum<NT>(m, s);
   const float f = (mloc == -INFINITY ? 0.f : exp2f((mloc - m) * kLog2e)) / s;
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    const int i = threadIdx.x + k * NT;
-    if (i < n4) {
-      float4 o = v[k];
-      o.x *= f; o.y *= f; o.z *= f; o.w *= f;
-      y[i] = o;
-    }
+    float4 o = v[k];
+    o.x *= f; o.y *= f; o.z *= f; o.w *= f;
+    if (tid + k * NT < n4) y[tid + k * NT] = o;
   }
 }
 
@@ -578,8 +526,8 @@ int launch_softmax(const float *logits, int64_t rows, int64_t T, float scale, fl
   const unsigned g = (unsigned)rows;
   if (vec && T <= 256 * 4 * 4) {
     softmax_reg_kernel<256, 4><<<g, 256, 0, stream>>>(logits, probs, T, scale);
-  } else if (vec && T <= 256 * 4 * 32) {
-    softmax_reg_kernel<256, 32><<<g, 256, 0, stream>>>(logits, probs, T, scale);
+  } else if (vec && T <= TQ_SOFTMAX_NT * 4 * (32768 / 4 / TQ_SOFTMAX_NT)) {
+    softmax_reg_kernel<TQ_SOFTMAX_NT, 32768 / 4 / TQ_SOFTMAX_NT><<<g, TQ_SOFTMAX_NT, 0, stream>>>(logits, probs, T, scale);
   } else if (vec && T <= 1024 * 4 * 16) {
     softmax_reg_kernel<1024, 16><<<g, 1024, 0, stream>>>(logits, probs, T, scale);
   } else {

@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(64 * scan_waves(KP)) topk_scan_kernel(ScanArgs
     for (int s = 0; s < 4; ++s) {
       int64_t t = t0 + 16 * s + col;
       if (t >= end) t = end - 1;
-      load_key_words(kw[s], a.codes + t * a.cb, a.signs + t * a.sb, grp);
+      load_key_words<false>(kw[s], a.codes + t * a.cb, a.signs + t * a.sb, grp);
       nu[s] = a.norms[t];
       ga[s] = a.rnorms[t];
     }
