@@ -19,6 +19,7 @@
 //     D. stream partials summed through LDS; (m, l, acc[d]) written out.
 //   combine kernel: merges chunks with the usual max rescaling, divides by
 //     the total, applies Pi_v^T; optionally normalises the logits to probs.
+#include <algorithm>
 #include <cfloat>
 
 #include "tq_score_core.h"
@@ -29,6 +30,9 @@ namespace {
 constexpr int CH = 512;            // tokens per chunk
 constexpr int NT = 256;            // threads per partial block
 constexpr int VB_MAX = 64;         // value code bytes per token handled (d <= 128 at 4 bits; 170 at 3)
+#ifndef TQ_ATT_BLOCKS
+#define TQ_ATT_BLOCKS 512          // partial blocks per call (2 per CU are resident)
+#endif
 
 struct AttArgs {
   const uint8_t *kcodes, *ksigns;
@@ -37,168 +41,221 @@ struct AttArgs {
   const float *vnorms;
   const uint8_t *prep;
   float *logits;                   // optional [G][qpg][T]
-  float *part;                     // [G*hg][nchunk][4][d + 2]
+  float *part;                     // [G*hg][nsplit][4][d + 2]
   int64_t T, ldk;
-  int qpg, hg, nchunk, d, kcb, ksb, vcb, vw;
+  int qpg, hg, nchunk, nsplit, cps, d, kcb, ksb, vcb, vw;
   float alpha, scale;
   float vc[16];                    // value centroids
 };
 
-template <int CB16, int SB16, int W>
-__global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
+// One block = one query group x one split (a run of `cps` chunks of CH
+// tokens), with an online softmax over the chunks: the running max M and the
+// value accumulators (rotated coordinates, in registers) are rescaled by
+// exp(M_old - M_new) whenever a chunk raises the max.  The key words, value
+// codes and value norms of chunk c+1 are loaded into registers while chunk c
+// is processed, so every block keeps its next ~50 KB in flight.
+#ifndef TQ_ATT_WAVES_PER_EU
+#define TQ_ATT_WAVES_PER_EU 2
+#endif
+template <int CB16, int SB16, int W, int VR>      // VR = value code bytes / 8 = 16-byte units per thread per chunk
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(TQ_ATT_WAVES_PER_EU)))
+attend_partial_kernel(AttArgs a) {
   constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
+  using KW = KeyWords<CB16, SB16, W>;
   __shared__ __align__(16) float zt[CH][4];         // scaled logits, then weights, [token][head]
   __shared__ __align__(16) uint8_t vbytes[CH * VB_MAX + 16];
   __shared__ float vnu[CH];
-  __shared__ float lut[16];
+  __shared__ float2 lut2[256];                       // (c[a], c[b]) for the code pair a | b << vw
   __shared__ float red[4][NT / 64];
-  __shared__ float stat[4][2];
   __shared__ float accs[NT / 64][4][128];          // per-wave partials (d <= 128)
 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4, wv = tid >> 6;
   const int64_t gidx = blockIdx.y, kg = gidx / a.hg;
   const int hgi = (int)(gidx - kg * a.hg);
-  const int chunk = blockIdx.x;
-  const int64_t tbeg = (int64_t)chunk * CH;
-  const int nval = (int)min((int64_t)CH, a.T - tbeg);
+  const int c_begin = blockIdx.x * a.cps;
+  const int c_end = min(c_begin + a.cps, a.nchunk);
   const int d = a.d;
+  const int64_t T = a.T;
 
-  // ---- A: logits of this chunk
+  const uint8_t *prep = a.prep + gidx * prep_stride(NM);
+  i32x4 A[NM];
+#pragma unroll
+  for (int mu = 0; mu < NM; ++mu) A[mu] = reinterpret_cast<const i32x4 *>(prep)[mu * 64 + lane];
+  const float *cst = reinterpret_cast<const float *>(prep + NM * 1024) + grp * 4;
+  const HeadConsts hc{cst[0], cst[1], cst[2], cst[3]};
+  const int head = hgi * 4 + grp;
+  const uint8_t *kcb = a.kcodes + kg * a.ldk * a.kcb;
+  const uint8_t *ksb = a.ksigns + kg * a.ldk * a.ksb;
+  const float *knb = a.knorms + kg * a.ldk, *krb = a.krnorms + kg * a.ldk;
+  const uint8_t *vcb = a.vcodes + kg * a.ldk * a.vcb;
+  const float *vnb = a.vnorms + kg * a.ldk;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
   {
-    const uint8_t *prep = a.prep + gidx * prep_stride(NM);
-    i32x4 A[NM];
-#pragma unroll
-    for (int mu = 0; mu < NM; ++mu) A[mu] = reinterpret_cast<const i32x4 *>(prep)[mu * 64 + lane];
-    const float *cst = reinterpret_cast<const float *>(prep + NM * 1024) + grp * 4;
-    const HeadConsts hc{cst[0], cst[1], cst[2], cst[3]};
-    const int head = hgi * 4 + grp;
-    const uint8_t *cb = a.kcodes + kg * a.ldk * a.kcb;
-    const uint8_t *sb = a.ksigns + kg * a.ldk * a.ksb;
-    const float *nb = a.knorms + kg * a.ldk, *rb = a.krnorms + kg * a.ldk;
-    for (int tile = wv; tile * 64 < nval; tile += NT / 64) {
-      KeyWords<CB16, SB16, W> kw[4];
-      float nu[4], ga[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        int64_t t = tbeg + tile * 64 + 16 * s + col;
-        if (t >= a.T) t = a.T - 1;
-        load_key_words<true>(kw[s], cb + t * a.kcb, sb + t * a.ksb, grp);
-        nu[s] = nb[t];
-        ga[s] = rb[t];
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int tl = tile * 64 + 16 * s + col;
-        float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
-        __asm__ volatile("" : "+v"(l));     // keep the norm loads ahead of the guarded stores
-        if (tl < nval) {
-          zt[tl][grp] = a.scale * l;
-          if (a.logits && head < a.qpg) a.logits[(kg * a.qpg + head) * a.T + tbeg + tl] = l;
-        }
-      }
-    }
-  }
-  // stage value codes and norms of the chunk: batches of independent 16-byte
-  // loads from clamped rows (rows past the cache end are never read back)
-  {
-    const int n16 = CH * a.vcb / 16;                    // multiple of NT (vcb % 16 == 0, CH = 2 NT)
-    const uint4 *src = reinterpret_cast<const uint4 *>(a.vcodes + (kg * a.ldk + tbeg) * a.vcb);
-    const int lim = nval * a.vcb / 16 - 1;              // last valid 16-byte unit
-    for (int base = 0; base < n16; base += 4 * NT) {
-      uint4 v[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src) + min(base + b * NT + tid, lim));
-        v[b] = make_uint4(t.x, t.y, t.z, t.w);
-      }
-      // unconditional stores: an index past the end rewrites the last unit
-      // with the value it already gets (both loads clamp to the same source)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) reinterpret_cast<uint4 *>(vbytes)[min(base + b * NT + tid, n16 - 1)] = v[b];
-    }
-    const float *vn = a.vnorms + kg * a.ldk + tbeg;
-    float nv[CH / NT];
-#pragma unroll
-    for (int b = 0; b < CH / NT; ++b) nv[b] = vn[min(b * NT + tid, nval - 1)];
-#pragma unroll
-    for (int b = 0; b < CH / NT; ++b) vnu[b * NT + tid] = (b * NT + tid < nval) ? nv[b] : 0.f;
+    const int vw = a.vw, np = 1 << (2 * vw);
+    __shared__ float lut[16];
     if (tid < 16) lut[tid] = a.vc[tid & 15];
+    __syncthreads();
+    for (int i = tid; i < np; i += NT) lut2[i] = make_float2(lut[i & ((1 << vw) - 1)], lut[i >> vw]);
   }
-  for (int t = nval + tid; t < CH; t += NT)
-    for (int h = 0; h < 4; ++h) zt[t][h] = -INFINITY;
   for (int i = tid; i < (NT / 64) * 4 * 128; i += NT) (&accs[0][0][0])[i] = 0.f;
-  __syncthreads();
 
-  // ---- B: chunk softmax statistics, weights
-  float mloc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  for (int t = tid; t < nval; t += NT)
-    for (int h = 0; h < 4; ++h) mloc[h] = fmaxf(mloc[h], zt[t][h]);
-  for (int h = 0; h < 4; ++h) {
-    float v = mloc[h];
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    if (lane == 0) red[h][wv] = v;
-  }
-  __syncthreads();
-  if (tid < 4) {
-    float v = red[tid][0];
-    for (int i = 1; i < NT / 64; ++i) v = fmaxf(v, red[tid][i]);
-    stat[tid][0] = v;
-  }
-  __syncthreads();
-  float sloc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int t = tid; t < CH; t += NT) {
-    for (int h = 0; h < 4; ++h) {
-      const float p = t < nval ? __expf(zt[t][h] - stat[h][0]) : 0.f;
-      sloc[h] += p;
-      zt[t][h] = p * vnu[t];
-    }
-  }
-  for (int h = 0; h < 4; ++h) {
-    float v = sloc[h];
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0) red[h][wv] = v;
-  }
-  __syncthreads();
-  if (tid < 4) {
-    float v = 0.f;
-    for (int i = 0; i < NT / 64; ++i) v += red[tid][i];
-    stat[tid][1] = v;
-  }
+  // registers of the chunk in flight
+  KW kw[2][4];
+  float knu[2][4], kga[2][4];
+  u32x4 vr[VR];
+  float vn[CH / NT];
+  auto issue = [&](int c) {
+    // 32-bit offsets from the group's base pointers (the host checks that a
+    // group's records span less than 4 GB) keep the address math short
+    const int tbeg = c * CH, tlast = (int)T - 1;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t t = (uint32_t)min(tbeg + (wv + 4 * tt) * 64 + 16 * s + col, tlast);
+        load_key_words<true>(kw[tt][s], kcb + t * (CB16 * 16), ksb + t * (SB16 * 16), grp);
+        knu[tt][s] = knb[t];
+        kga[tt][s] = krb[t];
+      }
+    // value codes: clamped 16-byte units (units past the cache end repeat the
+    // last real one and are never read back)
+    const uint32_t lim = (uint32_t)(min(CH, (int)T - tbeg) * (VR / 2)) - 1u;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(vcb + (uint32_t)tbeg * (VR * 8));
+#pragma unroll
+    for (int b = 0; b < VR; ++b) vr[b] = __builtin_nontemporal_load(src + min((uint32_t)(b * NT + tid), lim));
+#pragma unroll
+    for (int b = 0; b < CH / NT; ++b) vn[b] = vnb[(uint32_t)min(tbeg + b * NT + tid, tlast)];
+  };
 
-  // ---- C: value accumulation in rotated coordinates
-  const int lpt = d / 8;                     // lanes per token (8 coordinates each)
-  const int spw = min(64 / lpt, 4);          // token streams per wave (<= 16 per block)
+  // value-stream geometry: lanes own 8 rotated coordinates (one byte run of a
+  // record); token streams are split across lane groups and waves
+  // (d <= 128: at least 4 streams fit in a wave; 16 streams per block)
+  constexpr int SPW = 4, NSTREAM = SPW * (NT / 64);
+  const int lpt = d / 8;
   const int stream = lane / lpt, j = lane - stream * lpt;
-  const bool active = stream < spw;
-  const int nstreams = spw * (NT / 64);
-  const int sid = wv * spw + stream;
+  const bool active = stream < SPW;
+  const int sid = wv * SPW + stream;
+  const int vw = a.vw, boff = j * vw;
+  const int dw0 = boff >> 2, sh = 8 * (boff & 3);
+
+  float M[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
   float acc[4][8];
 #pragma unroll
   for (int h = 0; h < 4; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  if (active) {
-    const int vw = a.vw, boff = j * vw;       // this lane's byte run in a record
-    const int dw0 = boff >> 2, sh = 8 * (boff & 3);
-    const uint32_t mask = (1u << vw) - 1u;
-    for (int t = sid; t < nval; t += nstreams) {
-      const uint32_t *rec = reinterpret_cast<const uint32_t *>(vbytes + t * a.vcb);
-      const uint32_t bits = __builtin_amdgcn_alignbit(rec[dw0 + 1], rec[dw0], sh);
-      const float4 wq = *reinterpret_cast<const float4 *>(&zt[t][0]);
-      const float w0 = wq.x, w1 = wq.y, w2 = wq.z, w3 = wq.w;
+
+  issue(c_begin);
+  for (int c = c_begin; c < c_end; ++c) {
+    const int64_t tbeg = (int64_t)c * CH;
+    const int nval = (int)min((int64_t)CH, T - tbeg);
+    // ---- A: logits of the chunk; value codes and norms to LDS
+    // all eight 16-key logits first (independent MFMA chains interleave),
+    // then the stores
+    float lg[2][4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float c = lut[(bits >> (e * vw)) & mask];
-        acc[0][e] = fmaf(w0, c, acc[0][e]);
-        acc[1][e] = fmaf(w1, c, acc[1][e]);
-        acc[2][e] = fmaf(w2, c, acc[2][e]);
-        acc[3][e] = fmaf(w3, c, acc[3][e]);
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        lg[tt][s] = tile_logit<CB16, SB16, W>(A, kw[tt][s], knu[tt][s], kga[tt][s], a.alpha, hc);
+        __asm__ volatile("" : "+v"(lg[tt][s]));
+      }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int tl = (wv + 4 * tt) * 64 + 16 * s + col;
+        zt[tl][grp] = tl < nval ? a.scale * lg[tt][s] : -INFINITY;
+      }
+    if (a.logits && head < a.qpg) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int tl = (wv + 4 * tt) * 64 + 16 * s + col;
+          if (tl < nval) a.logits[(kg * a.qpg + head) * T + tbeg + tl] = lg[tt][s];
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < VR; ++b)
+      reinterpret_cast<u32x4 *>(vbytes)[b * NT + tid] = vr[b];
+#pragma unroll
+    for (int b = 0; b < CH / NT; ++b) vnu[b * NT + tid] = b * NT + tid < nval ? vn[b] : 0.f;
+    if (c + 1 < c_end) issue(c + 1);
+    __syncthreads();
+
+    // ---- B: chunk max, new running max, weights w_t = exp(z_t - M) nu_t
+    float f[4];
+    {
+      const float4 z0 = *reinterpret_cast<const float4 *>(&zt[tid][0]);
+      const float4 z1 = *reinterpret_cast<const float4 *>(&zt[tid + NT][0]);
+      const float mx[4] = {fmaxf(z0.x, z1.x), fmaxf(z0.y, z1.y), fmaxf(z0.z, z1.z), fmaxf(z0.w, z1.w)};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float t = wave_max(mx[h]);
+        if (lane == 0) red[h][wv] = t;
+      }
+      __syncthreads();
+      float p0[4], p1[4];
+      const float za[4] = {z0.x, z0.y, z0.z, z0.w}, zb[4] = {z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        float mc = red[h][0];
+#pragma unroll
+        for (int i = 1; i < NT / 64; ++i) mc = fmaxf(mc, red[h][i]);
+        const float mn = fmaxf(M[h], mc);
+        f[h] = M[h] == -INFINITY ? 0.f : __expf(M[h] - mn);
+        M[h] = mn;
+        p0[h] = __expf(za[h] - mn);
+        p1[h] = __expf(zb[h] - mn);
+        lsum[h] = fmaf(lsum[h], f[h], p0[h] + p1[h]);
+      }
+      const float n0 = vnu[tid], n1 = vnu[tid + NT];
+      *reinterpret_cast<float4 *>(&zt[tid][0]) = make_float4(p0[0] * n0, p0[1] * n0, p0[2] * n0, p0[3] * n0);
+      *reinterpret_cast<float4 *>(&zt[tid + NT][0]) = make_float4(p1[0] * n1, p1[1] * n1, p1[2] * n1, p1[3] * n1);
+    }
+    __syncthreads();
+
+    // ---- C: rescale the accumulators, add this chunk's weighted centroids
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= f[h];
+    if (active) {
+      // every token of the chunk: past nval the weights are 0 and the staged
+      // codes are copies of real ones; a fixed trip count lets the LDS reads
+      // of several tokens be in flight together
+#pragma unroll 4
+      for (int k = 0; k < CH / NSTREAM; ++k) {
+        const int t = sid + NSTREAM * k;
+        const uint32_t *rec = reinterpret_cast<const uint32_t *>(vbytes + t * a.vcb);
+        const uint32_t bits = __builtin_amdgcn_alignbit(rec[dw0 + 1], rec[dw0], sh);
+        const float4 wq = *reinterpret_cast<const float4 *>(&zt[t][0]);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float2 cv = lut2[__builtin_amdgcn_ubfe(bits, e * vw, 2 * vw)];
+          acc[0][e] = fmaf(wq.x, cv.x, acc[0][e]);
+          acc[1][e] = fmaf(wq.y, cv.x, acc[1][e]);
+          acc[2][e] = fmaf(wq.z, cv.x, acc[2][e]);
+          acc[3][e] = fmaf(wq.w, cv.x, acc[3][e]);
+          acc[0][e + 1] = fmaf(wq.x, cv.y, acc[0][e + 1]);
+          acc[1][e + 1] = fmaf(wq.y, cv.y, acc[1][e + 1]);
+          acc[2][e + 1] = fmaf(wq.z, cv.y, acc[2][e + 1]);
+          acc[3][e + 1] = fmaf(wq.w, cv.y, acc[3][e + 1]);
+        }
       }
     }
+    __syncthreads();      // zt, vbytes and red are rewritten by the next chunk
   }
-  __syncthreads();
-  // ---- D: sum the token streams (lane groups by shuffles, waves via LDS)
+
+  // ---- D: block totals: sums over threads, accumulators over token streams
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float t = wave_sum(lsum[h]);
+    if (lane == 0) red[h][wv] = t;
+  }
   const bool by_group = (lpt == 16);          // d == 128: the 4 streams are the 4 lane groups
   if (by_group) {
 #pragma unroll
@@ -221,17 +278,21 @@ __global__ void __launch_bounds__(NT) attend_partial_kernel(AttArgs a) {
       }
   }
   __syncthreads();
-  float *out = a.part + (gidx * a.nchunk + chunk) * 4 * (d + 2);
+  float *out = a.part + (gidx * a.nsplit + blockIdx.x) * 4 * (d + 2);
   for (int i = tid; i < 4 * d; i += NT) {
-    const int h = i / d, c = i - h * d;
+    const int h = i / d, cc = i - h * d;
     float v = 0.f;
 #pragma unroll
-    for (int s = 0; s < NT / 64; ++s) v += accs[s][h][c];
-    out[h * (d + 2) + c] = v;
+    for (int s = 0; s < NT / 64; ++s) v += accs[s][h][cc];
+    out[h * (d + 2) + cc] = v;
   }
   if (tid < 4) {
-    out[tid * (d + 2) + d] = stat[tid][0];
-    out[tid * (d + 2) + d + 1] = stat[tid][1];
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) l += red[tid][i];
+    const float mt = tid == 0 ? M[0] : tid == 1 ? M[1] : tid == 2 ? M[2] : M[3];
+    out[tid * (d + 2) + d] = mt;
+    out[tid * (d + 2) + d + 1] = l;
   }
 }
 
@@ -319,14 +380,23 @@ __global__ void __launch_bounds__(256) attend_probs_kernel(const float *logits, 
     probs[row * T + t] = __expf(scale * logits[row * T + t] - M) * invL;
 }
 
+// Key geometries d <= 128 produces (one sign word per lane group) x value
+// code sizes 16, 32, 48, 64 bytes.
 int dispatch(const AttArgs &a, dim3 grid, int cb16, int sb16, int w, hipStream_t s) {
-#define TQ_CASE(C, S, W_)                                         \
-  if (cb16 == C && sb16 == S && w == W_) {                        \
-    attend_partial_kernel<C, S, W_><<<grid, NT, 0, s>>>(a);       \
-    return hip_status();                                          \
+  const int vr = a.vcb / 8;
+#define TQ_CASE_V(C, S, W_, V)                                         \
+  if (vr == V) {                                                       \
+    attend_partial_kernel<C, S, W_, V><<<grid, NT, 0, s>>>(a);         \
+    return hip_status();                                               \
   }
-  TQ_FOR_EACH_GEOMETRY(TQ_CASE)
+#define TQ_CASE(C, S, W_)                                              \
+  if (cb16 == C && sb16 == S && w == W_) {                             \
+    TQ_CASE_V(C, S, W_, 2) TQ_CASE_V(C, S, W_, 4) TQ_CASE_V(C, S, W_, 6) TQ_CASE_V(C, S, W_, 8) \
+    return TQ_ENOTSUP;                                                 \
+  }
+  TQ_CASE(1, 1, 1) TQ_CASE(1, 1, 2) TQ_CASE(2, 1, 2) TQ_CASE(1, 1, 3) TQ_CASE(2, 1, 3) TQ_CASE(3, 1, 3)
 #undef TQ_CASE
+#undef TQ_CASE_V
   return TQ_ENOTSUP;
 }
 
@@ -356,7 +426,10 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   const int nm = mfma_count(cb16, sb16, w);
   const int64_t nchunk = (T + CH - 1) / CH;
   const int64_t groups = G * hg;
-  if (groups > 65535 || nchunk > MAXCH_LDS || G * qpg > 0x7fffffff) return TQ_ENOTSUP;
+  if (groups > 65535 || T > 0x7fffffff - CH || G * qpg > 0x7fffffff) return TQ_ENOTSUP;
+  // per-group record offsets are 32-bit in the partial kernel
+  const int64_t rec_max = std::max<int64_t>(std::max(kc->code_bytes, kc->sign_bytes), vc->code_bytes);
+  if (ldk * rec_max >= ((int64_t)1 << 32)) return TQ_ENOTSUP;
   uint8_t *base = reinterpret_cast<uint8_t *>(ws);
   uint8_t *prep = base;
   float *part = reinterpret_cast<float *>(base + align256(groups * prep_stride(nm)));
@@ -379,6 +452,12 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   a.qpg = qpg;
   a.hg = hg;
   a.nchunk = (int)nchunk;
+  // splits per query group: about TQ_ATT_BLOCKS blocks in all, equal runs of chunks
+  int64_t want = (TQ_ATT_BLOCKS + groups - 1) / groups;
+  if (want > nchunk) want = nchunk;
+  if (want < 1) want = 1;
+  a.cps = (int)((nchunk + want - 1) / want);
+  a.nsplit = (int)((nchunk + a.cps - 1) / a.cps);
   a.d = d;
   a.kcb = kc->code_bytes;
   a.ksb = kc->sign_bytes;
@@ -387,7 +466,7 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   a.alpha = kc->alpha;
   a.scale = scale;
   for (int i = 0; i < 16; ++i) a.vc[i] = vc->cf[i];
-  st = dispatch(a, dim3((unsigned)nchunk, (unsigned)groups), cb16, sb16, w, stream);
+  st = dispatch(a, dim3((unsigned)a.nsplit, (unsigned)groups), cb16, sb16, w, stream);
   if (st != TQ_OK) return st;
   CombArgs c{};
   c.part = part;
@@ -397,7 +476,7 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   c.G = G;
   c.qpg = qpg;
   c.hg = hg;
-  c.nchunk = (int)nchunk;
+  c.nchunk = a.nsplit;
   c.d = d;
   attend_combine_kernel<<<(unsigned)(G * qpg), CT, 0, stream>>>(c);
   if (hip_status() != TQ_OK) return TQ_EHIP;
