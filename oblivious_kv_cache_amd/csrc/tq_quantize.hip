@@ -379,6 +379,12 @@ int launch_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int6
       a.ntiles = (n + 31) / 32;
       return launch_d<64, true, 2>(a, w, bf16, stream);
     case 128:
+      // few vectors (e.g. one decode token per KV head): 16-vector tiles, so
+      // that twice as many waves share the work and each finishes sooner
+      if (n <= 4096) {
+        a.ntiles = (n + 15) / 16;
+        return launch_d<128, true, 1>(a, w, bf16, stream);
+      }
       a.ntiles = (n + 31) / 32;
       return launch_d<128, true, 2>(a, w, bf16, stream);
     case 256:

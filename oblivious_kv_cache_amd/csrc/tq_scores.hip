@@ -298,17 +298,22 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   };
   auto score_tile = [&](const KeyWords<CB16, SB16, W> (&kw)[4], const float (&nu)[4], const float (&ga)[4],
                         int t0) {
+    // the four 16-key logits first (their MFMA chains interleave), then the
+    // guarded stores; materialising l keeps the norm loads from being sunk
+    // into the stores' branches
+    float l[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      l[s] = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
+      __asm__ volatile("" : "+v"(l[s]));
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int t = t0 + 16 * s + col;
-      float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
-      // Materialise l here: otherwise the compiler sinks the norm loads into
-      // the guarded store and waits on each of them in turn.
-      __asm__ volatile("" : "+v"(l));
 #if TQ_NT_LOGITS
-      if (head_ok && t < T) __builtin_nontemporal_store(l, lrow + t);
+      if (head_ok && t < T) __builtin_nontemporal_store(l[s], lrow + t);
 #else
-      if (head_ok && t < T) lrow[t] = l;
+      if (head_ok && t < T) lrow[t] = l[s];
 #endif
     }
   };

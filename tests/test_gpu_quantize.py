@@ -53,6 +53,18 @@ def test_quantize_bf16_outlier_keys(tq, bits):
     check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_bf16_two_tile_path(tq, bits):
+    # d = 128 launches 16-vector tiles up to 4096 vectors and 32-vector tiles
+    # above; 6001 vectors take the second path with a ragged last tile
+    K, _ = wl.outlier_keys_np(1, 1, 6001, 128, seed=12)
+    X = wl.bf16_round(K.reshape(-1, 128))
+    print(f"quantize bf16 outlier keys n=6001 d=128 b={bits}", flush=True)
+    ctx, g, xin = _run(tq, 128, bits, X, dtype=torch.bfloat16)
+    p = O.make_params(128, bits, 0)
+    check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
+
+
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_quantize_mse_mode(tq, bits):
     X = wl.bf16_round(wl.gaussian((777, 128), 4))
