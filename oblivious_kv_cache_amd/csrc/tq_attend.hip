@@ -114,9 +114,9 @@ attend_partial_kernel(AttArgs a) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const uint32_t t = (uint32_t)min(tbeg + (wv + 4 * tt) * 64 + 16 * s + col, tlast);
-        load_key_words<true>(kw[tt][s], kcb + t * (CB16 * 16), ksb + t * (SB16 * 16), grp);
-        knu[tt][s] = knb[t];
-        kga[tt][s] = krb[t];
+        load_key_words<true>(kw[tt][s], kcb, ksb, t, grp);
+        knu[tt][s] = load_f32(knb, t);
+        kga[tt][s] = load_f32(krb, t);
       }
     // value codes: clamped 16-byte units (units past the cache end repeat the
     // last real one and are never read back)

@@ -47,19 +47,27 @@ __device__ __forceinline__ uint32_t key_word(const uint32_t *p) {
     return *p;
 }
 
+// Words of key t for lane group g: uniform base pointers plus 32-bit byte
+// offsets (t * record bytes + g * bytes per lane group), so the loads take
+// the scalar-base + 32-bit-offset address form with no 64-bit math per lane.
 template <bool NT, int CB16, int SB16, int W>
-__device__ __forceinline__ void load_key_words(KeyWords<CB16, SB16, W> &k, const uint8_t *crec,
-                                               const uint8_t *srec, int grp) {
-  const uint32_t *cp = reinterpret_cast<const uint32_t *>(crec + grp * (CB16 * 4));
+__device__ __forceinline__ void load_key_words(KeyWords<CB16, SB16, W> &k, const uint8_t *cbase,
+                                               const uint8_t *sbase, uint32_t t, int grp) {
+  const uint32_t co = t * (CB16 * 16) + (uint32_t)grp * (CB16 * 4);
+  const uint32_t so = t * (SB16 * 16) + (uint32_t)grp * (SB16 * 4);
 #pragma unroll
-  for (int i = 0; i < CB16; ++i) k.cw[i] = key_word<NT>(cp + i);
+  for (int i = 0; i < CB16; ++i) k.cw[i] = key_word<NT>(reinterpret_cast<const uint32_t *>(cbase + co + 4 * i));
   if constexpr (W == 3) {   // first word of the next lane group's chunk (none for the last group)
-    const uint32_t nxt = key_word<NT>(cp + (grp < 3 ? CB16 : CB16 - 1));
+    const uint32_t nxt = key_word<NT>(reinterpret_cast<const uint32_t *>(cbase + co + 4 * (grp < 3 ? CB16 : CB16 - 1)));
     k.cw[CB16] = grp < 3 ? nxt : 0u;
   }
-  const uint32_t *sp = reinterpret_cast<const uint32_t *>(srec + grp * (SB16 * 4));
 #pragma unroll
-  for (int i = 0; i < SB16; ++i) k.sw[i] = key_word<NT>(sp + i);
+  for (int i = 0; i < SB16; ++i) k.sw[i] = key_word<NT>(reinterpret_cast<const uint32_t *>(sbase + so + 4 * i));
+}
+
+// base[i] with a 32-bit byte offset (scalar base + 32-bit offset address form)
+__device__ __forceinline__ float load_f32(const float *base, uint32_t i) {
+  return *reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(base) + i * 4u);
 }
 
 __device__ __forceinline__ i32x4 mfma8(const i32x4 &a, const i32x4 &b, const i32x4 &c) {

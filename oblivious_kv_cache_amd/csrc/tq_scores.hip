@@ -38,6 +38,9 @@ constexpr int PREP_THREADS = 256;
 #ifndef TQ_NT_LOGITS
 #define TQ_NT_LOGITS 0
 #endif
+#ifndef TQ_SOFTMAX_NT_STORE
+#define TQ_SOFTMAX_NT_STORE 1   // probabilities stream out past the caches
+#endif
 #ifndef TQ_SOFTMAX_NT
 #define TQ_SOFTMAX_NT 512     // threads per row for rows of up to 32768 values
 #endif
@@ -290,10 +293,10 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   auto load_tile = [&](KeyWords<CB16, SB16, W> (&kw)[4], float (&nu)[4], float (&ga)[4], int t0) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int t = min(t0 + 16 * s + col, T - 1);
-      load_key_words<true>(kw[s], cbase + (uint32_t)t * (CB16 * 16), sbase + (uint32_t)t * (SB16 * 16), grp);
-      nu[s] = nbase[t];
-      ga[s] = rbase[t];
+      const uint32_t t = (uint32_t)min(t0 + 16 * s + col, T - 1);
+      load_key_words<true>(kw[s], cbase, sbase, t, grp);
+      nu[s] = load_f32(nbase, t);
+      ga[s] = load_f32(rbase, t);
     }
   };
   auto score_tile = [&](const KeyWords<CB16, SB16, W> (&kw)[4], const float (&nu)[4], const float (&ga)[4],
@@ -317,7 +320,23 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
 #endif
     }
   };
-#if TQ_SCORES_PREFETCH
+#if TQ_SCORES_PREFETCH == 2
+  // three named register sets: the two following tiles load while one is scored
+  KeyWords<CB16, SB16, W> k0[4], k1[4], k2[4];
+  float n0[4], g0[4], n1[4], g1[4], n2[4], g2[4];
+  if (ntile > 0) load_tile(k0, n0, g0, tile0 * 64);
+  if (ntile > 1) load_tile(k1, n1, g1, (tile0 + 1) * 64);
+  for (int it = 0; it < ntile; it += 3) {
+    if (it + 2 < ntile) load_tile(k2, n2, g2, (tile0 + it + 2) * 64);
+    score_tile(k0, n0, g0, (tile0 + it) * 64);
+    if (it + 1 >= ntile) break;
+    if (it + 3 < ntile) load_tile(k0, n0, g0, (tile0 + it + 3) * 64);
+    score_tile(k1, n1, g1, (tile0 + it + 1) * 64);
+    if (it + 2 >= ntile) break;
+    if (it + 4 < ntile) load_tile(k1, n1, g1, (tile0 + it + 4) * 64);
+    score_tile(k2, n2, g2, (tile0 + it + 2) * 64);
+  }
+#elif TQ_SCORES_PREFETCH
   // two named register sets: the next tile's words load while this one is scored
   KeyWords<CB16, SB16, W> k0[4], k1[4];
   float n0[4], g0[4], n1[4], g1[4];
@@ -396,6 +415,9 @@ int launch_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t
   const int cb16 = ctx->code_bytes / 16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
   const int64_t groups = G * hg;
   if (groups > 65535 || T > 0x7fffffff - 64) return TQ_ENOTSUP;
+  // per-group record offsets are 32-bit in the scores kernel
+  if (ldk * (int64_t)(ctx->code_bytes > ctx->sign_bytes ? ctx->code_bytes : ctx->sign_bytes) >= ((int64_t)1 << 32))
+    return TQ_ENOTSUP;
   int st = launch_prep(ctx, q, groups, qpg, hg, G * qpg, reinterpret_cast<uint8_t *>(ws), stream);
   if (st != TQ_OK) return st;
 
@@ -497,7 +519,14 @@ __global__ void __launch_bounds__(NT) softmax_reg_kernel(const float *in, float 
   for (int k = 0; k < VPT; ++k) {
     float4 o = v[k];
     o.x *= f; o.y *= f; o.z *= f; o.w *= f;
-    if (tid + k * NT < n4) y[tid + k * NT] = o;
+    if (tid + k * NT < n4) {
+#if TQ_SOFTMAX_NT_STORE
+      typedef float f32x4v __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(f32x4v{o.x, o.y, o.z, o.w}, reinterpret_cast<f32x4v *>(y) + tid + k * NT);
+#else
+      y[tid + k * NT] = o;
+#endif
+    }
   }
 }
 

@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(64 * scan_waves(KP)) topk_scan_kernel(ScanArgs
     for (int s = 0; s < 4; ++s) {
       int64_t t = t0 + 16 * s + col;
       if (t >= end) t = end - 1;
-      load_key_words<false>(kw[s], a.codes + t * a.cb, a.signs + t * a.sb, grp);
+      load_key_words<false>(kw[s], a.codes, a.signs, (uint32_t)t, grp);
       nu[s] = a.norms[t];
       ga[s] = a.rnorms[t];
     }
@@ -209,6 +209,9 @@ int launch_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const 
   float *cand_s = reinterpret_cast<float *>(base + align256(g.groups * prep_stride(nm)));
   int *cand_i = reinterpret_cast<int *>(reinterpret_cast<uint8_t *>(cand_s) + align256(nq * g.ncand * 4));
   if (n > INT_MAX || g.qblocks > 65535 || nq > 0x7fffffff) return TQ_ENOTSUP;
+  // record offsets are 32-bit in the scan kernel
+  if (n * (int64_t)(ctx->code_bytes > ctx->sign_bytes ? ctx->code_bytes : ctx->sign_bytes) >= ((int64_t)1 << 32))
+    return TQ_ENOTSUP;
   int st = launch_prep(ctx, q, g.groups, 4, 1, nq, prep, stream);
   if (st != TQ_OK) return st;
   ScanArgs a{};
