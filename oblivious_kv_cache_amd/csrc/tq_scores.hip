@@ -62,18 +62,19 @@ struct PrepArgs {
 //
 // The kernel is latency-bound (one block per group, a few microseconds each),
 // so it is laid out for few round trips and few barriers:
-//   * every thread owns one output coordinate of one projection (Pi q or S q,
-//     all 4 heads) and loads that column of Pi^T / S^T straight into registers
-//     with one batch of coalesced loads, issued before the queries arrive;
+//   * d <= 128: threads [0, 128) project with Pi, [128, 256) with S, at once;
+//     each loads a 4-column x JC/4-row block of Pi^T / S^T with one batch of
+//     16-byte loads issued before the queries arrive, and the column's owner
+//     adds the four row blocks' partial products;
+//   * d > 128: one column per thread, both projections in turn, rows in
+//     chunks of JC;
 //   * the owner of a coordinate writes its bit coefficients and keeps the
 //     partial sums and scaled maxima; one DPP + LDS reduction serves both;
-//   * the fragments are written after the second (and last) barrier.
-// d <= 128: threads [0, 128) project with Pi, [128, 256) with S, at once, and
-// JC (>= d) is the column length; d > 128: both projections in turn, each in
-// row chunks of JC.
+//   * the fragments are written after the last barrier.
 template <int JC, bool SPLIT>
 __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
-  __shared__ __align__(16) float qv[4][TQ_MAX_D];
+  __shared__ __align__(16) float qT[TQ_MAX_D][4];  // queries, [coordinate][head]
+  __shared__ __align__(16) float part[SPLIT ? 2 * 4 * 128 * 4 : 4];   // [matrix][row group][column][head]
   __shared__ float vP[4][2 * 96 * 8];     // code-bit + parity-bit coefficients
   __shared__ float vQ[4][32 * 8];         // sign-bit coefficients
   __shared__ float red[PREP_THREADS / 64][16];
@@ -86,47 +87,95 @@ __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
   const int npar = w == 3 ? ncb : 0;
   const int cwpl = a.cb / 16, swpl = a.sb / 16;
 
-  // column loads first (they do not depend on the queries)
+  // d <= 128: thread (matrix, column quad, row group) loads RPG rows x 4
+  // columns of Pi^T or S^T with 16-byte loads, issued before the queries
+  // arrive (RPG <= 32 loads in flight per thread)
+  constexpr int RPG = JC / 4;
   const int mat0 = SPLIT ? (tid >> 7) : 0;
   const int col = SPLIT ? (tid & 127) : tid;
-  float mc[JC];
-  auto load_col = [&](int mat, int j0) {
-    const float *MT = mat ? a.ST : a.PiT;
-    const int cols = mat ? m : d;
-    const int c = min(col, max(cols, 1) - 1);
+  const int quad = col & 31, rg = col >> 5;
+  float4 mq[SPLIT ? RPG : 1];
+  if constexpr (SPLIT) {
+    const float *MT = mat0 ? a.ST : a.PiT;
+    const int cols = mat0 ? m : d;
+    const int qc = min(quad, max(cols / 4, 1) - 1);
+    if (cols > 0) {
 #pragma unroll
-    for (int j = 0; j < JC; ++j) mc[j] = MT[(int64_t)min(j0 + j, d - 1) * cols + c];
-  };
-  if (SPLIT && (mat0 == 0 || m > 0)) load_col(mat0, 0);
+      for (int jj = 0; jj < RPG; ++jj)
+        mq[jj] = *reinterpret_cast<const float4 *>(MT + min(rg * RPG + jj, d - 1) * cols + 4 * qc);
+    }
+  }
 
-  for (int i = tid; i < 4 * d; i += PREP_THREADS) {
-    const int hh = i / d, j = i - hh * d;
+  // queries (rows past d are zero, so clamped matrix rows add nothing)
+  const int nrow = SPLIT ? JC : d;
+  for (int i = tid; i < 4 * nrow; i += PREP_THREADS) {
+    const int hh = i / nrow, j = i - hh * nrow;
     const int h = hgi * 4 + hh;
     const int64_t flat = (int64_t)grp * a.qpg + h;
-    qv[hh][j] = (h < a.qpg && flat < a.nq_total) ? a.q[flat * d + j] : 0.f;
+    qT[j][hh] = (j < d && h < a.qpg && flat < a.nq_total) ? a.q[flat * d + j] : 0.f;
   }
   for (int i = tid; i < 4 * (ncb + npar); i += PREP_THREADS) (&vP[0][0])[(i / (ncb + npar)) * (2 * 96 * 8) + i % (ncb + npar)] = 0.f;
   for (int i = tid; i < 4 * nsb; i += PREP_THREADS) (&vQ[0][0])[(i / nsb) * (32 * 8) + i % nsb] = 0.f;
   __syncthreads();
+
+  float accS[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (SPLIT) {
+    // partial products of this thread's rows, then the 4 row groups summed
+    // by the column's owner
+    float pc[4][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) pc[c][hh] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < RPG; ++jj) {
+      const float4 q4 = *reinterpret_cast<const float4 *>(&qT[rg * RPG + jj][0]);
+      const float mv[4] = {mq[jj].x, mq[jj].y, mq[jj].z, mq[jj].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        pc[c][0] = fmaf(mv[c], q4.x, pc[c][0]);
+        pc[c][1] = fmaf(mv[c], q4.y, pc[c][1]);
+        pc[c][2] = fmaf(mv[c], q4.z, pc[c][2]);
+        pc[c][3] = fmaf(mv[c], q4.w, pc[c][3]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<float4 *>(&part[(((mat0 * 4 + rg) * 128) + 4 * quad + c) * 4]) =
+          make_float4(pc[c][0], pc[c][1], pc[c][2], pc[c][3]);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float4 v = *reinterpret_cast<const float4 *>(&part[(((mat0 * 4 + r) * 128) + col) * 4]);
+      accS[0] += v.x;
+      accS[1] += v.y;
+      accS[2] += v.z;
+      accS[3] += v.w;
+    }
+  }
 
   // per thread: sums (P: code chain, Q: sign chain) and maxima of |v| 2^-(bit & 7)
   float sP[4] = {0.f, 0.f, 0.f, 0.f}, sQ[4] = {0.f, 0.f, 0.f, 0.f};
   float mP[4] = {0.f, 0.f, 0.f, 0.f}, mQ[4] = {0.f, 0.f, 0.f, 0.f};
   for (int mat = mat0; mat < (SPLIT ? mat0 + 1 : 2); ++mat) {
     const int cols = mat ? m : d;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < (SPLIT ? 1 : d); j0 += JC) {
-      if (!SPLIT) load_col(mat, j0);
+    float acc[4] = {accS[0], accS[1], accS[2], accS[3]};
+    if constexpr (!SPLIT) {
+      // d > 128: one column per thread, rows in chunks of JC
+      const float *MT = mat ? a.ST : a.PiT;
+      const int c = min(col, max(cols, 1) - 1);
+      for (int j0 = 0; j0 < d; j0 += JC) {
+        float mc[JC];
 #pragma unroll
-      for (int j = 0; j < JC; j += 4) {
-        if (j0 + j < d) {               // d % 8 == 0; rows past d are skipped
+        for (int j = 0; j < JC; ++j) mc[j] = MT[min(j0 + j, d - 1) * cols + c];
 #pragma unroll
-          for (int hh = 0; hh < 4; ++hh) {
-            const float4 qq = *reinterpret_cast<const float4 *>(&qv[hh][j0 + j]);
-            acc[hh] = fmaf(mc[j], qq.x, acc[hh]);
-            acc[hh] = fmaf(mc[j + 1], qq.y, acc[hh]);
-            acc[hh] = fmaf(mc[j + 2], qq.z, acc[hh]);
-            acc[hh] = fmaf(mc[j + 3], qq.w, acc[hh]);
+        for (int j = 0; j < JC; ++j) {
+          if (j0 + j < d) {
+            const float4 q4 = *reinterpret_cast<const float4 *>(&qT[j0 + j][0]);
+            acc[0] = fmaf(mc[j], q4.x, acc[0]);
+            acc[1] = fmaf(mc[j], q4.y, acc[1]);
+            acc[2] = fmaf(mc[j], q4.z, acc[2]);
+            acc[3] = fmaf(mc[j], q4.w, acc[3]);
           }
         }
       }
