@@ -75,6 +75,11 @@ __global__ void __launch_bounds__(USE_LDS ? 512 : 256) quantize_kernel(QArgs a) 
   constexpr int SW = (PER + 31) / 32;       // sign words per lane
   constexpr int CBYTES = PER * W / 8;       // code bytes per lane (whole bytes: PER % 8 == 0)
   constexpr int SBYTES = PER / 8;
+  // d == DPAD (and m == d): when the lane groups' byte runs are whole dwords
+  // and together fill a 16-byte-multiple record, the record has no padding
+  // and every lane stores plain dwords
+  constexpr bool CEXACT = FULL && CBYTES % 4 == 0 && (4 * CBYTES) % 16 == 0;
+  constexpr bool SEXACT = FULL && SBYTES % 4 == 0 && (4 * SBYTES) % 16 == 0;
 
   __shared__ Frag lds[USE_LDS ? 4 * FR * 64 : 1];
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
@@ -221,19 +226,27 @@ __global__ void __launch_bounds__(USE_LDS ? 512 : 256) quantize_kernel(QArgs a) 
           const int li = 4 * u + jj;                 // local coordinate index
           const float y = acc[t][jj] * inv[t];
           const float ay = fabsf(y);
-          int mm = 0;
+          uint32_t mm = 0;
           float cm = a.cpos[0];
 #pragma unroll
           for (int j = 0; j < HALF - 1; ++j) {
             const bool gt = ay > a.tpos[j];
-            mm += gt ? 1 : 0;
+            mm += gt ? 1u : 0u;
             cm = gt ? a.cpos[j + 1] : cm;
           }
-          uint32_t idx = y > 0.f ? (uint32_t)(HALF + mm) : (uint32_t)(HALF - 1 - mm);
-          float r = y > 0.f ? y - cm : y + cm;
-          if ((!FULL && li >= nval) || !(nu[t] > 0.f)) {
-            idx = 0u;
-            r = 0.f;
+          // sign from the sign bit, with no lane masks: idx = HALF + mm for
+          // y >= +0, its mirror HALF - 1 - mm (= (HALF + mm) ^ (2 HALF - 1)) for
+          // y <= -0; r = y - copysign(c, y).  (y == +0 exactly lies on the
+          // middle threshold, inside the decision band.)
+          const uint32_t yb = __float_as_uint(y);
+          const uint32_t neg = (uint32_t)((int32_t)yb >> 31);
+          uint32_t idx = ((uint32_t)HALF + mm) ^ (neg & (uint32_t)(2 * HALF - 1));
+          float r = y - __uint_as_float((__float_as_uint(cm) & 0x7fffffffu) | (yb & 0x80000000u));
+          if constexpr (!FULL) {
+            if (li >= nval) {               // padding coordinates
+              idx = 0u;
+              r = 0.f;
+            }
           }
           const int bit = li * W;
           cw[t][bit >> 5] |= idx << (bit & 31);
@@ -247,6 +260,15 @@ __global__ void __launch_bounds__(USE_LDS ? 512 : 256) quantize_kernel(QArgs a) 
       __builtin_amdgcn_sched_barrier(0);   // keep fragment loads from piling up
     }
 
+    // a zero vector stores zero codes and gamma = 0 (its signs are cleared below)
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      if (!(nu[t] > 0.f)) {
+#pragma unroll
+        for (int i = 0; i < CW; ++i) cw[t][i] = 0u;
+        rs[t] = 0.f;
+      }
+    }
 #pragma unroll
     for (int t = 0; t < NTL; ++t) {
       rs[t] += __shfl_xor(rs[t], 16);
@@ -254,8 +276,14 @@ __global__ void __launch_bounds__(USE_LDS ? 512 : 256) quantize_kernel(QArgs a) 
       if (valid[t]) {
         uint8_t *rec = a.codes + vi[t] * a.ldr * a.code_bytes;
         const int off = grp * CBYTES;
-        store_bytes<CW>(rec + off, cw[t], min(CBYTES, a.code_bytes - off));
-        if (grp == 3 && 4 * CBYTES < a.code_bytes) zero_bytes(rec + 4 * CBYTES, a.code_bytes - 4 * CBYTES);
+        if constexpr (CEXACT) {
+          // the 4 lane groups' byte runs tile the record exactly, dword-aligned
+#pragma unroll
+          for (int i = 0; i < CBYTES / 4; ++i) reinterpret_cast<uint32_t *>(rec + off)[i] = cw[t][i];
+        } else {
+          store_bytes<CW>(rec + off, cw[t], min(CBYTES, a.code_bytes - off));
+          if (grp == 3 && 4 * CBYTES < a.code_bytes) zero_bytes(rec + 4 * CBYTES, a.code_bytes - 4 * CBYTES);
+        }
         if (grp == 0) a.norms[vi[t] * a.ldr] = nu[t];
       }
     }
@@ -284,11 +312,10 @@ __global__ void __launch_bounds__(USE_LDS ? 512 : 256) quantize_kernel(QArgs a) 
         }
 #pragma unroll
         for (int t = 0; t < NTL; ++t) {
-          const bool live = nu[t] > 0.f;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int li = 4 * u + jj;
-            const bool b = live && (FULL || li < mval) && z[t][jj] >= 0.f;
+            const bool b = (FULL || li < mval) && z[t][jj] >= 0.f;
             sw[t][li >> 5] |= (b ? 1u : 0u) << (li & 31);
           }
         }
@@ -296,11 +323,20 @@ __global__ void __launch_bounds__(USE_LDS ? 512 : 256) quantize_kernel(QArgs a) 
       }
 #pragma unroll
       for (int t = 0; t < NTL; ++t) {
+        if (!(nu[t] > 0.f)) {
+#pragma unroll
+          for (int i = 0; i < SW; ++i) sw[t][i] = 0u;
+        }
         if (valid[t]) {
           uint8_t *rec = a.signs + vi[t] * a.ldr * a.sign_bytes;
           const int off = grp * SBYTES;
-          store_bytes<SW>(rec + off, sw[t], min(SBYTES, a.sign_bytes - off));
-          if (grp == 3 && 4 * SBYTES < a.sign_bytes) zero_bytes(rec + 4 * SBYTES, a.sign_bytes - 4 * SBYTES);
+          if constexpr (SEXACT) {
+#pragma unroll
+            for (int i = 0; i < SBYTES / 4; ++i) reinterpret_cast<uint32_t *>(rec + off)[i] = sw[t][i];
+          } else {
+            store_bytes<SW>(rec + off, sw[t], min(SBYTES, a.sign_bytes - off));
+            if (grp == 3 && 4 * SBYTES < a.sign_bytes) zero_bytes(rec + 4 * SBYTES, a.sign_bytes - 4 * SBYTES);
+          }
           if (grp == 0) a.rnorms[vi[t] * a.ldr] = nu[t] > 0.f ? sqrtf(rs[t]) : 0.f;
         }
       }

@@ -65,6 +65,16 @@ def test_quantize_bf16_two_tile_path(tq, bits):
     check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantize_fp32_two_tile_path(tq, bits):
+    # fp32 input (three GEMM-1 passes) on the 32-vector-tile path, ragged tail
+    X = wl.gaussian((5003, 128), 14)
+    print(f"quantize fp32 n=5003 d=128 b={bits}", flush=True)
+    ctx, g, xin = _run(tq, 128, bits, X)
+    p = O.make_params(128, bits, 0)
+    check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
+
+
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_quantize_mse_mode(tq, bits):
     X = wl.bf16_round(wl.gaussian((777, 128), 4))
