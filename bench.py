@@ -35,6 +35,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 EVENT_EVERY = 5
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
+FP32_VALU_TFLOPS = 78.6        # non-packed fp32 FMA: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 2
 
 
 def log(*a):
@@ -112,6 +114,58 @@ def cpu_quantize_baseline(bits, n=16384):
     return n / (time.perf_counter() - t0)
 
 
+def _host_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    return min(len(os.sched_getaffinity(0)), blas) or 1
+
+
+def cpu_attend_baseline():
+    """Oracle decode attention on one (batch, KV head) group of the 128K workload
+    (random packed records of the same geometry; 4 query heads)."""
+    import oracle as O
+    from oblivious_kv_cache_amd import workloads as wl
+    d, T = 128, 131072
+    pk, pv = O.make_params(d, 3, 0), O.make_params(d, 3, 1, "mse")
+    kc, ks, kn, kr = wl.random_records(T, 32, 16, seed=50)
+    vc, _, vn, _ = wl.random_records(T, 48, 16, seed=51)
+    Q = wl.gaussian((4, d), 52, np.float64)
+    t0 = time.perf_counter()
+    O.attend(pk, pv, Q, kc, ks, kn, kr, vc, vn, 1.0 / math.sqrt(d))
+    el = time.perf_counter() - t0
+    return {"value": T / el, "unit": "tokens/s (one group, 4 heads)", "cores": _host_threads(),
+            "kind": "oracle", "sample": f"1 group x {T} tokens, {el:.1f} s"}
+
+
+def cpu_topk_baseline(n=100000, nq=4):
+    """Oracle estimator scores + top-10 for 4 queries over 10^5 random d=200
+    records (b=2 geometry), scaled to pairs/s."""
+    import oracle as O
+    from oblivious_kv_cache_amd import workloads as wl
+    d = 200
+    p = O.make_params(d, 2, 0)
+    c, sg, nu, ga = wl.random_records(n, 32, 32, seed=53)
+    Q = wl.gaussian((nq, d), 54, np.float64)
+    t0 = time.perf_counter()
+    O.topk(O.scores(p, Q, c, sg, nu, ga), 10)
+    el = time.perf_counter() - t0
+    return {"value": nq * n / el, "unit": "pairs/s", "cores": _host_threads(), "kind": "oracle",
+            "sample": f"{nq} queries x {n} vectors, {el:.1f} s"}
+
+
+def cpu_softmax_baseline(rows=1024, T=32768):
+    import oracle as O
+    L = np.random.default_rng(55).standard_normal((rows, T))
+    t0 = time.perf_counter()
+    O.softmax(L, 0.088)
+    el = time.perf_counter() - t0
+    return {"value": rows * T / el, "unit": "values/s", "cores": _host_threads(), "kind": "oracle",
+            "sample": f"{rows} rows x {T}, {el:.2f} s"}
+
+
 def _time(torch, fn, reps):
     for _ in range(2):
         fn()
@@ -145,10 +199,16 @@ def bench_attend(tq, wl, dev):
     scale = 1.0 / math.sqrt(d)
     ms = _time(torch, lambda: tq.tq_attend(kctx, vctx, q, krec, vrec, scale, ws=ws), 10)
     kv_bytes = G * T * (kctx.code_bytes + kctx.sign_bytes + 8 + vctx.code_bytes + 4)
+    # the value sum is 4 heads x d fp32 FMAs per token and group; non-packed
+    # fp32 VALU peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz FMAs
+    fmas = G * T * 4 * d
     r = {"ms": ms, "tokens_per_s": G * T / (ms / 1e3), "logits_per_s": G * qpg * T / (ms / 1e3),
          "kv_bytes": kv_bytes, "alg_gbs": kv_bytes / (ms / 1e3) / 1e9,
-         "hbm_frac": kv_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
-    log(f"  attend: {ms:.3f} ms, {r['alg_gbs']:.0f} GB/s of packed K+V")
+         "hbm_frac": kv_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+         "value_fma_tflops": 2 * fmas / (ms / 1e3) / 1e12,
+         "value_fma_frac_of_fp32_valu": 2 * fmas / (ms / 1e3) / 1e12 / FP32_VALU_TFLOPS}
+    log(f"  attend: {ms:.3f} ms, {r['alg_gbs']:.0f} GB/s of packed K+V, value FMAs "
+        f"{r['value_fma_tflops']:.1f} TF/s")
     return r
 
 
@@ -173,8 +233,15 @@ def bench_topk(tq, wl, dev, nq=10000, n=1000000, d=200, k=10):
         ids = res["r"][0]
         rec_k = {str(kk): float((ids[:, :kk] == top1[:, None]).any(dim=1).float().mean()) for kk in (1, 2, 4, 8, 10)}
         db_bytes = n * (ctx.code_bytes + ctx.sign_bytes + 8)
+        # int8 MFMA work: per 16 vectors x 4 queries, NM v_mfma_i32_16x16x64_i8
+        # (2 per 32-bit record word and lane group: code, parity, sign words)
+        cb16, sb16, w = ctx.code_bytes // 16, ctx.sign_bytes // 16, ctx.w
+        nm = 2 * cb16 + (2 * cb16 if w == 3 else 0) + 2 * sb16
+        mfma_ops = nq * n / 64 * nm * 2 * 16 * 16 * 64
         out[f"b{bits}"] = {"ms": ms, "pairs_per_s": nq * n / (ms / 1e3), "queries_per_s": nq / (ms / 1e3),
-                           "db_bytes": db_bytes, "db_quantize_ms": ms_q, "recall_1_at_k": rec_k}
+                           "db_bytes": db_bytes, "db_quantize_ms": ms_q, "recall_1_at_k": rec_k,
+                           "int8_mfma_tops": mfma_ops / (ms / 1e3) / 1e12,
+                           "int8_mfma_frac": mfma_ops / (ms / 1e3) / 1e12 / INT8_PEAK_TOPS}
         log(f"  b={bits}: topk {ms:.2f} ms ({nq * n / (ms / 1e3):.3e} pairs/s), "
             f"db quantize {ms_q:.3f} ms, recall1@k {rec_k}")
         del rec, ws
@@ -265,19 +332,25 @@ def main():
              "key_bytes_per_token": cb + sb + 8, "logits_per_step": n_logits}
 
     if not args.no_extra:
-        log("quantize throughput: 2^20 x 128 bf16, power-law spectrum")
-        X = wl.power_law_torch(1 << 20, d, seed=3, device=dev)
+        log("softmax: 1024 rows x 32768")
+        sm_ms = _time(torch, lambda: tq.tq_softmax(logits, scale, probs=probs), 20)
+        sm_bytes = 2 * n_logits * 4
+        extra["softmax_32k"] = {"ms": sm_ms, "bytes": sm_bytes, "gbs": sm_bytes / (sm_ms / 1e3) / 1e9,
+                                "hbm_frac": sm_bytes / (sm_ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+        log(f"  softmax: {sm_ms * 1e3:.1f} us, {extra['softmax_32k']['gbs']:.0f} GB/s")
+        log("quantize throughput: 2^20 x 128 bf16, power-law spectrum (two input sets, alternated)")
+        Xs = [wl.power_law_torch(1 << 20, d, seed=3 + i, device=dev) for i in range(2)]
         qz = {}
         for b in (2, 3, 4):
             c2 = tq.Context(d, b, seed=0)
             out = c2.empty_records(1 << 20, dev)
-            for _ in range(3):
-                tq.tq_quantize(c2, X, out=out)
+            for i in range(3):
+                tq.tq_quantize(c2, Xs[i % 2], out=out)
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
             reps = 10
-            for _ in range(reps):
-                tq.tq_quantize(c2, X, out=out)
+            for i in range(reps):
+                tq.tq_quantize(c2, Xs[i % 2], out=out)
             e.record()
             torch.cuda.synchronize()
             ms = s.elapsed_time(e) / reps
@@ -289,11 +362,12 @@ def main():
                            "alg_frac_bf16_peak": alg_tflops / BF16_PEAK_TFLOPS,
                            "mfma_tflops_split": hw_tflops,
                            "mfma_frac_bf16_peak": hw_tflops / BF16_PEAK_TFLOPS,
-                           "io_gbs": io_gbs}
+                           "io_gbs": io_gbs, "io_hbm_frac": io_gbs / HBM_PEAK_GBS}
             log(f"  b={b}: {ms:.3f} ms, {vps:.3e} vec/s, alg {alg_tflops:.0f} TF/s, "
                 f"MFMA {hw_tflops:.0f} TF/s, io {io_gbs:.0f} GB/s")
             c2.close()
             del out
+        del Xs
         extra["quantize_2p20"] = qz
         extra["attend_128k"] = bench_attend(tq, wl, dev)
         extra["topk_1e6"] = bench_topk(tq, wl, dev)
@@ -312,6 +386,11 @@ def main():
         log("cpu baseline: oracle estimator on a bounded sample")
         cpu = cpu_baseline(bits)
         extra["cpu_oracle_quantize_vec_per_s"] = cpu_quantize_baseline(bits)
+        if not args.no_extra:
+            log("cpu oracle: softmax, attention (one 128K group), top-k sample")
+            extra["cpu_oracle_softmax"] = cpu_softmax_baseline()
+            extra["cpu_oracle_attend_128k"] = cpu_attend_baseline()
+            extra["cpu_oracle_topk"] = cpu_topk_baseline()
 
     line = {
         "metric": "packed-key attention logits/s (d=128, 3-bit, decode 32K)",
