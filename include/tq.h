@@ -158,6 +158,28 @@ int tq_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, 
               const float *rnorms, float *logits, void *ws, size_t ws_bytes,
               hipStream_t stream);
 
+/* The two halves of tq_scores, for callers that prepare the queries apart
+ * from scoring (on another stream while the cache is still being appended
+ * to, or once for several key sets).
+ *
+ * tq_prep_queries projects the queries with Pi and S (the query side of the
+ * estimator: hao.cnyes.com "TurboQuant", 1 bit 掃尾; suzuke blog, 第三步) and
+ * writes, per group and 4-head block, the int8 operand fragments and per-head
+ * constants that scoring reads into ws.
+ *   q  [device] float [G][qpg][d];
+ *   ws [device] >= tq_workspace_size(TQ_OP_SCORES, G, qpg) bytes, written.
+ * tq_scores_prepared scores key records against a workspace prepared by
+ * tq_prep_queries with the same ctx, G and qpg (read only; it stays valid
+ * until the caller overwrites it), with the arguments and results of
+ * tq_scores.  tq_scores(...) is tq_prep_queries followed by
+ * tq_scores_prepared on the same stream; results are identical. */
+int tq_prep_queries(const tq_ctx *ctx, const float *q, int64_t G, int qpg, void *ws,
+                    size_t ws_bytes, hipStream_t stream);
+int tq_scores_prepared(const tq_ctx *ctx, const void *ws, size_t ws_bytes, int64_t G, int qpg,
+                       int64_t T, int64_t ldk, const uint8_t *codes, const uint8_t *signs,
+                       const float *norms, const float *rnorms, float *logits,
+                       hipStream_t stream);
+
 /* Row softmax of scale * logits: probs[r][t] = exp(s l - max_r) / sum.
  * logits, probs [device] float [rows][T]; probs == logits is allowed. */
 int tq_softmax(const float *logits, int64_t rows, int64_t T, float scale, float *probs,

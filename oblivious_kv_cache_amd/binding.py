@@ -22,8 +22,8 @@ TQ_MAX_D, TQ_MAX_TOPK = 256, 64
 
 EXPORTS = [
     "tq_init", "tq_init_mse", "tq_free", "tq_layout", "tq_host_params", "tq_get_params",
-    "tq_quantize", "tq_workspace_size", "tq_scores", "tq_softmax", "tq_attend",
-    "tq_dequant", "tq_topk", "tq_strerror",
+    "tq_quantize", "tq_workspace_size", "tq_scores", "tq_prep_queries", "tq_scores_prepared",
+    "tq_softmax", "tq_attend", "tq_dequant", "tq_topk", "tq_strerror",
 ]
 
 
@@ -56,6 +56,8 @@ def _load():
         "tq_quantize": (I, [P, P, I, I64, I64, I64, P, P, P, P, P]),
         "tq_workspace_size": (I, [P, I, I64, I64, I64, ctypes.POINTER(SZ)]),
         "tq_scores": (I, [P, P, I64, I, I64, I64, P, P, P, P, P, P, SZ, P]),
+        "tq_prep_queries": (I, [P, P, I64, I, P, SZ, P]),
+        "tq_scores_prepared": (I, [P, P, SZ, I64, I, I64, I64, P, P, P, P, P, P]),
         "tq_softmax": (I, [P, I64, I64, F, P, P]),
         "tq_attend": (I, [P, P, P, I64, I, I64, I64, P, P, P, P, P, P, F, P, P, P, P, SZ, P]),
         "tq_dequant": (I, [P, P, P, P, P, I64, P, P]),
@@ -186,6 +188,30 @@ def tq_scores(ctx, q, rec, T=None, ldk=None, logits=None, ws=None):
     _check(LIB.tq_scores(ctx.handle, _ptr(q), G, qpg, T, ldk, _ptr(rec["codes"]), _ptr(rec["signs"]),
                          _ptr(rec["norms"]), _ptr(rec["rnorms"]), _ptr(logits), _ptr(ws), ws.numel(),
                          _stream()), "tq_scores")
+    return logits
+
+
+def tq_prep_queries(ctx, q, ws=None):
+    """Prepared query state for q [G, qpg, d] (a workspace tensor, returned)."""
+    G, qpg, d = q.shape
+    assert q.is_contiguous() and q.dtype == torch.float32 and d == ctx.d
+    if ws is None:
+        ws = ctx.workspace(TQ_OP_SCORES, G, qpg, device=q.device)
+    _check(LIB.tq_prep_queries(ctx.handle, _ptr(q), G, qpg, _ptr(ws), ws.numel(), _stream()),
+           "tq_prep_queries")
+    return ws
+
+
+def tq_scores_prepared(ctx, ws, G, qpg, rec, T=None, ldk=None, logits=None):
+    """Logits [G, qpg, T] from a workspace made by tq_prep_queries."""
+    n = rec["codes"].shape[0]
+    ldk = ldk if ldk is not None else n // max(G, 1)
+    T = T if T is not None else ldk
+    if logits is None:
+        logits = torch.empty((G, qpg, T), dtype=torch.float32, device=ws.device)
+    _check(LIB.tq_scores_prepared(ctx.handle, _ptr(ws), ws.numel(), G, qpg, T, ldk, _ptr(rec["codes"]),
+                                  _ptr(rec["signs"]), _ptr(rec["norms"]), _ptr(rec["rnorms"]),
+                                  _ptr(logits), _stream()), "tq_scores_prepared")
     return logits
 
 

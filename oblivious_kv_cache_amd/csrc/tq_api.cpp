@@ -268,6 +268,36 @@ int tq_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, 
   return tq::launch_scores(ctx, q, G, qpg, T, ldk, codes, signs, norms, rnorms, logits, ws, stream);
 }
 
+int tq_prep_queries(const tq_ctx *ctx, const float *q, int64_t G, int qpg, void *ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
+  if (G < 0 || qpg < 1 || qpg > 64) return TQ_EINVAL;
+  if (G == 0) return TQ_OK;
+  if (!q || !ws || !aligned(q, 4) || !aligned(ws, 16)) return TQ_EINVAL;
+  if (ws_bytes < tq::scores_ws_bytes(ctx, G, qpg)) return TQ_EINVAL;
+  const int st = current_device_matches(ctx);
+  if (st != TQ_OK) return st;
+  return tq::launch_prep_queries(ctx, q, G, qpg, ws, stream);
+}
+
+int tq_scores_prepared(const tq_ctx *ctx, const void *ws, size_t ws_bytes, int64_t G, int qpg,
+                       int64_t T, int64_t ldk, const uint8_t *codes, const uint8_t *signs,
+                       const float *norms, const float *rnorms, float *logits,
+                       hipStream_t stream) {
+  if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
+  if (G < 0 || T < 0 || ldk < T || qpg < 1 || qpg > 64) return TQ_EINVAL;
+  if (G == 0 || T == 0) return TQ_OK;
+  if (!ws || !codes || !signs || !norms || !rnorms || !logits) return TQ_EINVAL;
+  if (!aligned(codes, 16) || !aligned(signs, 16) || !aligned(norms, 4) || !aligned(rnorms, 4) ||
+      !aligned(logits, 4) || !aligned(ws, 16))
+    return TQ_EINVAL;
+  if (ws_bytes < tq::scores_ws_bytes(ctx, G, qpg)) return TQ_EINVAL;
+  const int st = current_device_matches(ctx);
+  if (st != TQ_OK) return st;
+  return tq::launch_scores_prepared(ctx, ws, G, qpg, T, ldk, codes, signs, norms, rnorms, logits,
+                                    stream);
+}
+
 int tq_softmax(const float *logits, int64_t rows, int64_t T, float scale, float *probs,
                hipStream_t stream) {
   if (rows < 0 || T < 0) return TQ_EINVAL;

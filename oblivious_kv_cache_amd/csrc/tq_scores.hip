@@ -456,20 +456,33 @@ size_t scores_ws_bytes(const tq_ctx *ctx, int64_t G, int qpg) {
   return (size_t)(G * hg * prep_stride(nm));
 }
 
-int launch_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,
-                  const uint8_t *codes, const uint8_t *signs, const float *norms,
-                  const float *rnorms, float *logits, void *ws, hipStream_t stream) {
-  if (G == 0 || T == 0) return TQ_OK;
-  const int hg = (qpg + 3) / 4;
-  const int cb16 = ctx->code_bytes / 16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
-  const int64_t groups = G * hg;
+int check_scores_shape(const tq_ctx *ctx, int64_t G, int qpg, int64_t T, int64_t ldk) {
+  const int64_t groups = G * ((qpg + 3) / 4);
   if (groups > 65535 || T > 0x7fffffff - 64) return TQ_ENOTSUP;
   // per-group record offsets are 32-bit in the scores kernel
   if (ldk * (int64_t)(ctx->code_bytes > ctx->sign_bytes ? ctx->code_bytes : ctx->sign_bytes) >= ((int64_t)1 << 32))
     return TQ_ENOTSUP;
-  int st = launch_prep(ctx, q, groups, qpg, hg, G * qpg, reinterpret_cast<uint8_t *>(ws), stream);
-  if (st != TQ_OK) return st;
+  return TQ_OK;
+}
 
+int launch_prep_queries(const tq_ctx *ctx, const float *q, int64_t G, int qpg, void *ws,
+                        hipStream_t stream) {
+  if (G == 0) return TQ_OK;
+  const int hg = (qpg + 3) / 4;
+  if (G * hg > 65535) return TQ_ENOTSUP;
+  return launch_prep(ctx, q, G * hg, qpg, hg, G * qpg, reinterpret_cast<uint8_t *>(ws), stream);
+}
+
+int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg, int64_t T,
+                           int64_t ldk, const uint8_t *codes, const uint8_t *signs,
+                           const float *norms, const float *rnorms, float *logits,
+                           hipStream_t stream) {
+  if (G == 0 || T == 0) return TQ_OK;
+  int st = check_scores_shape(ctx, G, qpg, T, ldk);
+  if (st != TQ_OK) return st;
+  const int hg = (qpg + 3) / 4;
+  const int cb16 = ctx->code_bytes / 16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
+  const int64_t groups = G * hg;
   ScoreArgs sa{};
   sa.codes = codes;
   sa.signs = signs;
@@ -492,6 +505,17 @@ int launch_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t
   const int64_t chunks = (tiles + 4 * tpw - 1) / (4 * tpw);
   sa.tiles_per_wave = (int)tpw;
   return dispatch(sa, dim3((unsigned)chunks, (unsigned)groups), cb16, sb16, w, stream);
+}
+
+int launch_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,
+                  const uint8_t *codes, const uint8_t *signs, const float *norms,
+                  const float *rnorms, float *logits, void *ws, hipStream_t stream) {
+  if (G == 0 || T == 0) return TQ_OK;
+  int st = check_scores_shape(ctx, G, qpg, T, ldk);
+  if (st != TQ_OK) return st;
+  st = launch_prep_queries(ctx, q, G, qpg, ws, stream);
+  if (st != TQ_OK) return st;
+  return launch_scores_prepared(ctx, ws, G, qpg, T, ldk, codes, signs, norms, rnorms, logits, stream);
 }
 
 // ------------------------------------------------------------------ softmax

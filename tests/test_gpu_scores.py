@@ -126,3 +126,26 @@ def test_scores_errors(tq):
     ws = ctx.workspace(tq.TQ_OP_SCORES, 1, 4)
     with pytest.raises(tq.TQError):
         tq.tq_scores(ctx, q, rec, T=10, ldk=10, ws=ws[:16])   # workspace too small
+
+
+def test_prepared_queries_match_tq_scores_and_oracle(tq):
+    # tq_prep_queries + tq_scores_prepared == tq_scores (bit for bit), and one
+    # prepared workspace scores two different key sets
+    d, bits, G, qpg, T = 128, 3, 3, 6, 700
+    ctx = tq.Context(d, bits, 0)
+    p = O.make_params(d, bits, 0)
+    Q = wl.gaussian((G, qpg, d), 61)
+    recs = []
+    for seed in (62, 63):
+        c, sg, nu, ga = wl.random_records(G * T, ctx.code_bytes, ctx.sign_bytes, seed=seed)
+        recs.append({"codes": c, "signs": sg, "norms": nu, "rnorms": ga})
+    q = torch.from_numpy(np.ascontiguousarray(Q, dtype=np.float32)).cuda()
+    print("scores prepared: G=3 qpg=6 T=700, two key sets", flush=True)
+    ws = tq.tq_prep_queries(ctx, q)
+    for rec in recs:
+        dev = _dev(rec)
+        got = tq.tq_scores_prepared(ctx, ws, G, qpg, dev, T=T, ldk=T)
+        ref = tq.tq_scores(ctx, q, dev, T=T, ldk=T)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+        assert_close(got.cpu().numpy(), _oracle_grouped(p, Q, rec, G, T, T), what="logits")
