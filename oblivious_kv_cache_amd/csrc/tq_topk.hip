@@ -57,12 +57,29 @@ struct ScanArgs {
   float *cand_s;
   int *cand_i;
   int64_t n, nq, groups, chunk;
-  int nchunk, cb, sb;
+  int nchunk, cb, sb, k;
   float alpha;
 };
 
 __device__ __forceinline__ bool better(float s, int i, float ts, int ti) {
   return s > ts || (s == ts && i < ti);
+}
+
+// k-th largest (k in [1, 16]) of the 16 values held by the lanes of each
+// 16-lane row: bitonic sort of the row into descending lane order, then a
+// read of lane k - 1.  Every lane of the row gets the result.
+__device__ __forceinline__ float row_kth_largest(float v, int k, int lane) {
+  const int col = lane & 15;
+#pragma unroll
+  for (int size = 2; size <= 16; size <<= 1) {
+#pragma unroll
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      const float o = __shfl_xor(v, j);
+      const bool desc = (col & size) == 0, lower = (col & j) == 0;
+      v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
+    }
+  }
+  return __shfl(v, (lane & ~15) + k - 1);
 }
 
 template <int CB16, int SB16, int W, int KP>
@@ -86,28 +103,36 @@ __global__ void __launch_bounds__(64 * scan_waves(KP)) topk_scan_kernel(ScanArgs
     ls[j] = -FLT_MAX;
     li[j] = INT_MAX;
   }
-  const int64_t begin = (int64_t)c * a.chunk;
-  int64_t end = begin + a.chunk;
-  if (end > a.n) end = a.n;
-  for (int64_t t0 = begin; t0 < end; t0 += 64) {
+  // n < 2^31 and record offsets < 2^32 are checked on the host
+  const int begin = (int)((int64_t)c * a.chunk);
+  const int end = (int)min((int64_t)begin + a.chunk, a.n);
+  // Pruning bound for k <= 16: the k-th largest of the 16 lanes' current
+  // best scores of a query.  k distinct vectors score at least that much, so
+  // a score below it cannot be in the query's top k; refreshed every 4 tiles.
+  float thr = -FLT_MAX;
+  int tile = 0;
+  for (int t0 = begin; t0 < end; t0 += 64, ++tile) {
     KeyWords<CB16, SB16, W> kw[4];
     float nu[4], ga[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      int64_t t = t0 + 16 * s + col;
-      if (t >= end) t = end - 1;
-      load_key_words<false>(kw[s], a.codes, a.signs, (uint32_t)t, grp);
-      nu[s] = a.norms[t];
-      ga[s] = a.rnorms[t];
+      const uint32_t t = (uint32_t)min(t0 + 16 * s + col, end - 1);
+      load_key_words<false>(kw[s], a.codes, a.signs, t, grp);
+      nu[s] = load_f32(a.norms, t);
+      ga[s] = load_f32(a.rnorms, t);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int64_t t = t0 + 16 * s + col;
+      const int t = t0 + 16 * s + col;
       const float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
-      if (t < end && l > ls[KP - 1]) {
+      const bool want = t < end && l > ls[KP - 1] && !(l < thr);
+      // few scores pass once the lists have filled: a wave-uniform branch
+      // skips the insertion network
+      if (__builtin_amdgcn_ballot_w64(want) == 0) continue;
+      if (want) {
         // ids seen by a lane increase, so a tie with the last entry never enters
         float cs = l;
-        int ci = (int)t;
+        int ci = t;
 #pragma unroll
         for (int j = 0; j < KP; ++j) {
           const bool b = better(cs, ci, ls[j], li[j]);
@@ -120,6 +145,7 @@ __global__ void __launch_bounds__(64 * scan_waves(KP)) topk_scan_kernel(ScanArgs
         }
       }
     }
+    if (a.k <= 16 && (tile & 3) == 3) thr = row_kth_largest(ls[0], a.k, lane);
   }
   const int64_t q = qg * 4 + grp;
   if (q < a.nq) {
@@ -230,6 +256,7 @@ int launch_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const 
   a.cb = ctx->code_bytes;
   a.sb = ctx->sign_bytes;
   a.alpha = ctx->alpha;
+  a.k = k;
   st = dispatch_scan(a, dim3((unsigned)g.nchunk, (unsigned)g.qblocks), cb16, sb16, w, g.kp, stream);
   if (st != TQ_OK) return st;
   int npow2 = 1;
