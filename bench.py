@@ -210,6 +210,15 @@ def bench_attend(tq, wl, dev):
          "value_fma_frac_of_fp32_valu": 2 * fmas / (ms / 1e3) / 1e12 / FP32_VALU_TFLOPS}
     log(f"  attend: {ms:.3f} ms, {r['alg_gbs']:.0f} GB/s of packed K+V, value FMAs "
         f"{r['value_fma_tflops']:.1f} TF/s")
+    # the whole online step: append the new key and value of every group at
+    # token T-1, then attend over the T tokens (tq_decode_step, one call)
+    nk = wl.gaussian_torch((G, d), 46, dev, torch.bfloat16)
+    nv = wl.gaussian_torch((G, d), 47, dev, torch.bfloat16)
+    ms_step = _time(torch, lambda: tq.tq_decode_step(kctx, vctx, q, nk, nv, krec, vrec, T - 1, scale,
+                                                     ldk=T, ws=ws), 10)
+    r["decode_step_ms"] = ms_step
+    r["decode_step_tokens_per_s"] = G * T / (ms_step / 1e3)
+    log(f"  decode step (append K and V + attend): {ms_step:.3f} ms")
     return r
 
 

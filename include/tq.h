@@ -202,6 +202,22 @@ int tq_attend(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G,
               float scale, float *logits, float *probs, float *out,
               void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* One online decode step (xujun.org note 189244, KV 缓存: every generated
+ * token's key and value are compressed as they are produced and appended to
+ * the cache): on one stream, with no host synchronisation,
+ *   1. the new key of every group, new_k[g] (row stride ldx, fp32 or bf16),
+ *      is quantized into key record g*ldk + pos (tq_quantize, kctx);
+ *   2. the new value new_v[g] into value record g*ldk + pos (vctx);
+ *   3. tq_attend over tokens 0..pos (T = pos + 1) of every group.
+ * Arguments as in tq_quantize and tq_attend; pos < ldk;
+ * ws >= tq_workspace_size(TQ_OP_ATTEND, G, qpg, pos + 1) bytes.  All checks
+ * happen before the first launch: on error nothing is written. */
+int tq_decode_step(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G, int qpg,
+                   const void *new_k, const void *new_v, int dtype, int64_t ldx, int64_t pos,
+                   int64_t ldk, uint8_t *kcodes, uint8_t *ksigns, float *knorms, float *krnorms,
+                   uint8_t *vcodes, float *vnorms, float scale, float *logits, float *probs,
+                   float *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Reconstruct n vectors: prod x_hat = nu (Pi^T c[idx] + alpha gamma S^T (2 bits - 1)),
  * mse x_hat = nu Pi^T c[idx] (suzuke blog, 第三步).  out [device] float [n][d].
  * signs/rnorms are ignored (may be NULL) in mse mode. */

@@ -332,6 +332,49 @@ int tq_attend(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G,
                            vnorms, scale, logits, probs, out, ws, stream);
 }
 
+int tq_decode_step(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G, int qpg,
+                   const void *new_k, const void *new_v, int dtype, int64_t ldx, int64_t pos,
+                   int64_t ldk, uint8_t *kcodes, uint8_t *ksigns, float *knorms, float *krnorms,
+                   uint8_t *vcodes, float *vnorms, float scale, float *logits, float *probs,
+                   float *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  // everything is checked before the first launch: on error nothing is written
+  if (!kctx || !vctx || kctx->hp.mode != TQ_MODE_PROD || vctx->hp.mode != TQ_MODE_MSE)
+    return TQ_EINVAL;
+  const int d = kctx->hp.d;
+  if (vctx->hp.d != d) return TQ_EINVAL;
+  if (G < 0 || qpg < 1 || qpg > 64 || pos < 0 || ldk < pos + 1) return TQ_EINVAL;
+  if (G == 0) return TQ_OK;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EINVAL;
+  if (ldx < d || (dtype == TQ_BF16 ? (ldx % 8) : (ldx % 4))) return TQ_EINVAL;
+  if (!q || !new_k || !new_v || !kcodes || !ksigns || !knorms || !krnorms || !vcodes || !vnorms ||
+      !out || !ws)
+    return TQ_EINVAL;
+  if (probs && !logits) return TQ_EINVAL;
+  if (!aligned(new_k, 16) || !aligned(new_v, 16) || !aligned(kcodes, 16) || !aligned(ksigns, 16) ||
+      !aligned(vcodes, 16) || !aligned(ws, 16) || !aligned(knorms, 4) || !aligned(krnorms, 4) ||
+      !aligned(vnorms, 4) || !aligned(q, 4) || !aligned(out, 4) ||
+      (logits && !aligned(logits, 4)) || (probs && !aligned(probs, 4)))
+    return TQ_EINVAL;
+  if (!std::isfinite(scale)) return TQ_EINVAL;
+  const int64_t T = pos + 1;
+  if (ws_bytes < tq::attend_ws_bytes(kctx, G, qpg, T)) return TQ_EINVAL;
+  int st = current_device_matches(kctx);
+  if (st != TQ_OK) return st;
+  if (vctx->device != kctx->device) return TQ_EINVAL;
+  st = tq::check_attend(kctx, vctx, G, qpg, T, ldk, probs != nullptr);
+  if (st != TQ_OK) return st;
+  // 1-2: the new key and value of every group into slot pos of its cache
+  st = tq::launch_quantize(kctx, new_k, dtype, G, ldx, ldk, kcodes + pos * kctx->code_bytes,
+                           ksigns + pos * kctx->sign_bytes, knorms + pos, krnorms + pos, stream);
+  if (st != TQ_OK) return st;
+  st = tq::launch_quantize(vctx, new_v, dtype, G, ldx, ldk, vcodes + pos * vctx->code_bytes, nullptr,
+                           vnorms + pos, nullptr, stream);
+  if (st != TQ_OK) return st;
+  // 3: attention over tokens 0..pos
+  return tq::launch_attend(kctx, vctx, q, G, qpg, T, ldk, kcodes, ksigns, knorms, krnorms, vcodes,
+                           vnorms, scale, logits, probs, out, ws, stream);
+}
+
 int tq_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs, const float *norms,
                const float *rnorms, int64_t n, float *out, hipStream_t stream) {
   if (!ctx || n < 0) return TQ_EINVAL;

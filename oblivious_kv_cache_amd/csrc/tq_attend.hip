@@ -413,29 +413,38 @@ size_t attend_ws_bytes(const tq_ctx *k, int64_t G, int qpg, int64_t T) {
                   align256(G * qpg * 2 * 4));
 }
 
+int check_attend(const tq_ctx *kc, const tq_ctx *vc, int64_t G, int qpg, int64_t T, int64_t ldk,
+                 bool want_probs) {
+  const int d = kc->hp.d;
+  if (d > 128 || d % 16 != 0) return TQ_ENOTSUP;       // value path: 8 coordinates per lane
+  if (vc->code_bytes > VB_MAX || (vc->code_bytes * CH) % 16 != 0) return TQ_ENOTSUP;
+  const int64_t groups = G * ((qpg + 3) / 4);
+  if (groups > 65535 || T > 0x7fffffff - CH || G * qpg > 0x7fffffff) return TQ_ENOTSUP;
+  const int64_t rec_max = std::max<int64_t>(std::max(kc->code_bytes, kc->sign_bytes), vc->code_bytes);
+  if (ldk * rec_max >= ((int64_t)1 << 32)) return TQ_ENOTSUP;
+  if (want_probs && G * qpg > 65535) return TQ_ENOTSUP;   // probs pass: one grid row per (group, head)
+  return TQ_OK;
+}
+
 int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G, int qpg, int64_t T,
                   int64_t ldk, const uint8_t *kcodes, const uint8_t *ksigns, const float *knorms,
                   const float *krnorms, const uint8_t *vcodes, const float *vnorms, float scale,
                   float *logits, float *probs, float *out, void *ws, hipStream_t stream) {
   const int d = kc->hp.d;
-  if (d > 128 || d % 16 != 0) return TQ_ENOTSUP;       // value path: 8 coordinates per lane
-  if (vc->code_bytes > VB_MAX || (vc->code_bytes * CH) % 16 != 0) return TQ_ENOTSUP;
   if (probs && !logits) return TQ_EINVAL;
+  int st = check_attend(kc, vc, G, qpg, T, ldk, probs != nullptr);
+  if (st != TQ_OK) return st;
   const int hg = (qpg + 3) / 4;
   const int cb16 = kc->code_bytes / 16, sb16 = kc->sign_bytes / 16, w = kc->hp.w;
   const int nm = mfma_count(cb16, sb16, w);
   const int64_t nchunk = (T + CH - 1) / CH;
   const int64_t groups = G * hg;
-  if (groups > 65535 || T > 0x7fffffff - CH || G * qpg > 0x7fffffff) return TQ_ENOTSUP;
-  // per-group record offsets are 32-bit in the partial kernel
-  const int64_t rec_max = std::max<int64_t>(std::max(kc->code_bytes, kc->sign_bytes), vc->code_bytes);
-  if (ldk * rec_max >= ((int64_t)1 << 32)) return TQ_ENOTSUP;
   uint8_t *base = reinterpret_cast<uint8_t *>(ws);
   uint8_t *prep = base;
   float *part = reinterpret_cast<float *>(base + align256(groups * prep_stride(nm)));
   float *mstat = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(part) +
                                            align256(groups * nchunk * 4 * (d + 2) * 4));
-  int st = launch_prep(kc, q, groups, qpg, hg, G * qpg, prep, stream);
+  st = launch_prep(kc, q, groups, qpg, hg, G * qpg, prep, stream);
   if (st != TQ_OK) return st;
   AttArgs a{};
   a.kcodes = kcodes;
@@ -481,8 +490,7 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   attend_combine_kernel<<<(unsigned)(G * qpg), CT, 0, stream>>>(c);
   if (hip_status() != TQ_OK) return TQ_EHIP;
   if (probs) {
-    const int64_t rows = G * qpg;
-    if (rows > 65535) return TQ_ENOTSUP;
+    const int64_t rows = G * qpg;       // <= 65535 (check_attend)
     const unsigned gx = (unsigned)((T + 256 * 8 - 1) / (256 * 8));
     attend_probs_kernel<<<dim3(gx, (unsigned)rows), 256, 0, stream>>>(logits, mstat, probs, T, scale);
     return hip_status();

@@ -73,6 +73,9 @@ int launch_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs
                    const float *norms, const float *rnorms, int64_t n, float *out,
                    hipStream_t stream);
 size_t attend_ws_bytes(const tq_ctx *k, int64_t G, int qpg, int64_t T);
+// shape limits of launch_attend (TQ_OK or TQ_ENOTSUP), checked before any launch
+int check_attend(const tq_ctx *kc, const tq_ctx *vc, int64_t G, int qpg, int64_t T, int64_t ldk,
+                 bool want_probs);
 int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G, int qpg,
                   int64_t T, int64_t ldk, const uint8_t *kcodes, const uint8_t *ksigns,
                   const float *knorms, const float *krnorms, const uint8_t *vcodes,

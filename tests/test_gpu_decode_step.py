@@ -1,0 +1,114 @@
+"""GPU parity: tq_decode_step (append the new key and value, then attend)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oblivious_kv_cache_amd import workloads as wl
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+MARGIN = 1e-4     # new tokens are drawn clear of every decision boundary
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from oblivious_kv_cache_amd import binding
+    return binding
+
+
+def _clear_rows(p, G, d, seed, bf16):
+    """G vectors whose oracle encoding has no coordinate within MARGIN of a
+    threshold and no sketch value within MARGIN of 0 (so the encoding is
+    unique and the GPU must reproduce it bit for bit).  Rows are redrawn
+    from successive seeds until clear."""
+    rows, s = [], seed
+    while len(rows) < G:
+        x = wl.gaussian((1, d), s)
+        if bf16:
+            x = wl.bf16_round(x)
+        r = O.quantize(p, x.astype(np.float64), return_unpacked=True)
+        dist = np.min(np.abs(r["y"][0][:, None] - p.t[None, :]))
+        zmin = np.min(np.abs(r["z"][0])) if r["z"].size else 1.0
+        if dist > MARGIN and zmin > MARGIN:
+            rows.append(x[0])
+        s += 1
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("G,qpg,ldk,pos,bf16", [(3, 4, 700, 600, False), (2, 4, 1100, 1024, True),
+                                                (2, 3, 64, 0, False), (1, 8, 520, 511, True)])
+def test_decode_step_matches_oracle(tq, G, qpg, ldk, pos, bf16):
+    d = 128
+    pk, pv = O.make_params(d, 3, 0), O.make_params(d, 3, 1, "mse")
+    kctx, vctx = tq.Context(d, 3, 0), tq.Context(d, 3, 1, tq.TQ_MODE_MSE)
+    K = wl.gaussian((G * ldk, d), 70)
+    V = wl.gaussian((G * ldk, d), 71)
+    rk, rv = O.quantize(pk, K), O.quantize(pv, V)
+    newk = _clear_rows(pk, G, d, 1000, bf16)
+    newv = _clear_rows(pv, G, d, 2000, bf16)
+    ek, ev = O.quantize(pk, newk.astype(np.float64)), O.quantize(pv, newv.astype(np.float64))
+    Q = wl.gaussian((G, qpg, d), 72)
+    dev = torch.device("cuda")
+    krec = {k: torch.from_numpy(np.ascontiguousarray(rk[k])).to(dev) for k in ("codes", "signs", "norms", "rnorms")}
+    vrec = {k: torch.from_numpy(np.ascontiguousarray(rv[k])).to(dev) for k in ("codes", "norms")}
+    before = {k: v.clone() for k, v in krec.items()}
+    vbefore = {k: v.clone() for k, v in vrec.items()}
+    dt = torch.bfloat16 if bf16 else torch.float32
+    nk = torch.from_numpy(newk.astype(np.float32)).to(dev).to(dt)
+    nv = torch.from_numpy(newv.astype(np.float32)).to(dev).to(dt)
+    scale = 1.0 / math.sqrt(d)
+    print(f"decode step G={G} qpg={qpg} ldk={ldk} pos={pos} bf16={bf16}", flush=True)
+    out, logits, probs = tq.tq_decode_step(kctx, vctx, torch.from_numpy(Q).to(dev), nk, nv, krec, vrec,
+                                           pos, scale, ldk=ldk, want_logits=True, want_probs=True)
+    torch.cuda.synchronize()
+    slots = [g * ldk + pos for g in range(G)]
+    # the appended records are the oracle's (bit for bit; norms within 1 ulp)
+    for k in ("codes", "signs"):
+        assert np.array_equal(krec[k][slots].cpu().numpy(), ek[k]), k
+    assert np.array_equal(vrec["codes"][slots].cpu().numpy(), ev["codes"])
+    for got, want in ((krec["norms"][slots], ek["norms"]), (vrec["norms"][slots], ev["norms"])):
+        got = got.cpu().numpy().astype(np.float64)
+        assert (np.abs(got - want) <= np.spacing(np.abs(want).astype(np.float32))).all()
+    assert np.allclose(krec["rnorms"][slots].cpu().numpy(), ek["rnorms"], rtol=1e-5, atol=2e-5)
+    # every other record is untouched
+    mask = torch.ones(G * ldk, dtype=torch.bool, device=dev)
+    mask[slots] = False
+    for k in krec:
+        assert torch.equal(krec[k][mask], before[k][mask]), k
+    for k in vrec:
+        assert torch.equal(vrec[k][mask], vbefore[k][mask]), k
+    # attention over tokens 0..pos with the oracle's records throughout
+    for k in ("codes", "signs", "norms", "rnorms"):
+        rk[k][slots] = ek[k]
+    for k in ("codes", "norms"):
+        rv[k][slots] = ev[k]
+    for g in range(G):
+        sl = slice(g * ldk, g * ldk + pos + 1)
+        lw, pw, ow = O.attend(pk, pv, Q[g].astype(np.float64), rk["codes"][sl], rk["signs"][sl], rk["norms"][sl],
+                              rk["rnorms"][sl], rv["codes"][sl], rv["norms"][sl], scale)
+        assert_close(logits[g].cpu().numpy(), lw, what=f"logits g{g}")
+        assert_close(probs[g].cpu().numpy(), pw, atol=1e-6, rtol=1e-3, what=f"probs g{g}")
+        assert_close(out[g].cpu().numpy(), ow, what=f"out g{g}")
+
+
+def test_decode_step_rejects_before_writing(tq):
+    d = 128
+    kctx, vctx = tq.Context(d, 3, 0), tq.Context(d, 3, 1, tq.TQ_MODE_MSE)
+    dev = torch.device("cuda")
+    krec, vrec = kctx.empty_records(2 * 16, dev), vctx.empty_records(2 * 16, dev)
+    q = torch.zeros((2, 4, d), device=dev)
+    nk = torch.ones((2, d), device=dev)
+    with pytest.raises(tq.TQError):        # pos past the cache
+        tq.tq_decode_step(kctx, vctx, q, nk, nk, krec, vrec, 16, 0.1, ldk=16)
+    with pytest.raises(tq.TQError):        # contexts swapped
+        tq.tq_decode_step(vctx, kctx, q, nk, nk, krec, vrec, 3, 0.1, ldk=16)
+    torch.cuda.synchronize()
+    assert not krec["codes"].any() and not krec["norms"].any() and not vrec["codes"].any()
