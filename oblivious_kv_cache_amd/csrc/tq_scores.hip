@@ -32,15 +32,6 @@ namespace {
 
 constexpr int PREP_THREADS = 256;
 
-#ifndef TQ_SCORES_PREFETCH
-#define TQ_SCORES_PREFETCH 1
-#endif
-#ifndef TQ_NT_LOGITS
-#define TQ_NT_LOGITS 0
-#endif
-#ifndef TQ_SOFTMAX_NT_STORE
-#define TQ_SOFTMAX_NT_STORE 1   // probabilities stream out past the caches
-#endif
 #ifndef TQ_SOFTMAX_NT
 #define TQ_SOFTMAX_NT 512     // threads per row for rows of up to 32768 values
 #endif
@@ -362,30 +353,9 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int t = t0 + 16 * s + col;
-#if TQ_NT_LOGITS
-      if (head_ok && t < T) __builtin_nontemporal_store(l[s], lrow + t);
-#else
-      if (head_ok && t < T) lrow[t] = l[s];
-#endif
+      if (head_ok && t < T) lrow[t] = l[s];      // cached: the softmax reads them next
     }
   };
-#if TQ_SCORES_PREFETCH == 2
-  // three named register sets: the two following tiles load while one is scored
-  KeyWords<CB16, SB16, W> k0[4], k1[4], k2[4];
-  float n0[4], g0[4], n1[4], g1[4], n2[4], g2[4];
-  if (ntile > 0) load_tile(k0, n0, g0, tile0 * 64);
-  if (ntile > 1) load_tile(k1, n1, g1, (tile0 + 1) * 64);
-  for (int it = 0; it < ntile; it += 3) {
-    if (it + 2 < ntile) load_tile(k2, n2, g2, (tile0 + it + 2) * 64);
-    score_tile(k0, n0, g0, (tile0 + it) * 64);
-    if (it + 1 >= ntile) break;
-    if (it + 3 < ntile) load_tile(k0, n0, g0, (tile0 + it + 3) * 64);
-    score_tile(k1, n1, g1, (tile0 + it + 1) * 64);
-    if (it + 2 >= ntile) break;
-    if (it + 4 < ntile) load_tile(k1, n1, g1, (tile0 + it + 4) * 64);
-    score_tile(k2, n2, g2, (tile0 + it + 2) * 64);
-  }
-#elif TQ_SCORES_PREFETCH
   // two named register sets: the next tile's words load while this one is scored
   KeyWords<CB16, SB16, W> k0[4], k1[4];
   float n0[4], g0[4], n1[4], g1[4];
@@ -397,14 +367,6 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
     if (it + 2 < ntile) load_tile(k0, n0, g0, (tile0 + it + 2) * 64);
     score_tile(k1, n1, g1, (tile0 + it + 1) * 64);
   }
-#else
-  for (int it = 0; it < ntile; ++it) {
-    KeyWords<CB16, SB16, W> kw[4];
-    float nu[4], ga[4];
-    load_tile(kw, nu, ga, (tile0 + it) * 64);
-    score_tile(kw, nu, ga, (tile0 + it) * 64);
-  }
-#endif
 }
 
 int dispatch(const ScoreArgs &a, dim3 grid, int cb16, int sb16, int w, hipStream_t s) {
@@ -593,12 +555,10 @@ __global__ void __launch_bounds__(NT) softmax_reg_kernel(const float *in, float 
     float4 o = v[k];
     o.x *= f; o.y *= f; o.z *= f; o.w *= f;
     if (tid + k * NT < n4) {
-#if TQ_SOFTMAX_NT_STORE
+      // streamed out past the caches: their write-back would otherwise
+      // compete with the next scores pass
       typedef float f32x4v __attribute__((ext_vector_type(4)));
       __builtin_nontemporal_store(f32x4v{o.x, o.y, o.z, o.w}, reinterpret_cast<f32x4v *>(y) + tid + k * NT);
-#else
-      y[tid + k * NT] = o;
-#endif
     }
   }
 }
