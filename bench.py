@@ -222,6 +222,57 @@ def bench_attend(tq, wl, dev):
     return r
 
 
+def bench_decode_bits(tq, wl, dev, bits, steps=50):
+    """The default decode step (32 x 8 KV heads x 32768 tokens, d=128, GQA 4)
+    at another bit width: step time and the scores kernel's duration."""
+    import torch
+    B, Hkv, T, d, Hq = 32, 8, 32768, 128, 32
+    qpg, G = Hq // Hkv, B * Hkv
+    log(f"decode 32K at b={bits}: setup")
+    ctx = tq.Context(d, bits, seed=0)
+    K, _ = wl.outlier_keys_torch(B, Hkv, T, d, seed=2, device=dev)
+    cache = ctx.empty_records(G * T, dev)
+    tq.tq_quantize(ctx, K.view(G * T, d), out=cache)
+    del K
+    new_k, _ = wl.outlier_keys_torch(B, Hkv, 1, d, seed=102, device=dev)
+    new_k = new_k.view(G, d)
+    slot = {k: v[T - 1:] for k, v in cache.items()}
+    q = wl.gaussian_torch((B, Hq, d), 7, dev).view(G, qpg, d).contiguous()
+    logits = torch.empty((G, qpg, T), dtype=torch.float32, device=dev)
+    probs = torch.empty_like(logits)
+    ws = ctx.workspace(tq.TQ_OP_SCORES, G, qpg, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(0, steps, EVENT_EVERY)]
+
+    def step(e=None):
+        tq.tq_prep_queries(ctx, q, ws=ws)
+        tq.tq_quantize(ctx, new_k, out=slot, ldr=T)
+        if e is not None:
+            e[0].record()
+        tq.tq_scores_prepared(ctx, ws, G, qpg, cache, T=T, ldk=T, logits=logits)
+        if e is not None:
+            e[1].record()
+        tq.tq_softmax(logits, scale, probs=probs)
+
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i // EVENT_EVERY] if i % EVENT_EVERY == 0 else None)
+    torch.cuda.synchronize()
+    ms = 1000.0 * (time.perf_counter() - t0) / steps
+    sms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    sbytes = G * T * (ctx.code_bytes + ctx.sign_bytes + 8) + G * qpg * T * 4 + ws.numel()
+    r = {"ms_per_step": ms, "logits_per_s": G * qpg * T / (ms / 1e3), "scores_ms": sms,
+         "scores_bytes": sbytes, "scores_gbs": sbytes / (sms / 1e3) / 1e9,
+         "scores_hbm_frac": sbytes / (sms / 1e3) / 1e9 / HBM_PEAK_GBS}
+    log(f"  b={bits}: step {ms:.3f} ms, scores kernel {sms * 1e3:.1f} us = {r['scores_gbs']:.0f} GB/s")
+    ctx.close()
+    return r
+
+
 def bench_topk(tq, wl, dev, nq=10000, n=1000000, d=200, k=10):
     """Vector search: 10^6 unit-norm d=200 power-law database vectors, 10^4
     queries, top-10 by the estimator, recall of the exact fp32 top-1."""
@@ -352,6 +403,9 @@ def main():
         extra["softmax_32k"] = {"ms": sm_ms, "bytes": sm_bytes, "gbs": sm_bytes / (sm_ms / 1e3) / 1e9,
                                 "hbm_frac": sm_bytes / (sm_ms / 1e3) / 1e9 / HBM_PEAK_GBS}
         log(f"  softmax: {sm_ms * 1e3:.1f} us, {extra['softmax_32k']['gbs']:.0f} GB/s")
+        for b in (2, 4):
+            if b != bits:
+                extra[f"decode_32k_b{b}"] = bench_decode_bits(tq, wl, dev, b)
         log("quantize throughput: 2^20 x 128 bf16, power-law spectrum (two input sets, alternated)")
         Xs = [wl.power_law_torch(1 << 20, d, seed=3 + i, device=dev) for i in range(2)]
         qz = {}
