@@ -4,11 +4,11 @@ Default workload (one decode step at 32K context): batch 32 x 8 KV heads x
 32768 tokens x d=128 bf16 keys with 4 outlier channels per head (x10), 32 query
 heads (GQA group 4), 3-bit TurboQuant (2-bit Lloyd-Max codes + 1-bit QJL).
 The packed cache for tokens 0..T-2 is built before timing; one step then
-  1. prepares the queries (tq_prep_queries: projections, int8 operand digits),
-  2. quantizes the new token's key of every (batch, KV head) stream straight
-     into cache slot T-1 (tq_quantize, record stride T),
-  3. scores all T packed keys against the prepared queries (tq_scores_prepared),
-  4. takes the fp32 softmax of logits / sqrt(d) over the T tokens (tq_softmax),
+  1. quantizes the new token's key of every (batch, KV head) stream straight
+     into cache slot T-1 and prepares the queries (tq_decode_prep: both jobs
+     in one launch),
+  2. scores all T packed keys against the prepared queries (tq_scores_prepared),
+  3. takes the fp32 softmax of logits / sqrt(d) over the T tokens (tq_softmax),
 all on one stream.  The metric is logits per second over the whole step; for
 the roofline figure the scores kernel of every 5th timed step is bracketed by
 HIP events on the launch stream.
@@ -236,7 +236,6 @@ def bench_decode_bits(tq, wl, dev, bits, steps=50):
     del K
     new_k, _ = wl.outlier_keys_torch(B, Hkv, 1, d, seed=102, device=dev)
     new_k = new_k.view(G, d)
-    slot = {k: v[T - 1:] for k, v in cache.items()}
     q = wl.gaussian_torch((B, Hq, d), 7, dev).view(G, qpg, d).contiguous()
     logits = torch.empty((G, qpg, T), dtype=torch.float32, device=dev)
     probs = torch.empty_like(logits)
@@ -246,8 +245,7 @@ def bench_decode_bits(tq, wl, dev, bits, steps=50):
           for _ in range(0, steps, EVENT_EVERY)]
 
     def step(e=None):
-        tq.tq_prep_queries(ctx, q, ws=ws)
-        tq.tq_quantize(ctx, new_k, out=slot, ldr=T)
+        tq.tq_decode_prep(ctx, q, new_k, cache, T - 1, ldk=T, ws=ws)
         if e is not None:
             e[0].record()
         tq.tq_scores_prepared(ctx, ws, G, qpg, cache, T=T, ldk=T, logits=logits)
@@ -344,7 +342,6 @@ def main():
     del K
     new_k, _ = wl.outlier_keys_torch(B, Hkv, 1, d, seed=102, device=dev)
     new_k = new_k.view(G, d)
-    slot = {k: v[T - 1:] for k, v in cache.items()}
     q = wl.gaussian_torch((B, Hq, d), 7, dev).view(G, qpg, d).contiguous()
     logits = torch.empty((G, qpg, T), dtype=torch.float32, device=dev)
     probs = torch.empty_like(logits)
@@ -359,11 +356,10 @@ def main():
     ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for i in timed_steps}
 
-    # One stream: the query prep (tq_prep_queries) is split out of tq_scores so
-    # that the events bracket the scores kernel alone.
+    # One stream: the append of the new keys and the query prep run in one
+    # launch (tq_decode_prep), so the events bracket the scores kernel alone.
     def step(i=None):
-        tq.tq_prep_queries(ctx, q, ws=ws)
-        tq.tq_quantize(ctx, new_k, out=slot, ldr=T)
+        tq.tq_decode_prep(ctx, q, new_k, cache, T - 1, ldk=T, ws=ws)
         if i is not None:
             ev[i][0].record()
         tq.tq_scores_prepared(ctx, ws, G, qpg, cache, T=T, ldk=T, logits=logits)

@@ -202,6 +202,20 @@ int tq_attend(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G,
               float scale, float *logits, float *probs, float *out,
               void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* The append + query-prep half of a decode step: the new key of every group
+ * (and, if vctx is not NULL, its new value) is quantized into record
+ * g*ldk + pos of the caches, and the queries are prepared into ws exactly as
+ * tq_prep_queries does (so tq_scores_prepared over T = pos + 1 tokens
+ * follows).  For d = 128 and up to 4096 groups the jobs run in one launch
+ * (they are independent and each is latency-bound); otherwise in turn.
+ * Arguments as in tq_quantize and tq_prep_queries; pos < ldk;
+ * ws >= tq_workspace_size(TQ_OP_SCORES, G, qpg).  All checks happen before
+ * the first launch. */
+int tq_decode_prep(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G, int qpg,
+                   const void *new_k, const void *new_v, int dtype, int64_t ldx, int64_t pos,
+                   int64_t ldk, uint8_t *kcodes, uint8_t *ksigns, float *knorms, float *krnorms,
+                   uint8_t *vcodes, float *vnorms, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* One online decode step (xujun.org note 189244, KV 缓存: every generated
  * token's key and value are compressed as they are produced and appended to
  * the cache): on one stream, with no host synchronisation,
@@ -209,6 +223,8 @@ int tq_attend(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G,
  *      is quantized into key record g*ldk + pos (tq_quantize, kctx);
  *   2. the new value new_v[g] into value record g*ldk + pos (vctx);
  *   3. tq_attend over tokens 0..pos (T = pos + 1) of every group.
+ * Steps 1-2 and the query prep of step 3 are tq_decode_prep (one launch for
+ * d = 128).
  * Arguments as in tq_quantize and tq_attend; pos < ldk;
  * ws >= tq_workspace_size(TQ_OP_ATTEND, G, qpg, pos + 1) bytes.  All checks
  * happen before the first launch: on error nothing is written. */

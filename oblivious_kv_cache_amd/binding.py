@@ -23,7 +23,8 @@ TQ_MAX_D, TQ_MAX_TOPK = 256, 64
 EXPORTS = [
     "tq_init", "tq_init_mse", "tq_free", "tq_layout", "tq_host_params", "tq_get_params",
     "tq_quantize", "tq_workspace_size", "tq_scores", "tq_prep_queries", "tq_scores_prepared",
-    "tq_softmax", "tq_attend", "tq_decode_step", "tq_dequant", "tq_topk", "tq_strerror",
+    "tq_softmax", "tq_attend", "tq_decode_prep", "tq_decode_step", "tq_dequant", "tq_topk",
+    "tq_strerror",
 ]
 
 
@@ -60,6 +61,7 @@ def _load():
         "tq_scores_prepared": (I, [P, P, SZ, I64, I, I64, I64, P, P, P, P, P, P]),
         "tq_softmax": (I, [P, I64, I64, F, P, P]),
         "tq_attend": (I, [P, P, P, I64, I, I64, I64, P, P, P, P, P, P, F, P, P, P, P, SZ, P]),
+        "tq_decode_prep": (I, [P, P, P, I64, I, P, P, I, I64, I64, I64, P, P, P, P, P, P, P, SZ, P]),
         "tq_decode_step": (I, [P, P, P, I64, I, P, P, I, I64, I64, I64, P, P, P, P, P, P, F, P, P, P, P,
                                SZ, P]),
         "tq_dequant": (I, [P, P, P, P, P, I64, P, P]),
@@ -251,6 +253,26 @@ def tq_attend(kctx, vctx, q, krec, vrec, scale, T=None, ldk=None, want_logits=Fa
                          _ptr(vrec["codes"]), _ptr(vrec["norms"]), float(scale), _ptr(logits),
                          _ptr(probs), _ptr(out), _ptr(ws), ws.numel(), _stream()), "tq_attend")
     return out, logits, probs
+
+
+def tq_decode_prep(kctx, q, new_k, krec, pos, ldk=None, vctx=None, new_v=None, vrec=None, ws=None):
+    """Append new_k (and new_v) [G, d] at token pos of every group's caches and
+    prepare q [G, qpg, d] into a scores workspace (returned)."""
+    G, qpg, d = q.shape
+    assert new_k.shape == (G, d) and new_k.stride(1) == 1
+    if vctx is not None:
+        assert new_v.shape == (G, d) and new_v.dtype == new_k.dtype and new_v.stride() == new_k.stride()
+    dtype = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[new_k.dtype]
+    n = krec["codes"].shape[0]
+    ldk = ldk if ldk is not None else n // max(G, 1)
+    ws = ws if ws is not None else kctx.workspace(TQ_OP_SCORES, G, qpg, device=q.device)
+    _check(LIB.tq_decode_prep(kctx.handle, vctx.handle if vctx is not None else None, _ptr(q), G, qpg,
+                              _ptr(new_k), _ptr(new_v), dtype, new_k.stride(0), int(pos), ldk,
+                              _ptr(krec["codes"]), _ptr(krec["signs"]), _ptr(krec["norms"]),
+                              _ptr(krec["rnorms"]), _ptr(vrec["codes"]) if vrec is not None else None,
+                              _ptr(vrec["norms"]) if vrec is not None else None, _ptr(ws), ws.numel(),
+                              _stream()), "tq_decode_prep")
+    return ws
 
 
 def tq_decode_step(kctx, vctx, q, new_k, new_v, krec, vrec, pos, scale, ldk=None,

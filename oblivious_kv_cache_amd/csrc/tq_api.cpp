@@ -332,47 +332,93 @@ int tq_attend(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G,
                            vnorms, scale, logits, probs, out, ws, stream);
 }
 
+namespace {
+
+// Checks shared by the decode entry points (vctx may be null: keys only).
+int check_decode(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G, int qpg,
+                 const void *new_k, const void *new_v, int dtype, int64_t ldx, int64_t pos,
+                 int64_t ldk, const uint8_t *kcodes, const uint8_t *ksigns, const float *knorms,
+                 const float *krnorms, const uint8_t *vcodes, const float *vnorms, const void *ws) {
+  if (!kctx || kctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
+  if (vctx && (vctx->hp.mode != TQ_MODE_MSE || vctx->hp.d != kctx->hp.d)) return TQ_EINVAL;
+  const int d = kctx->hp.d;
+  if (G < 0 || qpg < 1 || qpg > 64 || pos < 0 || ldk < pos + 1) return TQ_EINVAL;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EINVAL;
+  if (ldx < d || (dtype == TQ_BF16 ? (ldx % 8) : (ldx % 4))) return TQ_EINVAL;
+  if (!q || !new_k || !kcodes || !ksigns || !knorms || !krnorms || !ws) return TQ_EINVAL;
+  if (vctx && (!new_v || !vcodes || !vnorms)) return TQ_EINVAL;
+  if (!aligned(new_k, 16) || !aligned(kcodes, 16) || !aligned(ksigns, 16) || !aligned(ws, 16) ||
+      !aligned(knorms, 4) || !aligned(krnorms, 4) || !aligned(q, 4))
+    return TQ_EINVAL;
+  if (vctx && (!aligned(new_v, 16) || !aligned(vcodes, 16) || !aligned(vnorms, 4))) return TQ_EINVAL;
+  int st = current_device_matches(kctx);
+  if (st != TQ_OK) return st;
+  if (vctx && vctx->device != kctx->device) return TQ_EINVAL;
+  if (G * ((qpg + 3) / 4) > 65535) return TQ_ENOTSUP;
+  return TQ_OK;
+}
+
+// Append + query prep: one fused launch where this build has one, else the
+// quantize and prep launches in turn (same results).
+int decode_prep(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G, int qpg,
+                const void *new_k, const void *new_v, int dtype, int64_t ldx, int64_t pos, int64_t ldk,
+                uint8_t *kcodes, uint8_t *ksigns, float *knorms, float *krnorms, uint8_t *vcodes,
+                float *vnorms, void *ws, hipStream_t stream) {
+  int st = tq::launch_decode_prep(kctx, vctx, q, G, qpg, new_k, new_v, dtype, ldx, pos, ldk, kcodes,
+                                  ksigns, knorms, krnorms, vcodes, vnorms, ws, stream);
+  if (st != TQ_ENOTSUP) return st;
+  st = tq::launch_quantize(kctx, new_k, dtype, G, ldx, ldk, kcodes + pos * kctx->code_bytes,
+                           ksigns + pos * kctx->sign_bytes, knorms + pos, krnorms + pos, stream);
+  if (st != TQ_OK) return st;
+  if (vctx) {
+    st = tq::launch_quantize(vctx, new_v, dtype, G, ldx, ldk, vcodes + pos * vctx->code_bytes, nullptr,
+                             vnorms + pos, nullptr, stream);
+    if (st != TQ_OK) return st;
+  }
+  return tq::launch_prep_queries(kctx, q, G, qpg, ws, stream);
+}
+
+}  // namespace
+
+int tq_decode_prep(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G, int qpg,
+                   const void *new_k, const void *new_v, int dtype, int64_t ldx, int64_t pos,
+                   int64_t ldk, uint8_t *kcodes, uint8_t *ksigns, float *knorms, float *krnorms,
+                   uint8_t *vcodes, float *vnorms, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_decode(kctx, vctx, q, G, qpg, new_k, new_v, dtype, ldx, pos, ldk, kcodes, ksigns,
+                        knorms, krnorms, vcodes, vnorms, ws);
+  if (st != TQ_OK) return st;
+  if (G == 0) return TQ_OK;
+  if (ws_bytes < tq::scores_ws_bytes(kctx, G, qpg)) return TQ_EINVAL;
+  return decode_prep(kctx, vctx, q, G, qpg, new_k, new_v, dtype, ldx, pos, ldk, kcodes, ksigns, knorms,
+                     krnorms, vcodes, vnorms, ws, stream);
+}
+
 int tq_decode_step(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G, int qpg,
                    const void *new_k, const void *new_v, int dtype, int64_t ldx, int64_t pos,
                    int64_t ldk, uint8_t *kcodes, uint8_t *ksigns, float *knorms, float *krnorms,
                    uint8_t *vcodes, float *vnorms, float scale, float *logits, float *probs,
                    float *out, void *ws, size_t ws_bytes, hipStream_t stream) {
   // everything is checked before the first launch: on error nothing is written
-  if (!kctx || !vctx || kctx->hp.mode != TQ_MODE_PROD || vctx->hp.mode != TQ_MODE_MSE)
-    return TQ_EINVAL;
-  const int d = kctx->hp.d;
-  if (vctx->hp.d != d) return TQ_EINVAL;
-  if (G < 0 || qpg < 1 || qpg > 64 || pos < 0 || ldk < pos + 1) return TQ_EINVAL;
+  if (!vctx) return TQ_EINVAL;
+  int st = check_decode(kctx, vctx, q, G, qpg, new_k, new_v, dtype, ldx, pos, ldk, kcodes, ksigns,
+                        knorms, krnorms, vcodes, vnorms, ws);
+  if (st != TQ_OK) return st;
   if (G == 0) return TQ_OK;
-  if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EINVAL;
-  if (ldx < d || (dtype == TQ_BF16 ? (ldx % 8) : (ldx % 4))) return TQ_EINVAL;
-  if (!q || !new_k || !new_v || !kcodes || !ksigns || !knorms || !krnorms || !vcodes || !vnorms ||
-      !out || !ws)
+  if (!out || !aligned(out, 4) || (probs && !logits) || (logits && !aligned(logits, 4)) ||
+      (probs && !aligned(probs, 4)) || !std::isfinite(scale))
     return TQ_EINVAL;
-  if (probs && !logits) return TQ_EINVAL;
-  if (!aligned(new_k, 16) || !aligned(new_v, 16) || !aligned(kcodes, 16) || !aligned(ksigns, 16) ||
-      !aligned(vcodes, 16) || !aligned(ws, 16) || !aligned(knorms, 4) || !aligned(krnorms, 4) ||
-      !aligned(vnorms, 4) || !aligned(q, 4) || !aligned(out, 4) ||
-      (logits && !aligned(logits, 4)) || (probs && !aligned(probs, 4)))
-    return TQ_EINVAL;
-  if (!std::isfinite(scale)) return TQ_EINVAL;
   const int64_t T = pos + 1;
   if (ws_bytes < tq::attend_ws_bytes(kctx, G, qpg, T)) return TQ_EINVAL;
-  int st = current_device_matches(kctx);
-  if (st != TQ_OK) return st;
-  if (vctx->device != kctx->device) return TQ_EINVAL;
   st = tq::check_attend(kctx, vctx, G, qpg, T, ldk, probs != nullptr);
   if (st != TQ_OK) return st;
-  // 1-2: the new key and value of every group into slot pos of its cache
-  st = tq::launch_quantize(kctx, new_k, dtype, G, ldx, ldk, kcodes + pos * kctx->code_bytes,
-                           ksigns + pos * kctx->sign_bytes, knorms + pos, krnorms + pos, stream);
-  if (st != TQ_OK) return st;
-  st = tq::launch_quantize(vctx, new_v, dtype, G, ldx, ldk, vcodes + pos * vctx->code_bytes, nullptr,
-                           vnorms + pos, nullptr, stream);
+  // 1-2: the new key and value of every group into slot pos, the queries
+  // prepared into the front of ws (the attention workspace starts with them)
+  st = decode_prep(kctx, vctx, q, G, qpg, new_k, new_v, dtype, ldx, pos, ldk, kcodes, ksigns, knorms,
+                   krnorms, vcodes, vnorms, ws, stream);
   if (st != TQ_OK) return st;
   // 3: attention over tokens 0..pos
   return tq::launch_attend(kctx, vctx, q, G, qpg, T, ldk, kcodes, ksigns, knorms, krnorms, vcodes,
-                           vnorms, scale, logits, probs, out, ws, stream);
+                           vnorms, scale, logits, probs, out, ws, stream, true);
 }
 
 int tq_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs, const float *norms,

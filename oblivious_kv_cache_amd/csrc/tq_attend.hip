@@ -429,7 +429,8 @@ int check_attend(const tq_ctx *kc, const tq_ctx *vc, int64_t G, int qpg, int64_t
 int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G, int qpg, int64_t T,
                   int64_t ldk, const uint8_t *kcodes, const uint8_t *ksigns, const float *knorms,
                   const float *krnorms, const uint8_t *vcodes, const float *vnorms, float scale,
-                  float *logits, float *probs, float *out, void *ws, hipStream_t stream) {
+                  float *logits, float *probs, float *out, void *ws, hipStream_t stream,
+                  bool prepped) {
   const int d = kc->hp.d;
   if (probs && !logits) return TQ_EINVAL;
   int st = check_attend(kc, vc, G, qpg, T, ldk, probs != nullptr);
@@ -444,8 +445,10 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   float *part = reinterpret_cast<float *>(base + align256(groups * prep_stride(nm)));
   float *mstat = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(part) +
                                            align256(groups * nchunk * 4 * (d + 2) * 4));
-  st = launch_prep(kc, q, groups, qpg, hg, G * qpg, prep, stream);
-  if (st != TQ_OK) return st;
+  if (!prepped) {                      // else the queries are already prepared in ws
+    st = launch_prep(kc, q, groups, qpg, hg, G * qpg, prep, stream);
+    if (st != TQ_OK) return st;
+  }
   AttArgs a{};
   a.kcodes = kcodes;
   a.ksigns = ksigns;

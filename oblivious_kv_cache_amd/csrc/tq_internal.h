@@ -80,7 +80,15 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
                   int64_t T, int64_t ldk, const uint8_t *kcodes, const uint8_t *ksigns,
                   const float *knorms, const float *krnorms, const uint8_t *vcodes,
                   const float *vnorms, float scale, float *logits, float *probs, float *out,
-                  void *ws, hipStream_t stream);
+                  void *ws, hipStream_t stream, bool prepped = false);
+// Append one token per group (keys in kc, values in vc if not null) at record
+// g * ldk + pos and prepare the queries into ws, in one launch.  TQ_ENOTSUP
+// when this build has no fused kernel for the shapes (the caller then runs
+// launch_quantize and the prep apart).
+int launch_decode_prep(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G, int qpg,
+                       const void *new_k, const void *new_v, int dtype, int64_t ldx, int64_t pos,
+                       int64_t ldk, uint8_t *kcodes, uint8_t *ksigns, float *knorms, float *krnorms,
+                       uint8_t *vcodes, float *vnorms, void *ws, hipStream_t stream);
 size_t topk_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int k);
 int launch_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const uint8_t *codes,
                 const uint8_t *signs, const float *norms, const float *rnorms, int k,

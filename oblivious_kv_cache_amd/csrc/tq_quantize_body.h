@@ -1,0 +1,380 @@
+// Quantize kernel body: norm, rotation, scalar codes, residual, QJL sign sketch.
+//
+// Per vector x (xujun.org note 189244, sections 第一步：PolarQuant and
+// 第二步：QJL; suzuke blog "turboquant-compressing-ai-consciousness",
+// 技術上怎麼做到的, 第一步 to 第三步):
+//   nu = |x|,  y = Pi x / nu,  idx_i = #{k : t_k < y_i},  r = y - c[idx],
+//   gamma = |r|,  bit_j = [(S' r)_j >= 0] with S' = S Pi^T.
+//
+// Mapping onto CDNA4: both products are GEMMs over a tile of vectors and run
+// on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  The operands that are
+// not exactly representable in bf16 are split into hi + lo bf16 parts, which
+// keeps every product to about 2^-17 relative error so that a code or sign
+// flips only for coordinates within ~1e-5 of a decision boundary:
+//   GEMM 1 (Y^T = Pi X^T): Pi_hi x + Pi_lo x  (bf16 x is exact), plus
+//                          Pi_hi x_lo for fp32 inputs;
+//   GEMM 2 (Z^T = S' R^T): S'_hi r_hi + S'_hi r_lo + S'_lo r_hi.
+// A lane of the 16x16 accumulator holds 4 rows of one column.  The rows of Pi
+// and S' are permuted on the host so that lane group g (= lane / 16) ends up
+// with the contiguous coordinate range [g d/4, (g+1) d/4) of its vector: the
+// codebook search, the bit packing and the GEMM-2 operand (the residual) all
+// stay in that lane's registers, and each lane stores one contiguous run of
+// code bytes and sign bytes.
+#pragma once
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct QArgs {
+  const void *x;
+  int64_t n, ldx, ldr, ntiles;
+  uint8_t *codes, *signs;
+  float *norms, *rnorms;
+  const Frag *PiA_hi, *PiA_lo, *S2A_hi, *S2A_lo;
+  int d, m, prod, code_bytes, sign_bytes;
+  float tpos[8], cpos[8];
+};
+
+__device__ __forceinline__ bf16x8 as_bf(const Frag &f) { return __builtin_bit_cast(bf16x8, f); }
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Store nb bytes held little-endian in words[] at dst (any alignment).
+template <int NW>
+__device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t (&words)[NW], int nb) {
+  if (nb <= 0) return;
+  if ((((uintptr_t)dst) & 3) == 0 && (nb & 3) == 0) {
+    uint32_t *d32 = reinterpret_cast<uint32_t *>(dst);
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      if (4 * i < nb) d32[i] = words[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4 * NW; ++i)
+      if (i < nb) dst[i] = (uint8_t)(words[i >> 2] >> (8 * (i & 3)));
+  }
+}
+
+__device__ __forceinline__ void zero_bytes(uint8_t *dst, int nb) {
+  for (int i = 0; i < nb; ++i) dst[i] = 0;
+}
+
+// The kernel body, callable from a kernel that also runs other jobs: block
+// `block` of `nblocks` blocks working on this quantize job; `lds` holds the
+// operand fragments (USE_LDS: 4 FR x 64 Frags, filled here).
+template <int DPAD, bool BF16IN, bool USE_LDS, int NTL, int W, bool FULL>
+__device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int block, int nblocks) {
+  constexpr int NT = DPAD / 16;       // 16-row output tiles (coordinates)
+  constexpr int NK = DPAD / 32;       // 32-deep k blocks
+  constexpr int FR = NT * NK;         // operand fragments per matrix
+  constexpr int PER = DPAD / 4;       // coordinates (and sketch rows) per lane
+  constexpr int HALF = (1 << W) / 2;  // L / 2
+  constexpr int CW = (PER * W + 31) / 32;   // code words per lane
+  constexpr int SW = (PER + 31) / 32;       // sign words per lane
+  constexpr int CBYTES = PER * W / 8;       // code bytes per lane (whole bytes: PER % 8 == 0)
+  constexpr int SBYTES = PER / 8;
+  // d == DPAD (and m == d): when the lane groups' byte runs are whole dwords
+  // and together fill a 16-byte-multiple record, the record has no padding
+  // and every lane stores plain dwords
+  constexpr bool CEXACT = FULL && CBYTES % 4 == 0 && (4 * CBYTES) % 16 == 0;
+  constexpr bool SEXACT = FULL && SBYTES % 4 == 0 && (4 * SBYTES) % 16 == 0;
+
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+
+  if constexpr (USE_LDS) {
+    // Fill LDS with one batch of independent 16-byte loads per thread over
+    // all operand matrices (each matrix pointer stays a scalar; choosing it
+    // with a runtime index would re-load it from the kernel arguments), then
+    // store: one memory round trip.  Clamped indices keep the loads free of
+    // branches; a duplicate store of the last element rewrites the same value.
+    constexpr int NF = FR * 64;
+    constexpr int ITER = (NF + 511) / 512;        // USE_LDS launches 512 threads
+    // Without the sketch (MSE-only contexts) slots 2 and 3 receive a second
+    // copy of Pi's fragments, unused: the loads stay unconditional.
+    const Frag *const s0 = a.PiA_hi, *const s1 = a.PiA_lo;
+    const Frag *const s2 = a.prod ? a.S2A_hi : a.PiA_hi, *const s3 = a.prod ? a.S2A_lo : a.PiA_lo;
+    Frag t0[ITER], t1[ITER], t2[ITER], t3[ITER];
+#pragma unroll
+    for (int b = 0; b < ITER; ++b) {
+      const int i = min(b * 512 + (int)threadIdx.x, NF - 1);
+      t0[b] = s0[i];
+      t1[b] = s1[i];
+      t2[b] = s2[i];
+      t3[b] = s3[i];
+    }
+#pragma unroll
+    for (int b = 0; b < ITER; ++b) {
+      const int i = min(b * 512 + (int)threadIdx.x, NF - 1);
+      lds[i] = t0[b];
+      lds[NF + i] = t1[b];
+      lds[2 * NF + i] = t2[b];
+      lds[3 * NF + i] = t3[b];
+    }
+    __syncthreads();
+  }
+  // Fragment f of operand matrix `which` for this lane.  `lofs` is re-made
+  // opaque in every tile iteration so that address arithmetic for all
+  // fragments is not hoisted out of the loop into registers.
+  int lofs = lane;
+  const Frag *const PiH = a.PiA_hi, *const PiL = a.PiA_lo, *const S2H = a.S2A_hi, *const S2L = a.S2A_lo;
+  auto frag = [&](int which, int f) -> bf16x8 {
+    if constexpr (USE_LDS) {
+      return as_bf(lds[(which * FR + f) * 64 + lofs]);
+    } else {
+      const Frag *src = which == 0 ? PiH : which == 1 ? PiL : which == 2 ? S2H : S2L;
+      return as_bf(src[f * 64 + lofs]);
+    }
+  };
+
+  const int64_t wave = ((int64_t)block * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)nblocks * blockDim.x) >> 6;
+
+  for (int64_t tile = wave; tile < a.ntiles; tile += nwaves) {
+    // The operand fragments are loop-invariant; a memory clobber per tile keeps
+    // the compiler from hoisting all of them into registers.
+    __asm__ volatile("" ::: "memory");
+    // Number of real coordinates / sketch rows in this lane's range.  Kept
+    // opaque so the per-coordinate compares are not hoisted out of the loop.
+    int nval = a.d - grp * PER, mval = a.m - grp * PER, xval = a.d - grp * 8;
+    lofs = lane;
+    __asm__ volatile("" : "+v"(nval), "+v"(mval), "+v"(xval), "+v"(lofs));
+    const int64_t vbase = tile * (16 * NTL);
+    bf16x8 bx[NTL][NK];
+    bf16x8 bxl[NTL][BF16IN ? 1 : NK];
+    double ss[NTL];
+    int64_t vi[NTL];
+    bool valid[NTL];
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      vi[t] = vbase + t * 16 + col;
+      valid[t] = vi[t] < a.n;
+      ss[t] = 0.0;
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const int j0 = k * 32 + grp * 8;
+        const bool in = valid[t] && (FULL || k * 32 < xval);   // j0 < d
+        if constexpr (BF16IN) {
+          Frag f = {{0u, 0u, 0u, 0u}};
+          if (in) f = *reinterpret_cast<const Frag *>(
+                      reinterpret_cast<const uint16_t *>(a.x) + vi[t] * a.ldx + j0);
+          bx[t][k] = as_bf(f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double v = (double)(float)bx[t][k][e];
+            ss[t] += v * v;
+          }
+        } else {
+          float4 lo4 = make_float4(0.f, 0.f, 0.f, 0.f), hi4 = lo4;
+          if (in) {
+            const float4 *p = reinterpret_cast<const float4 *>(
+                reinterpret_cast<const float *>(a.x) + vi[t] * a.ldx + j0);
+            lo4 = p[0];
+            hi4 = p[1];
+          }
+          const float xs[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const __bf16 h = (__bf16)xs[e];
+            bx[t][k][e] = h;
+            bxl[t][k][e] = (__bf16)(xs[e] - (float)h);
+            ss[t] += (double)xs[e] * (double)xs[e];
+          }
+        }
+      }
+      ss[t] += __shfl_xor(ss[t], 16);
+      ss[t] += __shfl_xor(ss[t], 32);
+    }
+
+    // Per vector: 1/nu, and state for the codes and the residual.
+    uint32_t cw[NTL][CW];
+    bf16x8 rh[NTL][NK], rl[NTL][NK];
+    float nu[NTL], inv[NTL], rs[NTL];
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      const double nud = sqrt(ss[t]);
+      nu[t] = (float)nud;
+      inv[t] = nud > 0.0 ? (float)(1.0 / nud) : 0.f;
+      rs[t] = 0.f;
+#pragma unroll
+      for (int i = 0; i < CW; ++i) cw[t][i] = 0u;
+    }
+
+    // GEMM 1, one 16-coordinate output tile at a time, each tile consumed at
+    // once by the codebook search (its accumulator is the only live state).
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      f32x4 acc[NTL];
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const bf16x8 ah = frag(0, u * NK + k), al = frag(1, u * NK + k);
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+          acc[t] = mfma(ah, bx[t][k], acc[t]);
+          acc[t] = mfma(al, bx[t][k], acc[t]);
+          if constexpr (!BF16IN) acc[t] = mfma(ah, bxl[t][k], acc[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int li = 4 * u + jj;                 // local coordinate index
+          const float y = acc[t][jj] * inv[t];
+          const float ay = fabsf(y);
+          uint32_t mm = 0;
+          float cm = a.cpos[0];
+#pragma unroll
+          for (int j = 0; j < HALF - 1; ++j) {
+            const bool gt = ay > a.tpos[j];
+            mm += gt ? 1u : 0u;
+            cm = gt ? a.cpos[j + 1] : cm;
+          }
+          // sign from the sign bit, with no lane masks: idx = HALF + mm for
+          // y >= +0, its mirror HALF - 1 - mm (= (HALF + mm) ^ (2 HALF - 1)) for
+          // y <= -0; r = y - copysign(c, y).  (y == +0 exactly lies on the
+          // middle threshold, inside the decision band.)
+          const uint32_t yb = __float_as_uint(y);
+          const uint32_t neg = (uint32_t)((int32_t)yb >> 31);
+          uint32_t idx = ((uint32_t)HALF + mm) ^ (neg & (uint32_t)(2 * HALF - 1));
+          float r = y - __uint_as_float((__float_as_uint(cm) & 0x7fffffffu) | (yb & 0x80000000u));
+          if constexpr (!FULL) {
+            if (li >= nval) {               // padding coordinates
+              idx = 0u;
+              r = 0.f;
+            }
+          }
+          const int bit = li * W;
+          cw[t][bit >> 5] |= idx << (bit & 31);
+          if (((bit & 31) + W) > 32) cw[t][(bit >> 5) + 1] |= idx >> (32 - (bit & 31));
+          rs[t] += r * r;
+          const __bf16 h = (__bf16)r;
+          rh[t][li >> 3][li & 7] = h;
+          rl[t][li >> 3][li & 7] = (__bf16)(r - (float)h);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep fragment loads from piling up
+    }
+
+    // a zero vector stores zero codes and gamma = 0 (its signs are cleared below)
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      if (!(nu[t] > 0.f)) {
+#pragma unroll
+        for (int i = 0; i < CW; ++i) cw[t][i] = 0u;
+        rs[t] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      rs[t] += __shfl_xor(rs[t], 16);
+      rs[t] += __shfl_xor(rs[t], 32);
+      if (valid[t]) {
+        uint8_t *rec = a.codes + vi[t] * a.ldr * a.code_bytes;
+        const int off = grp * CBYTES;
+        if constexpr (CEXACT) {
+          // the 4 lane groups' byte runs tile the record exactly, dword-aligned
+#pragma unroll
+          for (int i = 0; i < CBYTES / 4; ++i) reinterpret_cast<uint32_t *>(rec + off)[i] = cw[t][i];
+        } else {
+          store_bytes<CW>(rec + off, cw[t], min(CBYTES, a.code_bytes - off));
+          if (grp == 3 && 4 * CBYTES < a.code_bytes) zero_bytes(rec + 4 * CBYTES, a.code_bytes - 4 * CBYTES);
+        }
+        if (grp == 0) a.norms[vi[t] * a.ldr] = nu[t];
+      }
+    }
+
+    if (a.prod) {
+      // GEMM 2 (JL sketch of the residual), one 16-row output tile at a time.
+      uint32_t sw[NTL][SW];
+#pragma unroll
+      for (int t = 0; t < NTL; ++t)
+#pragma unroll
+        for (int i = 0; i < SW; ++i) sw[t][i] = 0u;
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        f32x4 z[NTL];
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) z[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          const bf16x8 sh = frag(2, u * NK + k), sl = frag(3, u * NK + k);
+#pragma unroll
+          for (int t = 0; t < NTL; ++t) {
+            z[t] = mfma(sh, rh[t][k], z[t]);
+            z[t] = mfma(sh, rl[t][k], z[t]);
+            z[t] = mfma(sl, rh[t][k], z[t]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int li = 4 * u + jj;
+            const bool b = (FULL || li < mval) && z[t][jj] >= 0.f;
+            sw[t][li >> 5] |= (b ? 1u : 0u) << (li & 31);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        if (!(nu[t] > 0.f)) {
+#pragma unroll
+          for (int i = 0; i < SW; ++i) sw[t][i] = 0u;
+        }
+        if (valid[t]) {
+          uint8_t *rec = a.signs + vi[t] * a.ldr * a.sign_bytes;
+          const int off = grp * SBYTES;
+          if constexpr (SEXACT) {
+#pragma unroll
+            for (int i = 0; i < SBYTES / 4; ++i) reinterpret_cast<uint32_t *>(rec + off)[i] = sw[t][i];
+          } else {
+            store_bytes<SW>(rec + off, sw[t], min(SBYTES, a.sign_bytes - off));
+            if (grp == 3 && 4 * SBYTES < a.sign_bytes) zero_bytes(rec + 4 * SBYTES, a.sign_bytes - 4 * SBYTES);
+          }
+          if (grp == 0) a.rnorms[vi[t] * a.ldr] = nu[t] > 0.f ? sqrtf(rs[t]) : 0.f;
+        }
+      }
+    }
+  }
+}
+
+// Kernel arguments of one quantize job (vector i goes to record i * ldr).
+inline QArgs make_qargs(const tq_ctx *ctx, const void *x, int64_t n, int64_t ldx, int64_t ldr,
+                        uint8_t *codes, uint8_t *signs, float *norms, float *rnorms) {
+  QArgs a{};
+  a.x = x;
+  a.n = n;
+  a.ldx = ldx;
+  a.ldr = ldr;
+  a.codes = codes;
+  a.signs = signs;
+  a.norms = norms;
+  a.rnorms = rnorms;
+  a.PiA_hi = ctx->PiA_hi;
+  a.PiA_lo = ctx->PiA_lo;
+  a.S2A_hi = ctx->S2A_hi;
+  a.S2A_lo = ctx->S2A_lo;
+  a.d = ctx->hp.d;
+  a.m = ctx->hp.m;
+  a.prod = ctx->hp.mode == TQ_MODE_PROD;
+  a.code_bytes = ctx->code_bytes;
+  a.sign_bytes = ctx->sign_bytes;
+  for (int j = 0; j < 8; ++j) {
+    a.tpos[j] = ctx->tpos[j];
+    a.cpos[j] = ctx->cpos[j];
+  }
+  return a;
+}
+
+}  // namespace
+}  // namespace tq

@@ -43,12 +43,15 @@ def _clear_rows(p, G, d, seed, bf16):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("G,qpg,ldk,pos,bf16", [(3, 4, 700, 600, False), (2, 4, 1100, 1024, True),
-                                                (2, 3, 64, 0, False), (1, 8, 520, 511, True)])
-def test_decode_step_matches_oracle(tq, G, qpg, ldk, pos, bf16):
-    d = 128
-    pk, pv = O.make_params(d, 3, 0), O.make_params(d, 3, 1, "mse")
-    kctx, vctx = tq.Context(d, 3, 0), tq.Context(d, 3, 1, tq.TQ_MODE_MSE)
+# d = 128 with equal key/value bits takes the one-launch append + prep; d = 64
+# and mixed bit widths take the separate launches
+@pytest.mark.parametrize("d,kb,vb,G,qpg,ldk,pos,bf16", [
+    (128, 3, 3, 3, 4, 700, 600, False), (128, 3, 3, 2, 4, 1100, 1024, True), (128, 3, 3, 2, 3, 64, 0, False),
+    (128, 3, 3, 1, 8, 520, 511, True), (128, 4, 4, 2, 4, 300, 299, True), (128, 2, 2, 3, 4, 90, 50, False),
+    (64, 3, 3, 2, 4, 600, 555, False), (128, 3, 2, 2, 4, 400, 123, True)])
+def test_decode_step_matches_oracle(tq, d, kb, vb, G, qpg, ldk, pos, bf16):
+    pk, pv = O.make_params(d, kb, 0), O.make_params(d, vb, 1, "mse")
+    kctx, vctx = tq.Context(d, kb, 0), tq.Context(d, vb, 1, tq.TQ_MODE_MSE)
     K = wl.gaussian((G * ldk, d), 70)
     V = wl.gaussian((G * ldk, d), 71)
     rk, rv = O.quantize(pk, K), O.quantize(pv, V)
@@ -65,7 +68,7 @@ def test_decode_step_matches_oracle(tq, G, qpg, ldk, pos, bf16):
     nk = torch.from_numpy(newk.astype(np.float32)).to(dev).to(dt)
     nv = torch.from_numpy(newv.astype(np.float32)).to(dev).to(dt)
     scale = 1.0 / math.sqrt(d)
-    print(f"decode step G={G} qpg={qpg} ldk={ldk} pos={pos} bf16={bf16}", flush=True)
+    print(f"decode step d={d} kb={kb} vb={vb} G={G} qpg={qpg} ldk={ldk} pos={pos} bf16={bf16}", flush=True)
     out, logits, probs = tq.tq_decode_step(kctx, vctx, torch.from_numpy(Q).to(dev), nk, nv, krec, vrec,
                                            pos, scale, ldk=ldk, want_logits=True, want_probs=True)
     torch.cuda.synchronize()
@@ -112,3 +115,53 @@ def test_decode_step_rejects_before_writing(tq):
         tq.tq_decode_step(vctx, kctx, q, nk, nk, krec, vrec, 3, 0.1, ldk=16)
     torch.cuda.synchronize()
     assert not krec["codes"].any() and not krec["norms"].any() and not vrec["codes"].any()
+
+
+@pytest.mark.parametrize("d,bits,with_v", [(128, 3, True), (128, 3, False), (128, 2, True), (64, 3, False)])
+def test_decode_prep_matches_separate_calls(tq, d, bits, with_v):
+    """tq_decode_prep (one launch at d = 128) writes exactly what tq_quantize
+    and tq_prep_queries write, and scoring the prepared workspace over T =
+    pos + 1 tokens equals tq_scores on the updated cache."""
+    G, qpg, ldk, pos = 5, 4, 300, 211
+    dev = torch.device("cuda")
+    kctx = tq.Context(d, bits, 0)
+    vctx = tq.Context(d, bits, 1, tq.TQ_MODE_MSE) if with_v else None
+    kc, ks, kn, kr = wl.random_records(G * ldk, kctx.code_bytes, kctx.sign_bytes, seed=80)
+    krec = {"codes": kc, "signs": ks, "norms": kn, "rnorms": kr}
+    krec = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in krec.items()}
+    vrec = None
+    if with_v:
+        vc_, _, vn, _ = wl.random_records(G * ldk, vctx.code_bytes, 16, seed=81)
+        vrec = {"codes": torch.from_numpy(vc_).to(dev), "norms": torch.from_numpy(vn).to(dev)}
+    nk = torch.from_numpy(wl.bf16_round(wl.gaussian((G, d), 82))).to(dev).to(torch.bfloat16)
+    nv = torch.from_numpy(wl.bf16_round(wl.gaussian((G, d), 83))).to(dev).to(torch.bfloat16)
+    q = torch.from_numpy(wl.gaussian((G, qpg, d), 84)).to(dev)
+    k2 = {k: v.clone() for k, v in krec.items()}
+    v2 = {k: v.clone() for k, v in vrec.items()} if with_v else None
+    print(f"decode prep d={d} b={bits} values={with_v}", flush=True)
+    ws = tq.tq_decode_prep(kctx, q, nk, krec, pos, ldk=ldk, vctx=vctx, new_v=nv if with_v else None, vrec=vrec)
+    tq.tq_quantize(kctx, nk, out={k: v[pos:] for k, v in k2.items()}, ldr=ldk)
+    if with_v:
+        tq.tq_quantize(vctx, nv, out={"codes": v2["codes"][pos:], "signs": None, "norms": v2["norms"][pos:],
+                                      "rnorms": None}, ldr=ldk)
+    ws2 = tq.tq_prep_queries(kctx, q)
+    torch.cuda.synchronize()
+    for k in krec:
+        assert torch.equal(krec[k], k2[k]), k
+    if with_v:
+        for k in vrec:
+            assert torch.equal(vrec[k], v2[k]), k
+    # the prepared state of every (group, 4-head block): NM operand fragments
+    # of 1 KB and 64 B of constants, in 256-byte-aligned strides
+    cb16, sb16, w = kctx.code_bytes // 16, kctx.sign_bytes // 16, kctx.w
+    nm = 2 * cb16 + (2 * cb16 if w == 3 else 0) + 2 * sb16
+    used, stride = nm * 1024 + 64, (nm * 1024 + 64 + 255) // 256 * 256
+    ngroups = G * ((qpg + 3) // 4)
+    a = ws[:ngroups * stride].view(ngroups, stride)[:, :used]
+    b = ws2[:ngroups * stride].view(ngroups, stride)[:, :used]
+    assert torch.equal(a, b)
+    T = pos + 1
+    got = tq.tq_scores_prepared(kctx, ws, G, qpg, krec, T=T, ldk=ldk)
+    ref = tq.tq_scores(kctx, q, k2, T=T, ldk=ldk)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
