@@ -113,6 +113,11 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
     delete ctx;
     return TQ_EHIP;
   }
+  {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, ctx->device) == hipSuccess && v > 0)
+      ctx->cus = v;
+  }
   const int dpad = ctx->dpad;
   const size_t nfr = (size_t)(dpad / 16) * (dpad / 32) * 64;
   const size_t bytes_f32 = sizeof(float) * ((size_t)2 * d * d + (size_t)2 * m * d);

@@ -33,6 +33,7 @@ struct alignas(16) Frag {
 struct tq_ctx {
   tq::HostParams hp;
   int device = 0;
+  int cus = 256;       // compute units of that device (grid sizing)
   int dpad = 0;        // d rounded up to the quantize kernel's tile (32/64/128/256)
   int code_bytes = 0;
   int sign_bytes = 0;

@@ -25,14 +25,8 @@ int launch_w(const QArgs &a, int w, int blocks, hipStream_t s) {
 }
 
 template <int DPAD, bool USE_LDS, int NTL>
-int launch_d(const QArgs &a, int w, bool bf16, hipStream_t s) {
+int launch_d(const QArgs &a, int w, bool bf16, int cus, hipStream_t s) {
   const int64_t per_block_tiles = USE_LDS ? 8 : 4;   // one tile per wave per pass
-  int cus = 256;
-  int dev = 0;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-  }
   const int64_t want = (a.ntiles + per_block_tiles - 1) / per_block_tiles;
   const int64_t cap = USE_LDS ? (int64_t)cus : (int64_t)cus * 4;
   const int blocks = (int)(want < cap ? (want > 0 ? want : 1) : cap);
@@ -56,22 +50,22 @@ int launch_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int6
   switch (ctx->dpad) {
     case 32:
       a.ntiles = (n + 31) / 32;
-      return launch_d<32, true, 2>(a, w, bf16, stream);
+      return launch_d<32, true, 2>(a, w, bf16, ctx->cus, stream);
     case 64:
       a.ntiles = (n + 31) / 32;
-      return launch_d<64, true, 2>(a, w, bf16, stream);
+      return launch_d<64, true, 2>(a, w, bf16, ctx->cus, stream);
     case 128:
       // few vectors (e.g. one decode token per KV head): 16-vector tiles, so
       // that twice as many waves share the work and each finishes sooner
       if (n <= 4096) {
         a.ntiles = (n + 15) / 16;
-        return launch_d<128, true, 1>(a, w, bf16, stream);
+        return launch_d<128, true, 1>(a, w, bf16, ctx->cus, stream);
       }
       a.ntiles = (n + 31) / 32;
-      return launch_d<128, true, 2>(a, w, bf16, stream);
+      return launch_d<128, true, 2>(a, w, bf16, ctx->cus, stream);
     case 256:
       a.ntiles = (n + 15) / 16;
-      return launch_d<256, false, 1>(a, w, bf16, stream);
+      return launch_d<256, false, 1>(a, w, bf16, ctx->cus, stream);
     default:
       return TQ_ENOTSUP;
   }

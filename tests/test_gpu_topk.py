@@ -98,6 +98,24 @@ def test_topk_random_records_large_db(tq):
     check_topk(ids, sc, want, k)
 
 
+@pytest.mark.parametrize("k", [10, 16])
+def test_topk_pruning_with_mass_ties(tq, k):
+    # 60000 records that are copies of 40 distinct ones: every lane sees many
+    # exact ties of the best scores, so the pruning bound (the k-th best of
+    # the lanes' current bests) equals real scores again and again; scores
+    # equal to the bound must still enter, and ties resolve by lower id
+    d, bits, nq, n = 128, 3, 5, 60000
+    p, ctx, base, Q = _setup(tq, d, bits, nq, 40, seed=91, records="random")
+    pick = np.random.default_rng(92).integers(0, 40, n)
+    rec = {key: np.ascontiguousarray(v[pick]) for key, v in base.items()}
+    ids, sc = _run(tq, ctx, Q, rec, k)
+    want = O.scores(p, Q.astype(np.float64), rec["codes"], rec["signs"], rec["norms"], rec["rnorms"])
+    check_topk(ids, sc, want, k)
+    for qi in range(nq):                 # equal GPU scores come in increasing id order
+        for r in range(k - 1):
+            assert sc[qi, r] > sc[qi, r + 1] or (sc[qi, r] == sc[qi, r + 1] and ids[qi, r] < ids[qi, r + 1])
+
+
 def test_topk_errors(tq):
     ctx = tq.Context(128, 3, 0)
     rec = ctx.empty_records(10)
