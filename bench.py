@@ -34,7 +34,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-EVENT_EVERY = 5
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 FP32_VALU_TFLOPS = 78.6        # non-packed fp32 FMA: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 2
@@ -241,24 +240,22 @@ def bench_decode_bits(tq, wl, dev, bits, steps=50):
     probs = torch.empty_like(logits)
     ws = ctx.workspace(tq.TQ_OP_SCORES, G, qpg, device=dev)
     scale = 1.0 / math.sqrt(d)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(0, steps, EVENT_EVERY)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
 
     def step(e=None):
         tq.tq_decode_prep(ctx, q, new_k, cache, T - 1, ldk=T, ws=ws)
-        if e is not None:
-            e[0].record()
-        tq.tq_scores_prepared(ctx, ws, G, qpg, cache, T=T, ldk=T, logits=logits)
-        if e is not None:
-            e[1].record()
+        tq.tq_scores_prepared(ctx, ws, G, qpg, cache, T=T, ldk=T, logits=logits, events=e)
         tq.tq_softmax(logits, scale, probs=probs)
 
+    for e in ev:                    # creates the events (first record) before timing
+        e[0].record()
+        e[1].record()
     for _ in range(10):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(ev[i // EVENT_EVERY] if i % EVENT_EVERY == 0 else None)
+        step(ev[i])
     torch.cuda.synchronize()
     ms = 1000.0 * (time.perf_counter() - t0) / steps
     sms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
@@ -349,22 +346,22 @@ def main():
     scale = 1.0 / math.sqrt(d)
     torch.cuda.synchronize()
 
-    # HIP events bracket the scores kernel of every EVENT_EVERY-th timed step
-    # (each recorded event costs the stream a few microseconds, so bracketing
-    # every step would inflate the step time it is meant to explain)
-    timed_steps = list(range(0, args.steps, EVENT_EVERY))
-    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for i in timed_steps}
+    # HIP events time the scores kernel of every timed step.  They are
+    # recorded by the kernel's own dispatch (tq_scores_prepared_timed, i.e.
+    # hipExtLaunchKernel with start/stop events), so they bracket exactly the
+    # kernel and add no packets to the stream between the step's launches.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e in ev:                    # creates the events (first record) before timing
+        e[0].record()
+        e[1].record()
 
     # One stream: the append of the new keys and the query prep run in one
-    # launch (tq_decode_prep), so the events bracket the scores kernel alone.
+    # launch (tq_decode_prep), then the scores kernel, then the softmax.
     def step(i=None):
         tq.tq_decode_prep(ctx, q, new_k, cache, T - 1, ldk=T, ws=ws)
-        if i is not None:
-            ev[i][0].record()
-        tq.tq_scores_prepared(ctx, ws, G, qpg, cache, T=T, ldk=T, logits=logits)
-        if i is not None:
-            ev[i][1].record()
+        tq.tq_scores_prepared(ctx, ws, G, qpg, cache, T=T, ldk=T, logits=logits,
+                              events=None if i is None else ev[i])
         tq.tq_softmax(logits, scale, probs=probs)
 
     log(f"warmup {args.warmup} steps")
@@ -374,11 +371,11 @@ def main():
     log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i if i in ev else None)
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1000.0 * wall / args.steps
-    score_ms = float(np.mean([a.elapsed_time(b) for a, b in ev.values()]))
+    score_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     n_logits = G * qpg * T
     value = n_logits / (ms_step / 1000.0)
 

@@ -180,6 +180,19 @@ int tq_scores_prepared(const tq_ctx *ctx, const void *ws, size_t ws_bytes, int64
                        const float *norms, const float *rnorms, float *logits,
                        hipStream_t stream);
 
+/* tq_scores_prepared with kernel timing: identical arguments, checks and
+ * results; in addition the scores kernel's own dispatch records `start` when
+ * it begins and `stop` when it ends (hipExtLaunchKernel), so that
+ * hipEventElapsedTime(start, stop) is the kernel's execution time, with no
+ * event packets of their own around it on the stream.  start and stop are
+ * events the caller created on the ctx's device with timing enabled; either
+ * may be NULL.  When G or T is 0 nothing is launched and the events are not
+ * touched.  The events stay owned by the caller. */
+int tq_scores_prepared_timed(const tq_ctx *ctx, const void *ws, size_t ws_bytes, int64_t G, int qpg,
+                             int64_t T, int64_t ldk, const uint8_t *codes, const uint8_t *signs,
+                             const float *norms, const float *rnorms, float *logits,
+                             hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 /* Row softmax of scale * logits: probs[r][t] = exp(s l - max_r) / sum.
  * logits, probs [device] float [rows][T]; probs == logits is allowed. */
 int tq_softmax(const float *logits, int64_t rows, int64_t T, float scale, float *probs,

@@ -23,6 +23,7 @@ TQ_MAX_D, TQ_MAX_TOPK = 256, 64
 EXPORTS = [
     "tq_init", "tq_init_mse", "tq_free", "tq_layout", "tq_host_params", "tq_get_params",
     "tq_quantize", "tq_workspace_size", "tq_scores", "tq_prep_queries", "tq_scores_prepared",
+    "tq_scores_prepared_timed",
     "tq_softmax", "tq_attend", "tq_decode_prep", "tq_decode_step", "tq_dequant", "tq_topk",
     "tq_strerror",
 ]
@@ -59,6 +60,7 @@ def _load():
         "tq_scores": (I, [P, P, I64, I, I64, I64, P, P, P, P, P, P, SZ, P]),
         "tq_prep_queries": (I, [P, P, I64, I, P, SZ, P]),
         "tq_scores_prepared": (I, [P, P, SZ, I64, I, I64, I64, P, P, P, P, P, P]),
+        "tq_scores_prepared_timed": (I, [P, P, SZ, I64, I, I64, I64, P, P, P, P, P, P, P, P]),
         "tq_softmax": (I, [P, I64, I64, F, P, P]),
         "tq_attend": (I, [P, P, P, I64, I, I64, I64, P, P, P, P, P, P, F, P, P, P, P, SZ, P]),
         "tq_decode_prep": (I, [P, P, P, I64, I, P, P, I, I64, I64, I64, P, P, P, P, P, P, P, SZ, P]),
@@ -206,17 +208,36 @@ def tq_prep_queries(ctx, q, ws=None):
     return ws
 
 
-def tq_scores_prepared(ctx, ws, G, qpg, rec, T=None, ldk=None, logits=None):
-    """Logits [G, qpg, T] from a workspace made by tq_prep_queries."""
+def tq_scores_prepared(ctx, ws, G, qpg, rec, T=None, ldk=None, logits=None, events=None):
+    """Logits [G, qpg, T] from a workspace made by tq_prep_queries.
+
+    events: optional (start, stop) pair of timing-enabled torch.cuda.Event; the
+    scores kernel's own dispatch records them (tq_scores_prepared_timed), so
+    start.elapsed_time(stop) is that kernel's execution time."""
     n = rec["codes"].shape[0]
     ldk = ldk if ldk is not None else n // max(G, 1)
     T = T if T is not None else ldk
     if logits is None:
         logits = torch.empty((G, qpg, T), dtype=torch.float32, device=ws.device)
-    _check(LIB.tq_scores_prepared(ctx.handle, _ptr(ws), ws.numel(), G, qpg, T, ldk, _ptr(rec["codes"]),
-                                  _ptr(rec["signs"]), _ptr(rec["norms"]), _ptr(rec["rnorms"]),
-                                  _ptr(logits), _stream()), "tq_scores_prepared")
+    args = (ctx.handle, _ptr(ws), ws.numel(), G, qpg, T, ldk, _ptr(rec["codes"]), _ptr(rec["signs"]),
+            _ptr(rec["norms"]), _ptr(rec["rnorms"]), _ptr(logits), _stream())
+    if events is None:
+        _check(LIB.tq_scores_prepared(*args), "tq_scores_prepared")
+    else:
+        _check(LIB.tq_scores_prepared_timed(*args, _event_handle(events[0]), _event_handle(events[1])),
+               "tq_scores_prepared_timed")
     return logits
+
+
+def _event_handle(ev):
+    """The hipEvent_t of a timing-enabled torch.cuda.Event (None -> NULL).  torch
+    creates the underlying event at its first record(), so an event that was
+    never recorded is recorded once here, on the current stream."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        ev.record()
+    return ctypes.c_void_p(ev.cuda_event)
 
 
 def tq_softmax(logits, scale, probs=None):

@@ -289,6 +289,14 @@ int tq_scores_prepared(const tq_ctx *ctx, const void *ws, size_t ws_bytes, int64
                        int64_t T, int64_t ldk, const uint8_t *codes, const uint8_t *signs,
                        const float *norms, const float *rnorms, float *logits,
                        hipStream_t stream) {
+  return tq_scores_prepared_timed(ctx, ws, ws_bytes, G, qpg, T, ldk, codes, signs, norms, rnorms, logits,
+                                  stream, nullptr, nullptr);
+}
+
+int tq_scores_prepared_timed(const tq_ctx *ctx, const void *ws, size_t ws_bytes, int64_t G, int qpg,
+                             int64_t T, int64_t ldk, const uint8_t *codes, const uint8_t *signs,
+                             const float *norms, const float *rnorms, float *logits,
+                             hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
   if (G < 0 || T < 0 || ldk < T || qpg < 1 || qpg > 64) return TQ_EINVAL;
   if (G == 0 || T == 0) return TQ_OK;
@@ -300,7 +308,7 @@ int tq_scores_prepared(const tq_ctx *ctx, const void *ws, size_t ws_bytes, int64
   const int st = current_device_matches(ctx);
   if (st != TQ_OK) return st;
   return tq::launch_scores_prepared(ctx, ws, G, qpg, T, ldk, codes, signs, norms, rnorms, logits,
-                                    stream);
+                                    stream, start, stop);
 }
 
 int tq_softmax(const float *logits, int64_t rows, int64_t T, float scale, float *probs,

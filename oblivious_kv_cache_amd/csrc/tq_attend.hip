@@ -82,7 +82,8 @@ attend_partial_kernel(AttArgs a) {
 #pragma unroll
   for (int mu = 0; mu < NM; ++mu) A[mu] = reinterpret_cast<const i32x4 *>(prep)[mu * 64 + lane];
   const float *cst = reinterpret_cast<const float *>(prep + NM * 1024) + grp * 4;
-  const HeadConsts hc{cst[0], cst[1], cst[2], cst[3]};
+  const HeadConsts hc = HeadConsts::load(cst);
+  const ParityMasks<CB16, W> pm = parity_masks<CB16, W>(grp);
   const int head = hgi * 4 + grp;
   const uint8_t *kcb = a.kcodes + kg * a.ldk * a.kcb;
   const uint8_t *ksb = a.ksigns + kg * a.ldk * a.ksb;
@@ -159,7 +160,7 @@ attend_partial_kernel(AttArgs a) {
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        lg[tt][s] = tile_logit<CB16, SB16, W>(A, kw[tt][s], knu[tt][s], kga[tt][s], a.alpha, hc);
+        lg[tt][s] = tile_logit<CB16, SB16, W>(A, kw[tt][s], knu[tt][s], kga[tt][s], a.alpha, hc, pm);
         __asm__ volatile("" : "+v"(lg[tt][s]));
       }
 #pragma unroll

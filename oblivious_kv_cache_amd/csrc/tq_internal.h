@@ -67,7 +67,8 @@ int launch_prep_queries(const tq_ctx *ctx, const float *q, int64_t G, int qpg, v
 int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg, int64_t T,
                            int64_t ldk, const uint8_t *codes, const uint8_t *signs,
                            const float *norms, const float *rnorms, float *logits,
-                           hipStream_t stream);
+                           hipStream_t stream,
+                           hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 int launch_softmax(const float *logits, int64_t rows, int64_t T, float scale, float *probs,
                    hipStream_t stream);
 int launch_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs,

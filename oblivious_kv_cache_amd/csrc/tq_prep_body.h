@@ -210,13 +210,14 @@ __device__ __forceinline__ void prep_body(const PrepArgs &a, PrepSmem<SPLIT> &sm
     mx1 = fmaxf(mx1, red[i][8 + 2 * hh + 1]);
   }
   const float sc0 = mx0 > 0.f ? 127.f / mx0 : 1.f, sc1 = mx1 > 0.f ? 127.f / mx1 : 1.f;
-  const int nmc = 2 * cwpl, nmp = w == 3 ? nmc : 0;
+  const int nmc = 2 * cwpl, nmp = 2 * parity_words(cwpl, w);
   for (int mu = 0; mu < a.nm; ++mu) {
     int mloc, wpl;
     const float *vv;
     float S;
+    bool par = false;
     if (mu < nmc + nmp) {
-      const bool par = mu >= nmc;
+      par = mu >= nmc;
       mloc = par ? mu - nmc : mu;
       wpl = cwpl;
       vv = vP[hh] + (par ? ncb : 0);
@@ -228,13 +229,16 @@ __device__ __forceinline__ void prep_body(const PrepArgs &a, PrepSmem<SPLIT> &sm
       S = sc1;
     }
     const int pair = mloc >> 1, half = mloc & 1;
-    const int word = g * wpl + pair;
     const int j = 4 * half + e;
     uint32_t dw = 0u;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const int bitpos = 32 * word + 8 * b + j;
-      float u = ldexpf(vv[bitpos] * S, -j);
+      const int q = 8 * b + j;
+      // merged parity word `pair`: bit q belongs to the code starting at bit
+      // q of record word g*wpl + p, p = 3 pair + ((q - g*wpl) mod 3), if any
+      const int p = par ? 3 * pair + ((q - g * wpl) % 3 + 3) % 3 : pair;
+      const int bitpos = 32 * (g * wpl + p) + q;
+      float u = p < wpl ? ldexpf(vv[bitpos] * S, -j) : 0.f;
       if (j == 7) u = -u;                 // B byte value is -128 for bit 7
       // base-128 digits, all four computed and one selected (no per-lane loop)
       const float r0 = rintf(u);

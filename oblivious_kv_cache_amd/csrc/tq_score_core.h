@@ -9,10 +9,14 @@ namespace tq {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// MFMAs per 16-key tile: two per 32-bit record word (bit planes 0-3, 4-7),
-// over code words, parity words (3-bit codes) and sign words.
+// Parity words per lane group (3-bit codes): the parity bits of three
+// consecutive code words share one word (see ParityMasks).
+__host__ __device__ constexpr int parity_words(int cb16, int w) { return w == 3 ? (cb16 + 2) / 3 : 0; }
+
+// MFMAs per 16-key tile: two per 32-bit word (bit planes 0-3, 4-7), over the
+// code words, the merged parity words (3-bit codes) and the sign words.
 __host__ __device__ inline int mfma_count(int cb16, int sb16, int w) {
-  return 2 * cb16 + (w == 3 ? 2 * cb16 : 0) + 2 * sb16;
+  return 2 * cb16 + 2 * parity_words(cb16, w) + 2 * sb16;
 }
 
 // bytes of prepared query state per (query group of 4 heads): NM fragments of
@@ -50,19 +54,27 @@ __device__ __forceinline__ uint32_t key_word(const uint32_t *p) {
 // Words of key t for lane group g: uniform base pointers plus 32-bit byte
 // offsets (t * record bytes + g * bytes per lane group), so the loads take
 // the scalar-base + 32-bit-offset address form with no 64-bit math per lane.
+// Words of one key for lane group g, from the lane's first code byte cp and
+// first sign byte sp.
+template <bool NT, int CB16, int SB16, int W>
+__device__ __forceinline__ void load_key_words_at(KeyWords<CB16, SB16, W> &k, const uint8_t *cp,
+                                                  const uint8_t *sp, int grp) {
+#pragma unroll
+  for (int i = 0; i < CB16; ++i) k.cw[i] = key_word<NT>(reinterpret_cast<const uint32_t *>(cp + 4 * i));
+  if constexpr (W == 3) {   // first word of the next lane group's chunk (none for the last group)
+    const uint32_t nxt = key_word<NT>(reinterpret_cast<const uint32_t *>(cp + 4 * (grp < 3 ? CB16 : CB16 - 1)));
+    k.cw[CB16] = grp < 3 ? nxt : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < SB16; ++i) k.sw[i] = key_word<NT>(reinterpret_cast<const uint32_t *>(sp + 4 * i));
+}
+
 template <bool NT, int CB16, int SB16, int W>
 __device__ __forceinline__ void load_key_words(KeyWords<CB16, SB16, W> &k, const uint8_t *cbase,
                                                const uint8_t *sbase, uint32_t t, int grp) {
   const uint32_t co = t * (CB16 * 16) + (uint32_t)grp * (CB16 * 4);
   const uint32_t so = t * (SB16 * 16) + (uint32_t)grp * (SB16 * 4);
-#pragma unroll
-  for (int i = 0; i < CB16; ++i) k.cw[i] = key_word<NT>(reinterpret_cast<const uint32_t *>(cbase + co + 4 * i));
-  if constexpr (W == 3) {   // first word of the next lane group's chunk (none for the last group)
-    const uint32_t nxt = key_word<NT>(reinterpret_cast<const uint32_t *>(cbase + co + 4 * (grp < 3 ? CB16 : CB16 - 1)));
-    k.cw[CB16] = grp < 3 ? nxt : 0u;
-  }
-#pragma unroll
-  for (int i = 0; i < SB16; ++i) k.sw[i] = key_word<NT>(reinterpret_cast<const uint32_t *>(sbase + so + 4 * i));
+  load_key_words_at<NT>(k, cbase + co, sbase + so, grp);
 }
 
 // base[i] with a 32-bit byte offset (scalar base + 32-bit offset address form)
@@ -81,21 +93,50 @@ __device__ __forceinline__ i32x4 planes(uint32_t w, int half) {
                (int)(w & (0x01010101u << (s + 2))), (int)(w & (0x01010101u << (s + 3)))};
 }
 
+// Per-head constants of the prepared query: 1/S_P and 1/S_Q (scaled by 2^-7
+// for the digit-pair recombination of tile_logit), K_P and K_Q.
 struct HeadConsts {
   float invSP, invSQ, KP, KQ;
+  __device__ static HeadConsts load(const float *cst) {
+    return HeadConsts{cst[0] * 0x1.0p-7f, cst[1] * 0x1.0p-7f, cst[2], cst[3]};
+  }
 };
 
 template <int CB16, int SB16, int W>
 struct ScoreShape {
-  static constexpr int NMC = 2 * CB16, NMP = (W == 3) ? 2 * CB16 : 0, NMS = 2 * SB16;
+  static constexpr int NPW = parity_words(CB16, W);
+  static constexpr int NMC = 2 * CB16, NMP = 2 * NPW, NMS = 2 * SB16;
   static constexpr int NM = NMC + NMP + NMS;
 };
+
+// 3-bit codes are packed back to back, so code k starts at record bit 3k.
+// Lane group g holds record words g*CB16 .. g*CB16+CB16-1; since 32 = 2 (mod 3),
+// a code starts at bit q of record word r exactly when q = r (mod 3).  The
+// parity words of three consecutive record words therefore carry their
+// code-start bits on three disjoint residues, and are merged into one word
+// with the masks m[p] (bits q = g*CB16+p mod 3); bits elsewhere (parities of
+// windows that are not codes) are dropped.  The A fragments of a merged word
+// carry, for bit q, the weight of the code that starts there.
+template <int CB16, int W>
+struct ParityMasks {
+  uint32_t m[W == 3 ? CB16 : 1];
+};
+template <int CB16, int W>
+__device__ __forceinline__ ParityMasks<CB16, W> parity_masks(int grp) {
+  ParityMasks<CB16, W> pm{};
+  if constexpr (W == 3) {
+#pragma unroll
+    for (int p = 0; p < CB16; ++p) pm.m[p] = 0x49249249u << ((grp * CB16 + p) % 3);
+  }
+  return pm;
+}
 
 // Logit of head (lane / 16) of this query group for key (lane % 16) of the tile:
 //   nu * (P + alpha * gamma * Q), P and Q recombined from four int32 digit rows.
 template <int CB16, int SB16, int W>
 __device__ __forceinline__ float tile_logit(const i32x4 *A, const KeyWords<CB16, SB16, W> &k, float nu,
-                                            float gamma, float alpha, const HeadConsts &hc) {
+                                            float gamma, float alpha, const HeadConsts &hc,
+                                            const ParityMasks<CB16, W> &pm) {
   using Sh = ScoreShape<CB16, SB16, W>;
   i32x4 accP = {0, 0, 0, 0}, accQ = {0, 0, 0, 0};
 #pragma unroll
@@ -104,12 +145,18 @@ __device__ __forceinline__ float tile_logit(const i32x4 *A, const KeyWords<CB16,
     accP = mfma8(A[2 * p + 1], planes(k.cw[p], 1), accP);
   }
   if constexpr (W == 3) {
+    // bit q of par = parity of record bits q, q+1, q+2
+    uint32_t pw[Sh::NPW];
 #pragma unroll
     for (int p = 0; p < CB16; ++p) {
       const uint32_t lo = k.cw[p], hi = k.cw[p + 1];
       const uint32_t par = lo ^ __builtin_amdgcn_alignbit(hi, lo, 1) ^ __builtin_amdgcn_alignbit(hi, lo, 2);
-      accP = mfma8(A[Sh::NMC + 2 * p], planes(par, 0), accP);
-      accP = mfma8(A[Sh::NMC + 2 * p + 1], planes(par, 1), accP);
+      pw[p / 3] = (p % 3 == 0) ? (par & pm.m[p]) : (pw[p / 3] | (par & pm.m[p]));
+    }
+#pragma unroll
+    for (int f = 0; f < Sh::NPW; ++f) {
+      accP = mfma8(A[Sh::NMC + 2 * f], planes(pw[f], 0), accP);
+      accP = mfma8(A[Sh::NMC + 2 * f + 1], planes(pw[f], 1), accP);
     }
   }
 #pragma unroll
@@ -117,12 +164,14 @@ __device__ __forceinline__ float tile_logit(const i32x4 *A, const KeyWords<CB16,
     accQ = mfma8(A[Sh::NMC + Sh::NMP + 2 * p], planes(k.sw[p], 0), accQ);
     accQ = mfma8(A[Sh::NMC + Sh::NMP + 2 * p + 1], planes(k.sw[p], 1), accQ);
   }
-  const float P = fmaf((float)accP[3], 0x1.0p-21f,
-                       fmaf((float)accP[2], 0x1.0p-14f, fmaf((float)accP[1], 0x1.0p-7f, (float)accP[0]))) *
-                      hc.invSP - hc.KP;
-  const float Q = fmaf((float)accQ[3], 0x1.0p-21f,
-                       fmaf((float)accQ[2], 0x1.0p-14f, fmaf((float)accQ[1], 0x1.0p-7f, (float)accQ[0]))) *
-                      hc.invSQ - hc.KQ;
+  // digits recombined in pairs in int32 (d0*128 + d1 and d2*128 + d3; every
+  // |digit sum| < 2^22 for records of up to 256 coordinates, so the pairs
+  // stays below 2^30), then in fp32; invSP and invSQ carry the 2^-7 of the
+  // leading pair (HeadConsts::load)
+  const float P = fmaf(fmaf((float)(accP[2] * 128 + accP[3]), 0x1.0p-14f, (float)(accP[0] * 128 + accP[1])),
+                       hc.invSP, -hc.KP);
+  const float Q = fmaf(fmaf((float)(accQ[2] * 128 + accQ[3]), 0x1.0p-14f, (float)(accQ[0] * 128 + accQ[1])),
+                       hc.invSQ, -hc.KQ);
   return nu * fmaf(alpha * gamma, Q, P);
 }
 

@@ -25,6 +25,8 @@
 // recombined in fp32.  Four digits keep the coefficient error below ~2.5e-7 of
 // the largest coefficient.  A query-prep kernel builds these A fragments once
 // per (KV group, head group) into the caller's workspace.
+#include <hip/hip_ext.h>
+
 #include "tq_prep_body.h"
 
 namespace tq {
@@ -34,8 +36,9 @@ namespace {
 #define TQ_SOFTMAX_NT 512     // threads per row for rows of up to 32768 values
 #endif
 #ifndef TQ_SCORES_WAVES
-#define TQ_SCORES_WAVES 32768
+#define TQ_SCORES_WAVES 16384
 #endif
+
 
 template <int JC, bool SPLIT>
 __global__ void __launch_bounds__(PREP_THREADS) prep_kernel(PrepArgs a) {
@@ -67,7 +70,8 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
 #pragma unroll
   for (int mu = 0; mu < NM; ++mu) A[mu] = reinterpret_cast<const i32x4 *>(prep)[mu * 64 + lane];
   const float *cst = reinterpret_cast<const float *>(prep + NM * 1024) + grp * 4;
-  const HeadConsts hc{cst[0], cst[1], cst[2], cst[3]};
+  const HeadConsts hc = HeadConsts::load(cst);
+  const ParityMasks<CB16, W> pm = parity_masks<CB16, W>(grp);
   const int head = hgi * 4 + grp;
   const bool head_ok = head < a.qpg;
   float *lrow = a.logits + ((int64_t)kg * a.qpg + (head_ok ? head : 0)) * a.T;
@@ -96,13 +100,12 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   };
   auto score_tile = [&](const KeyWords<CB16, SB16, W> (&kw)[4], const float (&nu)[4], const float (&ga)[4],
                         int t0) {
-    // the four 16-key logits first (their MFMA chains interleave), then the
-    // guarded stores; materialising l keeps the norm loads from being sunk
-    // into the stores' branches
+    // the four 16-key logits first, then the guarded stores; materialising l
+    // keeps the norm loads from being sunk into the stores' branches
     float l[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      l[s] = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
+      l[s] = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc, pm);
       __asm__ volatile("" : "+v"(l[s]));
     }
 #pragma unroll
@@ -111,24 +114,69 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
       if (head_ok && t < T) lrow[t] = l[s];      // cached: the softmax reads them next
     }
   };
+  // Full 64-key tiles (every key below T; only a group's last tile can be
+  // partial) take one 32-bit offset per stream and tile: the four 16-key
+  // subtiles sit at fixed byte distances, which the loads and stores carry
+  // as immediate offsets.  No clamping, and the stores need no key guard.
+  auto load_full = [&](KeyWords<CB16, SB16, W> (&kw)[4], float (&nu)[4], float (&ga)[4], int t0) {
+    const uint32_t t = (uint32_t)(t0 + col);
+    const uint8_t *cp = cbase + (t * (CB16 * 16) + (uint32_t)grp * (CB16 * 4));
+    const uint8_t *sp = sbase + (t * (SB16 * 16) + (uint32_t)grp * (SB16 * 4));
+    const uint8_t *np = reinterpret_cast<const uint8_t *>(nbase) + t * 4u;
+    const uint8_t *rp = reinterpret_cast<const uint8_t *>(rbase) + t * 4u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      load_key_words_at<true>(kw[s], cp + s * (16 * CB16 * 16), sp + s * (16 * SB16 * 16), grp);
+      nu[s] = *reinterpret_cast<const float *>(np + 64 * s);
+      ga[s] = *reinterpret_cast<const float *>(rp + 64 * s);
+    }
+  };
+  auto score_full = [&](const KeyWords<CB16, SB16, W> (&kw)[4], const float (&nu)[4], const float (&ga)[4],
+                        int t0) {
+    float l[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      l[s] = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc, pm);
+      __asm__ volatile("" : "+v"(l[s]));
+    }
+    float *lp = lrow + (uint32_t)(t0 + col);
+    if (head_ok) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) lp[16 * s] = l[s];   // cached: the softmax reads them next
+    }
+  };
+  if (ntile <= 0) return;
+  // first key of this wave's i-th tile
+  auto key0 = [&](int i) { return (tile0 + i) * 64; };
+  const int nfull = key0(ntile - 1) + 64 > T ? ntile - 1 : ntile;
   // two named register sets: the next tile's words load while this one is scored
   KeyWords<CB16, SB16, W> k0[4], k1[4];
   float n0[4], g0[4], n1[4], g1[4];
-  if (ntile > 0) load_tile(k0, n0, g0, tile0 * 64);
-  for (int it = 0; it < ntile; it += 2) {
-    if (it + 1 < ntile) load_tile(k1, n1, g1, (tile0 + it + 1) * 64);
-    score_tile(k0, n0, g0, (tile0 + it) * 64);
-    if (it + 1 >= ntile) break;
-    if (it + 2 < ntile) load_tile(k0, n0, g0, (tile0 + it + 2) * 64);
-    score_tile(k1, n1, g1, (tile0 + it + 1) * 64);
+  if (nfull > 0) load_full(k0, n0, g0, key0(0));
+  for (int it = 0; it < nfull; it += 2) {
+    if (it + 1 < nfull) load_full(k1, n1, g1, key0(it + 1));
+    score_full(k0, n0, g0, key0(it));
+    if (it + 1 >= nfull) break;
+    if (it + 2 < nfull) load_full(k0, n0, g0, key0(it + 2));
+    score_full(k1, n1, g1, key0(it + 1));
+  }
+  if (nfull < ntile) {          // the group's last tile, keys clamped and stores guarded
+    load_tile(k0, n0, g0, key0(nfull));
+    score_tile(k0, n0, g0, key0(nfull));
   }
 }
 
-int dispatch(const ScoreArgs &a, dim3 grid, int cb16, int sb16, int w, hipStream_t s) {
-#define TQ_CASE(C, S, W_)                                        \
-  if (cb16 == C && sb16 == S && w == W_) {                       \
-    scores_kernel<C, S, W_><<<grid, 256, 0, s>>>(a);             \
-    return hip_status();                                         \
+// With events, the dispatch itself records them (hipExtLaunchKernel): they
+// bracket exactly this kernel's execution.
+int dispatch(const ScoreArgs &a, dim3 grid, int cb16, int sb16, int w, hipStream_t s, hipEvent_t e0,
+             hipEvent_t e1) {
+#define TQ_CASE(C, S, W_)                                                               \
+  if (cb16 == C && sb16 == S && w == W_) {                                              \
+    if (e0 || e1)                                                                       \
+      hipExtLaunchKernelGGL(scores_kernel<C, S, W_>, grid, dim3(256), 0, s, e0, e1, 0, a); \
+    else                                                                                \
+      scores_kernel<C, S, W_><<<grid, 256, 0, s>>>(a);                                  \
+    return hip_status();                                                                \
   }
   TQ_FOR_EACH_GEOMETRY(TQ_CASE)
 #undef TQ_CASE
@@ -179,7 +227,7 @@ int launch_prep_queries(const tq_ctx *ctx, const float *q, int64_t G, int qpg, v
 int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg, int64_t T,
                            int64_t ldk, const uint8_t *codes, const uint8_t *signs,
                            const float *norms, const float *rnorms, float *logits,
-                           hipStream_t stream) {
+                           hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (G == 0 || T == 0) return TQ_OK;
   int st = check_scores_shape(ctx, G, qpg, T, ldk);
   if (st != TQ_OK) return st;
@@ -207,7 +255,7 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   if (tpw > 64) tpw = 64;
   const int64_t chunks = (tiles + 4 * tpw - 1) / (4 * tpw);
   sa.tiles_per_wave = (int)tpw;
-  return dispatch(sa, dim3((unsigned)chunks, (unsigned)groups), cb16, sb16, w, stream);
+  return dispatch(sa, dim3((unsigned)chunks, (unsigned)groups), cb16, sb16, w, stream, ev_start, ev_stop);
 }
 
 int launch_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,

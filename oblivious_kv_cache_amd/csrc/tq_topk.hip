@@ -94,7 +94,8 @@ __global__ void __launch_bounds__(64 * scan_waves(KP)) topk_scan_kernel(ScanArgs
 #pragma unroll
   for (int mu = 0; mu < NM; ++mu) A[mu] = reinterpret_cast<const i32x4 *>(prep)[mu * 64 + lane];
   const float *cst = reinterpret_cast<const float *>(prep + NM * 1024) + grp * 4;
-  const HeadConsts hc{cst[0], cst[1], cst[2], cst[3]};
+  const HeadConsts hc = HeadConsts::load(cst);
+  const ParityMasks<CB16, W> pm = parity_masks<CB16, W>(grp);
 
   float ls[KP];
   int li[KP];
@@ -124,7 +125,7 @@ __global__ void __launch_bounds__(64 * scan_waves(KP)) topk_scan_kernel(ScanArgs
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int t = t0 + 16 * s + col;
-      const float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc);
+      const float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc, pm);
       const bool want = t < end && l > ls[KP - 1] && !(l < thr);
       // few scores pass once the lists have filled: a wave-uniform branch
       // skips the insertion network

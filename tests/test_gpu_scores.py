@@ -61,6 +61,8 @@ def test_scores_tiny_config_on_oracle_records(tq, bits):
     (128, 3, 3, 4, 1000, 1100), (128, 2, 2, 1, 65, 65), (128, 4, 2, 5, 130, 131),
     (128, 3, 1, 8, 1, 1), (200, 2, 2, 4, 777, 777), (200, 4, 1, 4, 500, 512),
     (64, 3, 4, 4, 300, 300), (96, 4, 2, 3, 257, 260), (256, 3, 1, 2, 129, 129), (40, 2, 1, 4, 63, 63),
+    # 3-bit codes at every code-word count per lane group (1 .. 6): merged parity words
+    (40, 4, 1, 4, 70, 70), (80, 4, 2, 4, 100, 100), (160, 4, 1, 6, 90, 96), (256, 4, 1, 4, 129, 129),
 ])
 def test_scores_random_records(tq, d, bits, G, qpg, T, ldk):
     ctx = tq.Context(d, bits, 0)
@@ -149,3 +151,29 @@ def test_prepared_queries_match_tq_scores_and_oracle(tq):
         torch.cuda.synchronize()
         assert torch.equal(got, ref)
         assert_close(got.cpu().numpy(), _oracle_grouped(p, Q, rec, G, T, T), what="logits")
+
+
+def test_timed_scores_match_and_time_the_kernel(tq):
+    # tq_scores_prepared_timed: same logits as tq_scores_prepared; the events
+    # recorded by the kernel's dispatch give a positive duration, and events
+    # passed to a call that launches nothing (T = 0) keep their earlier times
+    d, bits, G, qpg, T = 128, 3, 4, 4, 5000
+    ctx = tq.Context(d, bits, 0)
+    Q = wl.gaussian((G, qpg, d), 71)
+    c, sg, nu, ga = wl.random_records(G * T, ctx.code_bytes, ctx.sign_bytes, seed=72)
+    dev = _dev({"codes": c, "signs": sg, "norms": nu, "rnorms": ga})
+    q = torch.from_numpy(np.ascontiguousarray(Q, dtype=np.float32)).cuda()
+    print("scores timed: G=4 qpg=4 T=5000", flush=True)
+    ws = tq.tq_prep_queries(ctx, q)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ref = tq.tq_scores_prepared(ctx, ws, G, qpg, dev, T=T, ldk=T)
+    for _ in range(3):
+        got = tq.tq_scores_prepared(ctx, ws, G, qpg, dev, T=T, ldk=T, events=ev)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+        ms = ev[0].elapsed_time(ev[1])
+        assert 0.0 < ms < 100.0
+    empty = torch.empty((G, qpg, 0), dtype=torch.float32, device="cuda")
+    tq.tq_scores_prepared(ctx, ws, G, qpg, dev, T=0, ldk=T, logits=empty, events=ev)
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) == ms

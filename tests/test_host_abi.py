@@ -75,6 +75,8 @@ def test_argument_validation_before_any_device_work():
     assert L.tq_decode_prep(None, None, None, 1, 4, None, None, tq.TQ_F32, 128, 0, 1, None, None, None, None,
                             None, None, None, 0, None) == tq.TQ_EINVAL
     assert L.tq_scores_prepared(None, None, 0, 1, 4, 1, 1, None, None, None, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_scores_prepared_timed(None, None, 0, 1, 4, 1, 1, None, None, None, None, None, None,
+                                      None, None) == tq.TQ_EINVAL
     assert L.tq_softmax(None, -1, 4, 1.0, None, None) == tq.TQ_EINVAL
     assert L.tq_softmax(None, 0, 4, 1.0, None, None) == tq.TQ_OK          # empty: nothing to do
     assert L.tq_dequant(None, None, None, None, None, 1, None, None) == tq.TQ_EINVAL
