@@ -290,9 +290,10 @@ def bench_topk(tq, wl, dev, nq=10000, n=1000000, d=200, k=10):
         rec_k = {str(kk): float((ids[:, :kk] == top1[:, None]).any(dim=1).float().mean()) for kk in (1, 2, 4, 8, 10)}
         db_bytes = n * (ctx.code_bytes + ctx.sign_bytes + 8)
         # int8 MFMA work: per 16 vectors x 4 queries, NM v_mfma_i32_16x16x64_i8
-        # (2 per 32-bit record word and lane group: code, parity, sign words)
+        # (2 per 32-bit word and lane group: code words, merged parity words of
+        # 3-bit codes (one per three code words), sign words)
         cb16, sb16, w = ctx.code_bytes // 16, ctx.sign_bytes // 16, ctx.w
-        nm = 2 * cb16 + (2 * cb16 if w == 3 else 0) + 2 * sb16
+        nm = 2 * cb16 + (2 * ((cb16 + 2) // 3) if w == 3 else 0) + 2 * sb16
         mfma_ops = nq * n / 64 * nm * 2 * 16 * 16 * 64
         out[f"b{bits}"] = {"ms": ms, "pairs_per_s": nq * n / (ms / 1e3), "queries_per_s": nq / (ms / 1e3),
                            "db_bytes": db_bytes, "db_quantize_ms": ms_q, "recall_1_at_k": rec_k,
