@@ -56,9 +56,15 @@ struct ScoreArgs {
   float alpha;
 };
 
+// 16-key subtiles per wave iteration, i.e. per register set of the double
+// buffer (2 for 3-bit codes, whose larger records and A fragments would
+// otherwise hold the kernel to 3 waves per SIMD)
+__host__ __device__ constexpr int scores_spb(int cb16, int sb16, int w) { return w == 3 ? 2 : 4; }
+
 template <int CB16, int SB16, int W>
 __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
+  constexpr int SPB = scores_spb(CB16, SB16, W), KT = 16 * SPB;
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   const int wv = threadIdx.x >> 6;
   const int64_t gidx = blockIdx.y;       // key group * hg + head group
@@ -87,78 +93,92 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
 
   const int tile0 = (blockIdx.x * 4 + wv) * a.tiles_per_wave;
   int ntile = a.tiles_per_wave;
-  const int last = (T + 63) / 64;
+  const int last = (T + KT - 1) / KT;
   if (tile0 + ntile > last) ntile = last - tile0;
-  auto load_tile = [&](KeyWords<CB16, SB16, W> (&kw)[4], float (&nu)[4], float (&ga)[4], int t0) {
+  auto load_tile = [&](KeyWords<CB16, SB16, W> (&kw)[SPB], float (&nu)[SPB], float (&ga)[SPB], int t0) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < SPB; ++s) {
       const uint32_t t = (uint32_t)min(t0 + 16 * s + col, T - 1);
       load_key_words<true>(kw[s], cbase, sbase, t, grp);
       nu[s] = load_f32(nbase, t);
       ga[s] = load_f32(rbase, t);
     }
   };
-  auto score_tile = [&](const KeyWords<CB16, SB16, W> (&kw)[4], const float (&nu)[4], const float (&ga)[4],
+  auto score_tile = [&](const KeyWords<CB16, SB16, W> (&kw)[SPB], const float (&nu)[SPB], const float (&ga)[SPB],
                         int t0) {
     // the four 16-key logits first, then the guarded stores; materialising l
     // keeps the norm loads from being sunk into the stores' branches
-    float l[4];
+    float l[SPB];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < SPB; ++s) {
       l[s] = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc, pm);
       __asm__ volatile("" : "+v"(l[s]));
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < SPB; ++s) {
       const int t = t0 + 16 * s + col;
       if (head_ok && t < T) lrow[t] = l[s];      // cached: the softmax reads them next
     }
   };
-  // Full 64-key tiles (every key below T; only a group's last tile can be
-  // partial) take one 32-bit offset per stream and tile: the four 16-key
-  // subtiles sit at fixed byte distances, which the loads and stores carry
-  // as immediate offsets.  No clamping, and the stores need no key guard.
-  auto load_full = [&](KeyWords<CB16, SB16, W> (&kw)[4], float (&nu)[4], float (&ga)[4], int t0) {
+  // Full tiles (every key below T; only a group's last tile can be partial)
+  // take one 32-bit offset per stream and tile: the 16-key subtiles sit at
+  // fixed byte distances, which the loads and stores carry as immediate
+  // offsets.  No clamping, and the stores need no key guard.  The register
+  // set holds the key words of each subtile and the tile's norms one per lane
+  // (lane l: key t0 + l mod KT), handed to the lanes that need them by a
+  // cross-lane read when the tile is scored; the next lane group's first code
+  // word (3-bit codes) also comes from its lane, not from memory.  Fewer
+  // load instructions per key is what the memory pipeline rewards here: the
+  // kernel's time follows the number of loads, not their bytes.
+  struct FullBuf {
+    KeyWords<CB16, SB16, W> kw[SPB];
+    float nu, ga;
+  };
+  auto load_full = [&](FullBuf &b, int t0) {
     const uint32_t t = (uint32_t)(t0 + col);
     const uint8_t *cp = cbase + (t * (CB16 * 16) + (uint32_t)grp * (CB16 * 4));
     const uint8_t *sp = sbase + (t * (SB16 * 16) + (uint32_t)grp * (SB16 * 4));
-    const uint8_t *np = reinterpret_cast<const uint8_t *>(nbase) + t * 4u;
-    const uint8_t *rp = reinterpret_cast<const uint8_t *>(rbase) + t * 4u;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      load_key_words_at<true>(kw[s], cp + s * (16 * CB16 * 16), sp + s * (16 * SB16 * 16), grp);
-      nu[s] = *reinterpret_cast<const float *>(np + 64 * s);
-      ga[s] = *reinterpret_cast<const float *>(rp + 64 * s);
+    for (int s = 0; s < SPB; ++s) {
+      KeyWords<CB16, SB16, W> &k = b.kw[s];
+      const uint8_t *c = cp + s * (16 * CB16 * 16), *g = sp + s * (16 * SB16 * 16);
+#pragma unroll
+      for (int i = 0; i < CB16; ++i) k.cw[i] = key_word<true>(reinterpret_cast<const uint32_t *>(c + 4 * i));
+#pragma unroll
+      for (int i = 0; i < SB16; ++i) k.sw[i] = key_word<true>(reinterpret_cast<const uint32_t *>(g + 4 * i));
     }
+    const uint32_t tl = (uint32_t)(t0 + (lane % KT));
+    b.nu = load_f32(nbase, tl);
+    b.ga = load_f32(rbase, tl);
   };
-  auto score_full = [&](const KeyWords<CB16, SB16, W> (&kw)[4], const float (&nu)[4], const float (&ga)[4],
-                        int t0) {
-    float l[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      l[s] = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc, pm);
-      __asm__ volatile("" : "+v"(l[s]));
-    }
+  auto score_full = [&](FullBuf &b, int t0) {
     float *lp = lrow + (uint32_t)(t0 + col);
-    if (head_ok) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) lp[16 * s] = l[s];   // cached: the softmax reads them next
+    for (int s = 0; s < SPB; ++s) {
+      if constexpr (W == 3) {   // first code word of the next lane group (lane + 16), none for the last
+        const uint32_t nxt = (uint32_t)__shfl((int)b.kw[s].cw[0], (lane + 16) & 63);
+        b.kw[s].cw[CB16] = grp < 3 ? nxt : 0u;
+      }
+      const float nu = __shfl(b.nu, 16 * s + col), ga = __shfl(b.ga, 16 * s + col);
+      const float l = tile_logit<CB16, SB16, W>(A, b.kw[s], nu, ga, a.alpha, hc, pm);
+      if (head_ok) lp[16 * s] = l;      // cached: the softmax reads them next
     }
   };
   if (ntile <= 0) return;
   // first key of this wave's i-th tile
-  auto key0 = [&](int i) { return (tile0 + i) * 64; };
-  const int nfull = key0(ntile - 1) + 64 > T ? ntile - 1 : ntile;
+  auto key0 = [&](int i) { return (tile0 + i) * KT; };
+  const int nfull = key0(ntile - 1) + KT > T ? ntile - 1 : ntile;
   // two named register sets: the next tile's words load while this one is scored
-  KeyWords<CB16, SB16, W> k0[4], k1[4];
-  float n0[4], g0[4], n1[4], g1[4];
-  if (nfull > 0) load_full(k0, n0, g0, key0(0));
+  KeyWords<CB16, SB16, W> k0[SPB];
+  float n0[SPB], g0[SPB];
+  FullBuf f0, f1;
+  if (nfull > 0) load_full(f0, key0(0));
   for (int it = 0; it < nfull; it += 2) {
-    if (it + 1 < nfull) load_full(k1, n1, g1, key0(it + 1));
-    score_full(k0, n0, g0, key0(it));
+    if (it + 1 < nfull) load_full(f1, key0(it + 1));
+    score_full(f0, key0(it));
     if (it + 1 >= nfull) break;
-    if (it + 2 < nfull) load_full(k0, n0, g0, key0(it + 2));
-    score_full(k1, n1, g1, key0(it + 1));
+    if (it + 2 < nfull) load_full(f0, key0(it + 2));
+    score_full(f1, key0(it + 1));
   }
   if (nfull < ntile) {          // the group's last tile, keys clamped and stores guarded
     load_tile(k0, n0, g0, key0(nfull));
@@ -248,11 +268,12 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   sa.cb = ctx->code_bytes;
   sa.sb = ctx->sign_bytes;
   sa.alpha = ctx->alpha;
-  // key tiles of 64 per wave iteration; aim for ~TQ_SCORES_WAVES waves overall
-  const int64_t tiles = (T + 63) / 64;
+  // key tiles of 16 * spb per wave iteration; aim for ~TQ_SCORES_WAVES waves overall
+  const int64_t kt = 16 * scores_spb(cb16, sb16, w);
+  const int64_t tiles = (T + kt - 1) / kt;
   int64_t tpw = (tiles * groups + TQ_SCORES_WAVES - 1) / TQ_SCORES_WAVES;
   if (tpw < 1) tpw = 1;
-  if (tpw > 64) tpw = 64;
+  if (tpw > 256) tpw = 256;
   const int64_t chunks = (tiles + 4 * tpw - 1) / (4 * tpw);
   sa.tiles_per_wave = (int)tpw;
   return dispatch(sa, dim3((unsigned)chunks, (unsigned)groups), cb16, sb16, w, stream, ev_start, ev_stop);
