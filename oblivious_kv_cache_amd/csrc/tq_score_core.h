@@ -131,18 +131,28 @@ __device__ __forceinline__ ParityMasks<CB16, W> parity_masks(int grp) {
   return pm;
 }
 
-// Logit of head (lane / 16) of this query group for key (lane % 16) of the tile:
-//   nu * (P + alpha * gamma * Q), P and Q recombined from four int32 digit rows.
-template <int CB16, int SB16, int W>
-__device__ __forceinline__ float tile_logit(const i32x4 *A, const KeyWords<CB16, SB16, W> &k, float nu,
-                                            float gamma, float alpha, const HeadConsts &hc,
-                                            const ParityMasks<CB16, W> &pm) {
+// Logits of head (lane / 16) of NQ query groups (A[g], hc[g]) for key
+// (lane % 16) of the tile:  nu * (P + alpha * gamma * Q), P and Q recombined
+// from four int32 digit rows.  Each bit-plane operand is built once and used
+// by the NQ groups' MFMAs.
+template <int CB16, int SB16, int W, int NQ>
+__device__ __forceinline__ void tile_logits(const i32x4 (*A)[ScoreShape<CB16, SB16, W>::NM],
+                                            const KeyWords<CB16, SB16, W> &k, float nu, float gamma,
+                                            float alpha, const HeadConsts *hc,
+                                            const ParityMasks<CB16, W> &pm, float *out) {
   using Sh = ScoreShape<CB16, SB16, W>;
-  i32x4 accP = {0, 0, 0, 0}, accQ = {0, 0, 0, 0};
+  i32x4 accP[NQ], accQ[NQ];
+#pragma unroll
+  for (int g = 0; g < NQ; ++g) accP[g] = accQ[g] = i32x4{0, 0, 0, 0};
+  auto mf = [&](i32x4 (&acc)[NQ], int mu, uint32_t word, int half) {
+    const i32x4 b = planes(word, half);
+#pragma unroll
+    for (int g = 0; g < NQ; ++g) acc[g] = mfma8(A[g][mu], b, acc[g]);
+  };
 #pragma unroll
   for (int p = 0; p < CB16; ++p) {
-    accP = mfma8(A[2 * p], planes(k.cw[p], 0), accP);
-    accP = mfma8(A[2 * p + 1], planes(k.cw[p], 1), accP);
+    mf(accP, 2 * p, k.cw[p], 0);
+    mf(accP, 2 * p + 1, k.cw[p], 1);
   }
   if constexpr (W == 3) {
     // bit q of par = parity of record bits q, q+1, q+2
@@ -155,24 +165,41 @@ __device__ __forceinline__ float tile_logit(const i32x4 *A, const KeyWords<CB16,
     }
 #pragma unroll
     for (int f = 0; f < Sh::NPW; ++f) {
-      accP = mfma8(A[Sh::NMC + 2 * f], planes(pw[f], 0), accP);
-      accP = mfma8(A[Sh::NMC + 2 * f + 1], planes(pw[f], 1), accP);
+      mf(accP, Sh::NMC + 2 * f, pw[f], 0);
+      mf(accP, Sh::NMC + 2 * f + 1, pw[f], 1);
     }
   }
 #pragma unroll
   for (int p = 0; p < SB16; ++p) {
-    accQ = mfma8(A[Sh::NMC + Sh::NMP + 2 * p], planes(k.sw[p], 0), accQ);
-    accQ = mfma8(A[Sh::NMC + Sh::NMP + 2 * p + 1], planes(k.sw[p], 1), accQ);
+    mf(accQ, Sh::NMC + Sh::NMP + 2 * p, k.sw[p], 0);
+    mf(accQ, Sh::NMC + Sh::NMP + 2 * p + 1, k.sw[p], 1);
   }
   // digits recombined in pairs in int32 (d0*128 + d1 and d2*128 + d3; every
   // |digit sum| < 2^22 for records of up to 256 coordinates, so the pairs
-  // stays below 2^30), then in fp32; invSP and invSQ carry the 2^-7 of the
+  // stay below 2^30), then in fp32; invSP and invSQ carry the 2^-7 of the
   // leading pair (HeadConsts::load)
-  const float P = fmaf(fmaf((float)(accP[2] * 128 + accP[3]), 0x1.0p-14f, (float)(accP[0] * 128 + accP[1])),
-                       hc.invSP, -hc.KP);
-  const float Q = fmaf(fmaf((float)(accQ[2] * 128 + accQ[3]), 0x1.0p-14f, (float)(accQ[0] * 128 + accQ[1])),
-                       hc.invSQ, -hc.KQ);
-  return nu * fmaf(alpha * gamma, Q, P);
+  const float ag = alpha * gamma;
+#pragma unroll
+  for (int g = 0; g < NQ; ++g) {
+    const float P = fmaf(fmaf((float)(accP[g][2] * 128 + accP[g][3]), 0x1.0p-14f,
+                              (float)(accP[g][0] * 128 + accP[g][1])),
+                         hc[g].invSP, -hc[g].KP);
+    const float Q = fmaf(fmaf((float)(accQ[g][2] * 128 + accQ[g][3]), 0x1.0p-14f,
+                              (float)(accQ[g][0] * 128 + accQ[g][1])),
+                         hc[g].invSQ, -hc[g].KQ);
+    out[g] = nu * fmaf(ag, Q, P);
+  }
+}
+
+// One query group's logit (tile_logits with NQ = 1).
+template <int CB16, int SB16, int W>
+__device__ __forceinline__ float tile_logit(const i32x4 *A, const KeyWords<CB16, SB16, W> &k, float nu,
+                                            float gamma, float alpha, const HeadConsts &hc,
+                                            const ParityMasks<CB16, W> &pm) {
+  float l;
+  tile_logits<CB16, SB16, W, 1>(reinterpret_cast<const i32x4 (*)[ScoreShape<CB16, SB16, W>::NM]>(A), k, nu,
+                                gamma, alpha, &hc, pm, &l);
+  return l;
 }
 
 // Wave-wide sum / max with DPP row permutes (quad swaps, half-row and row

@@ -4,8 +4,8 @@
 // The estimator of tq_scores.hip is evaluated for every (query, database
 // vector) pair, but logits are never written out (at 10^4 x 10^6 they would
 // be 40 GB).  Two kernels:
-//   scan:  a wave owns 4 queries (one int8-MFMA row group) and one database
-//          chunk; every lane keeps a sorted top-KP list (score desc, id asc)
+//   scan:  a wave owns 4 or 8 queries (one or two int8-MFMA row groups) and
+//          one database chunk; every lane keeps a sorted top-KP list (score desc, id asc)
 //          of the database vectors it scored, in registers; a new score enters
 //          only if it beats the lane's current KP-th best.  The waves of a
 //          block scan the same chunk in step, so database lines are reused
@@ -24,6 +24,12 @@ constexpr int MAX_CHUNKS = 8;
 // waves (query groups) per scan block: 8 with 16-entry lane lists; 4 with
 // 64-entry lists, which need the full register file of one wave per SIMD
 __host__ __device__ constexpr int scan_waves(int kp) { return kp <= 16 ? 8 : 4; }
+// Query groups per scan wave: with 16-entry lists and records of up to 12
+// MFMAs per tile, a wave scores two groups against each database tile and
+// builds every bit-plane operand once for both (the planes are most of the
+// VALU work per MFMA; 2^20-key scans at d=200, b=2: 26.2 -> 22.3 ms).  Larger
+// records would not fit two groups' fragments and lists in registers.
+__host__ __device__ constexpr int scan_qg(int kp, int nm) { return kp <= 16 && nm <= 12 ? 2 : 1; }
 
 struct TopkGeom {
   int64_t groups;      // query groups of 4
@@ -34,11 +40,12 @@ struct TopkGeom {
   int64_t ncand;       // candidates per query
 };
 
-TopkGeom topk_geom(int64_t nq, int64_t n, int k) {
+TopkGeom topk_geom(int64_t nq, int64_t n, int k, int nm) {
   TopkGeom g{};
   g.groups = (nq + 3) / 4;
   g.kp = k <= 16 ? 16 : 64;
-  g.qblocks = (g.groups + scan_waves(g.kp) - 1) / scan_waves(g.kp);
+  const int per_block = scan_waves(g.kp) * scan_qg(g.kp, nm);
+  g.qblocks = (g.groups + per_block - 1) / per_block;
   int64_t want = (2048 + g.qblocks - 1) / g.qblocks;
   const int64_t tiles = (n + 63) / 64;
   if (want > tiles) want = tiles;
@@ -85,76 +92,123 @@ __device__ __forceinline__ float row_kth_largest(float v, int k, int lane) {
 template <int CB16, int SB16, int W, int KP>
 __global__ void __launch_bounds__(64 * scan_waves(KP)) topk_scan_kernel(ScanArgs a) {
   constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
+  constexpr int QG = scan_qg(KP, NM);
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-  const int64_t qg = (int64_t)blockIdx.y * scan_waves(KP) + (threadIdx.x >> 6);
-  if (qg >= a.groups) return;                      // no block-wide sync below
+  const int64_t qg0 = ((int64_t)blockIdx.y * scan_waves(KP) + (threadIdx.x >> 6)) * QG;
+  if (qg0 >= a.groups) return;                     // no block-wide sync below
   const int c = blockIdx.x;
-  const uint8_t *prep = a.prep + qg * prep_stride(NM);
-  i32x4 A[NM];
+  // the wave's query groups qg0 .. qg0 + QG - 1 (past the last group, the
+  // last one again: scored, never stored)
+  i32x4 A[QG][NM];
+  HeadConsts hc[QG];
 #pragma unroll
-  for (int mu = 0; mu < NM; ++mu) A[mu] = reinterpret_cast<const i32x4 *>(prep)[mu * 64 + lane];
-  const float *cst = reinterpret_cast<const float *>(prep + NM * 1024) + grp * 4;
-  const HeadConsts hc = HeadConsts::load(cst);
+  for (int g = 0; g < QG; ++g) {
+    const uint8_t *prep = a.prep + min(qg0 + g, a.groups - 1) * prep_stride(NM);
+#pragma unroll
+    for (int mu = 0; mu < NM; ++mu) A[g][mu] = reinterpret_cast<const i32x4 *>(prep)[mu * 64 + lane];
+    hc[g] = HeadConsts::load(reinterpret_cast<const float *>(prep + NM * 1024) + grp * 4);
+  }
   const ParityMasks<CB16, W> pm = parity_masks<CB16, W>(grp);
 
-  float ls[KP];
-  int li[KP];
+  float ls[QG][KP];
+  int li[QG][KP];
 #pragma unroll
-  for (int j = 0; j < KP; ++j) {
-    ls[j] = -FLT_MAX;
-    li[j] = INT_MAX;
-  }
+  for (int g = 0; g < QG; ++g)
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      ls[g][j] = -FLT_MAX;
+      li[g][j] = INT_MAX;
+    }
   // n < 2^31 and record offsets < 2^32 are checked on the host
   const int begin = (int)((int64_t)c * a.chunk);
   const int end = (int)min((int64_t)begin + a.chunk, a.n);
   // Pruning bound for k <= 16: the k-th largest of the 16 lanes' current
   // best scores of a query.  k distinct vectors score at least that much, so
   // a score below it cannot be in the query's top k; refreshed every 4 tiles.
-  float thr = -FLT_MAX;
-  int tile = 0;
-  for (int t0 = begin; t0 < end; t0 += 64, ++tile) {
+  float thr[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) thr[g] = -FLT_MAX;
+  // Register set of one 64-key tile: the key words of its four 16-key
+  // subtiles, and its norms one per lane (lane l: key t0 + l), handed to the
+  // lanes that need them by a cross-lane read; the next lane group's first
+  // code word (3-bit codes) also comes from its lane.
+  struct Buf {
     KeyWords<CB16, SB16, W> kw[4];
-    float nu[4], ga[4];
+    float nu, ga;
+  };
+  auto load = [&](Buf &buf, int t0) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const uint32_t t = (uint32_t)min(t0 + 16 * s + col, end - 1);
-      load_key_words<false>(kw[s], a.codes, a.signs, t, grp);
-      nu[s] = load_f32(a.norms, t);
-      ga[s] = load_f32(a.rnorms, t);
+      const uint8_t *cp = a.codes + (t * (CB16 * 16) + (uint32_t)grp * (CB16 * 4));
+      const uint8_t *sp = a.signs + (t * (SB16 * 16) + (uint32_t)grp * (SB16 * 4));
+#pragma unroll
+      for (int i = 0; i < CB16; ++i) buf.kw[s].cw[i] = key_word<false>(reinterpret_cast<const uint32_t *>(cp + 4 * i));
+#pragma unroll
+      for (int i = 0; i < SB16; ++i) buf.kw[s].sw[i] = key_word<false>(reinterpret_cast<const uint32_t *>(sp + 4 * i));
     }
+    const uint32_t tl = (uint32_t)min(t0 + lane, end - 1);
+    buf.nu = load_f32(a.norms, tl);
+    buf.ga = load_f32(a.rnorms, tl);
+  };
+  auto score = [&](Buf &buf, int t0, int tile) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      if constexpr (W == 3) {   // first code word of the next lane group (lane + 16), none for the last
+        const uint32_t nxt = (uint32_t)__shfl((int)buf.kw[s].cw[0], (lane + 16) & 63);
+        buf.kw[s].cw[CB16] = grp < 3 ? nxt : 0u;
+      }
+      const float nu = __shfl(buf.nu, 16 * s + col), ga = __shfl(buf.ga, 16 * s + col);
       const int t = t0 + 16 * s + col;
-      const float l = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc, pm);
-      const bool want = t < end && l > ls[KP - 1] && !(l < thr);
-      // few scores pass once the lists have filled: a wave-uniform branch
-      // skips the insertion network
-      if (__builtin_amdgcn_ballot_w64(want) == 0) continue;
-      if (want) {
-        // ids seen by a lane increase, so a tie with the last entry never enters
-        float cs = l;
-        int ci = t;
+      float lq[QG];
+      tile_logits<CB16, SB16, W, QG>(A, buf.kw[s], nu, ga, a.alpha, hc, pm, lq);
 #pragma unroll
-        for (int j = 0; j < KP; ++j) {
-          const bool b = better(cs, ci, ls[j], li[j]);
-          const float ts = ls[j];
-          const int ti = li[j];
-          ls[j] = b ? cs : ts;
-          li[j] = b ? ci : ti;
-          cs = b ? ts : cs;
-          ci = b ? ti : ci;
+      for (int g = 0; g < QG; ++g) {
+        const float l = lq[g];
+        const bool want = t < end && l > ls[g][KP - 1] && !(l < thr[g]);
+        // few scores pass once the lists have filled: a wave-uniform branch
+        // skips the insertion network
+        if (__builtin_amdgcn_ballot_w64(want) == 0) continue;
+        if (want) {
+          // ids seen by a lane increase, so a tie with the last entry never enters
+          float cs = l;
+          int ci = t;
+#pragma unroll
+          for (int j = 0; j < KP; ++j) {
+            const bool b = better(cs, ci, ls[g][j], li[g][j]);
+            const float ts = ls[g][j];
+            const int ti = li[g][j];
+            ls[g][j] = b ? cs : ts;
+            li[g][j] = b ? ci : ti;
+            cs = b ? ts : cs;
+            ci = b ? ti : ci;
+          }
         }
       }
     }
-    if (a.k <= 16 && (tile & 3) == 3) thr = row_kth_largest(ls[0], a.k, lane);
-  }
-  const int64_t q = qg * 4 + grp;
-  if (q < a.nq) {
-    const int64_t base = ((q * a.nchunk + c) * 16 + col) * KP;
+    if (a.k <= 16 && (tile & 3) == 3) {
 #pragma unroll
-    for (int j = 0; j < KP; ++j) {
-      a.cand_s[base + j] = ls[j];
-      a.cand_i[base + j] = li[j];
+      for (int g = 0; g < QG; ++g) thr[g] = row_kth_largest(ls[g][0], a.k, lane);
+    }
+  };
+  // (a second register set, to overlap the next tile's loads, measured no
+  // faster: the scan is bound by VALU and MFMA issue, not by load latency)
+  int tile = 0;
+  for (int t0 = begin; t0 < end; t0 += 64, ++tile) {
+    Buf buf;
+    load(buf, t0);
+    score(buf, t0, tile);
+  }
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    const int64_t q = (qg0 + g) * 4 + grp;
+    if (qg0 + g < a.groups && q < a.nq) {
+      const int64_t base = ((q * a.nchunk + c) * 16 + col) * KP;
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        a.cand_s[base + j] = ls[g][j];
+        a.cand_i[base + j] = li[g][j];
+      }
     }
   }
 }
@@ -220,17 +274,17 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
 size_t topk_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int k) {
-  const TopkGeom g = topk_geom(nq, n, k);
   const int nm = mfma_count(ctx->code_bytes / 16, ctx->sign_bytes / 16, ctx->hp.w);
+  const TopkGeom g = topk_geom(nq, n, k, nm);
   return (size_t)(align256(g.groups * prep_stride(nm)) + 2 * align256(nq * g.ncand * 4));
 }
 
 int launch_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const uint8_t *codes,
                 const uint8_t *signs, const float *norms, const float *rnorms, int k,
                 int64_t *ids, float *scores, void *ws, hipStream_t stream) {
-  const TopkGeom g = topk_geom(nq, n, k);
   const int cb16 = ctx->code_bytes / 16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
   const int nm = mfma_count(cb16, sb16, w);
+  const TopkGeom g = topk_geom(nq, n, k, nm);
   uint8_t *base = reinterpret_cast<uint8_t *>(ws);
   uint8_t *prep = base;
   float *cand_s = reinterpret_cast<float *>(base + align256(g.groups * prep_stride(nm)));

@@ -65,6 +65,9 @@ def _run(tq, ctx, Q, rec, k):
 @pytest.mark.parametrize("d,bits,nq,n,k", [
     (200, 2, 7, 1000, 10), (200, 4, 9, 1500, 10), (128, 3, 4, 777, 1), (128, 3, 5, 3000, 16),
     (200, 2, 3, 2000, 17), (64, 3, 6, 500, 64), (128, 2, 2, 64, 64), (200, 4, 1, 65, 10),
+    # two query groups per scan wave, with an odd group count (the last wave's
+    # second group is a repeat that must not be stored) and a ragged last group
+    (128, 3, 9, 700, 10), (200, 2, 13, 900, 5),
 ])
 def test_topk_matches_oracle(tq, d, bits, nq, n, k):
     p, ctx, rec, Q = _setup(tq, d, bits, nq, n, seed=d + n)
