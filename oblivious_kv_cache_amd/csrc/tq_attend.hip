@@ -101,9 +101,11 @@ attend_partial_kernel(AttArgs a) {
   }
   for (int i = tid; i < (NT / 64) * 4 * 128; i += NT) (&accs[0][0][0])[i] = 0.f;
 
-  // registers of the chunk in flight
+  // registers of the chunk in flight: key words per 16-key subtile; key norms
+  // one per lane (lane l: key l of each of the wave's two 64-key tiles),
+  // handed to the lanes that need them by cross-lane reads
   KW kw[2][4];
-  float knu[2][4], kga[2][4];
+  float knu[2], kga[2];
   u32x4 vr[VR];
   float vn[CH / NT];
   auto issue = [&](int c) {
@@ -111,14 +113,21 @@ attend_partial_kernel(AttArgs a) {
     // group's records span less than 4 GB) keep the address math short
     const int tbeg = c * CH, tlast = (int)T - 1;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const uint32_t t = (uint32_t)min(tbeg + (wv + 4 * tt) * 64 + 16 * s + col, tlast);
-        load_key_words<true>(kw[tt][s], kcb, ksb, t, grp);
-        knu[tt][s] = load_f32(knb, t);
-        kga[tt][s] = load_f32(krb, t);
+        const uint8_t *cp = kcb + (t * (CB16 * 16) + (uint32_t)grp * (CB16 * 4));
+        const uint8_t *sp = ksb + (t * (SB16 * 16) + (uint32_t)grp * (SB16 * 4));
+#pragma unroll
+        for (int i = 0; i < CB16; ++i) kw[tt][s].cw[i] = key_word<true>(reinterpret_cast<const uint32_t *>(cp + 4 * i));
+#pragma unroll
+        for (int i = 0; i < SB16; ++i) kw[tt][s].sw[i] = key_word<true>(reinterpret_cast<const uint32_t *>(sp + 4 * i));
       }
+      const uint32_t tl = (uint32_t)min(tbeg + (wv + 4 * tt) * 64 + lane, tlast);
+      knu[tt] = load_f32(knb, tl);
+      kga[tt] = load_f32(krb, tl);
+    }
     // value codes: clamped 16-byte units (units past the cache end repeat the
     // last real one and are never read back)
     const uint32_t lim = (uint32_t)(min(CH, (int)T - tbeg) * (VR / 2)) - 1u;
@@ -160,7 +169,12 @@ attend_partial_kernel(AttArgs a) {
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        lg[tt][s] = tile_logit<CB16, SB16, W>(A, kw[tt][s], knu[tt][s], kga[tt][s], a.alpha, hc, pm);
+        if constexpr (W == 3) {   // first code word of the next lane group (lane + 16), none for the last
+          const uint32_t nxt = (uint32_t)__shfl((int)kw[tt][s].cw[0], (lane + 16) & 63);
+          kw[tt][s].cw[CB16] = grp < 3 ? nxt : 0u;
+        }
+        const float nu = __shfl(knu[tt], 16 * s + col), ga = __shfl(kga[tt], 16 * s + col);
+        lg[tt][s] = tile_logit<CB16, SB16, W>(A, kw[tt][s], nu, ga, a.alpha, hc, pm);
         __asm__ volatile("" : "+v"(lg[tt][s]));
       }
 #pragma unroll
