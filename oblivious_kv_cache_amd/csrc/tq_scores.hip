@@ -53,6 +53,7 @@ struct ScoreArgs {
   const uint8_t *ws;
   int64_t T, ldk;
   int qpg, hg, tiles_per_wave, cb, sb;
+  int wide;                 // T and the logits base allow one 4*spb-byte store per lane
   float alpha;
 };
 
@@ -151,8 +152,12 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
     b.nu = load_f32(nbase, tl);
     b.ga = load_f32(rbase, tl);
   };
+  // logits of the tile, [head][key] per wave: each lane then stores SPB
+  // consecutive keys of its head with one wide store (one store instruction
+  // per tile instead of one per 16-key subtile)
+  __shared__ __align__(16) float lt[4][4][KT];
+  typedef float fvec __attribute__((ext_vector_type(SPB)));
   auto score_full = [&](FullBuf &b, int t0) {
-    float *lp = lrow + (uint32_t)(t0 + col);
 #pragma unroll
     for (int s = 0; s < SPB; ++s) {
       if constexpr (W == 3) {   // first code word of the next lane group (lane + 16), none for the last
@@ -161,7 +166,19 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
       }
       const float nu = __shfl(b.nu, 16 * s + col), ga = __shfl(b.ga, 16 * s + col);
       const float l = tile_logit<CB16, SB16, W>(A, b.kw[s], nu, ga, a.alpha, hc, pm);
-      if (head_ok) lp[16 * s] = l;      // cached: the softmax reads them next
+      lt[wv][grp][16 * s + col] = l;
+    }
+    // one wave writes and reads its own rows: in-order LDS access, no barrier;
+    // the stores are cached (the softmax reads the logits next)
+    const fvec v = *reinterpret_cast<const fvec *>(&lt[wv][grp][SPB * col]);
+    float *dst = lrow + (uint32_t)(t0 + SPB * col);
+    if (head_ok) {
+      if (a.wide) {             // rows and the logits base allow SPB-float stores
+        *reinterpret_cast<fvec *>(dst) = v;
+      } else {
+#pragma unroll
+        for (int i = 0; i < SPB; ++i) dst[i] = v[i];
+      }
     }
   };
   if (ntile <= 0) return;
@@ -268,8 +285,10 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   sa.cb = ctx->code_bytes;
   sa.sb = ctx->sign_bytes;
   sa.alpha = ctx->alpha;
+  const int spb = scores_spb(cb16, sb16, w);
+  sa.wide = T % spb == 0 && reinterpret_cast<uintptr_t>(logits) % (4 * spb) == 0;
   // key tiles of 16 * spb per wave iteration; aim for ~TQ_SCORES_WAVES waves overall
-  const int64_t kt = 16 * scores_spb(cb16, sb16, w);
+  const int64_t kt = 16 * spb;
   const int64_t tiles = (T + kt - 1) / kt;
   int64_t tpw = (tiles * groups + TQ_SCORES_WAVES - 1) / TQ_SCORES_WAVES;
   if (tpw < 1) tpw = 1;

@@ -173,6 +173,12 @@ def test_timed_scores_match_and_time_the_kernel(tq):
         assert torch.equal(got, ref)
         ms = ev[0].elapsed_time(ev[1])
         assert 0.0 < ms < 100.0
+    # logits at a base that is 4-byte but not 16-byte aligned: per-float stores
+    flat = torch.empty(G * qpg * T + 1, dtype=torch.float32, device="cuda")
+    shifted = flat[1:].view(G, qpg, T)
+    tq.tq_scores_prepared(ctx, ws, G, qpg, dev, T=T, ldk=T, logits=shifted)
+    torch.cuda.synchronize()
+    assert torch.equal(shifted, ref)
     empty = torch.empty((G, qpg, 0), dtype=torch.float32, device="cuda")
     tq.tq_scores_prepared(ctx, ws, G, qpg, dev, T=0, ldk=T, logits=empty, events=ev)
     torch.cuda.synchronize()
