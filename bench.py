@@ -318,7 +318,7 @@ def main():
                          "the known-size reference for the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this build runs "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library runs "
               "on a single GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 

@@ -59,7 +59,7 @@ extern "C" {
 /* status codes */
 #define TQ_OK        0
 #define TQ_EINVAL   (-1)   /* bad dimension, bit width, size, pointer, alignment or mode */
-#define TQ_ENOTSUP  (-2)   /* valid request this build does not implement */
+#define TQ_ENOTSUP  (-2)   /* valid request the library does not implement */
 #define TQ_ENOMEM   (-3)   /* host or device allocation failed (init only) */
 #define TQ_EHIP     (-4)   /* a HIP runtime call or kernel launch failed */
 
@@ -76,7 +76,7 @@ extern "C" {
 #define TQ_OP_ATTEND  2
 #define TQ_OP_TOPK    3
 
-/* limits of this build */
+/* limits of the library */
 #define TQ_MAX_D       256   /* d in [8, 256], d % 8 == 0 */
 #define TQ_MAX_TOPK    64
 

@@ -371,7 +371,7 @@ int check_decode(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t
   return TQ_OK;
 }
 
-// Append + query prep: one fused launch where this build has one, else the
+// Append + query prep: one fused launch where the library has one, else the
 // quantize and prep launches in turn (same results).
 int decode_prep(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G, int qpg,
                 const void *new_k, const void *new_v, int dtype, int64_t ldx, int64_t pos, int64_t ldk,

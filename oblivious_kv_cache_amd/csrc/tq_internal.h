@@ -85,7 +85,7 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
                   void *ws, hipStream_t stream, bool prepped = false);
 // Append one token per group (keys in kc, values in vc if not null) at record
 // g * ldk + pos and prepare the queries into ws, in one launch.  TQ_ENOTSUP
-// when this build has no fused kernel for the shapes (the caller then runs
+// when the library has no fused kernel for the shapes (the caller then runs
 // launch_quantize and the prep apart).
 int launch_decode_prep(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G, int qpg,
                        const void *new_k, const void *new_v, int dtype, int64_t ldx, int64_t pos,
