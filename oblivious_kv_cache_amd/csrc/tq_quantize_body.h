@@ -28,6 +28,18 @@ namespace tq {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Bits collected by shifting each value's sign bit in at the bottom (one
+// alignbit per value, first value ends highest) -> bit i = NOT sign of value
+// i, i < n: reversed, moved down and inverted.
+template <int N>
+__device__ __forceinline__ uint32_t nonneg_bits(uint32_t shifted) {
+  const uint32_t r = __builtin_bitreverse32(shifted) >> (32 - N);
+  return r ^ (N == 32 ? 0xffffffffu : ((1u << N) - 1u));
+}
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct QArgs {
@@ -194,7 +206,7 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
 
     // Per vector: 1/nu, and state for the codes and the residual.
     uint32_t cw[NTL][CW];
-    bf16x8 rh[NTL][NK], rl[NTL][NK];
+    u32x4 rh[NTL][NK], rl[NTL][NK];      // residual hi / lo, bf16 pairs
     float nu[NTL], inv[NTL], rs[NTL];
 #pragma unroll
     for (int t = 0; t < NTL; ++t) {
@@ -225,45 +237,75 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
       }
 #pragma unroll
       for (int t = 0; t < NTL; ++t) {
+        float rr[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int li = 4 * u + jj;                 // local coordinate index
           const float y = acc[t][jj] * inv[t];
-          const float ay = fabsf(y);
+          const uint32_t yb = __float_as_uint(y), ab = yb & 0x7fffffffu;
+          // codebook search on |y| against the positive thresholds
           uint32_t mm = 0;
           float cm = a.cpos[0];
 #pragma unroll
           for (int j = 0; j < HALF - 1; ++j) {
-            const bool gt = ay > a.tpos[j];
+            const bool gt = __uint_as_float(ab) > a.tpos[j];
             mm += gt ? 1u : 0u;
             cm = gt ? a.cpos[j + 1] : cm;
           }
-          // sign from the sign bit, with no lane masks: idx = HALF + mm for
-          // y >= +0, its mirror HALF - 1 - mm (= (HALF + mm) ^ (2 HALF - 1)) for
-          // y <= -0; r = y - copysign(c, y).  (y == +0 exactly lies on the
-          // middle threshold, inside the decision band.)
-          const uint32_t yb = __float_as_uint(y);
-          const uint32_t neg = (uint32_t)((int32_t)yb >> 31);
-          uint32_t idx = ((uint32_t)HALF + mm) ^ (neg & (uint32_t)(2 * HALF - 1));
-          float r = y - __uint_as_float((__float_as_uint(cm) & 0x7fffffffu) | (yb & 0x80000000u));
-          if constexpr (!FULL) {
-            if (li >= nval) {               // padding coordinates
-              idx = 0u;
-              r = 0.f;
+          const uint32_t cmb = __float_as_uint(cm);
+          // r = y - copysign(c, y); the sign of y picks the half of the
+          // codebook: idx = HALF + mm for y >= +0, its mirror HALF - 1 - mm
+          // (= (HALF + mm) ^ (2 HALF - 1)) for y <= -0.  (y == +0 exactly lies
+          // on the middle threshold, inside the decision band.)
+          float r = y - __uint_as_float(cmb | (yb & 0x80000000u));
+          if constexpr (W == 1) {
+            // idx = NOT sign bit: collected with one alignbit, fixed per word below
+            cw[t][li >> 5] = __builtin_amdgcn_alignbit(cw[t][li >> 5], yb, 31);
+          } else {
+            const uint32_t neg = (uint32_t)((int32_t)yb >> 31);
+            uint32_t idx = ((uint32_t)HALF + mm) ^ (neg & (uint32_t)(2 * HALF - 1));
+            if constexpr (!FULL) {
+              if (li >= nval) idx = 0u;      // padding coordinates
             }
+            const int bit = li * W;
+            cw[t][bit >> 5] |= idx << (bit & 31);
+            if (((bit & 31) + W) > 32) cw[t][(bit >> 5) + 1] |= idx >> (32 - (bit & 31));
           }
-          const int bit = li * W;
-          cw[t][bit >> 5] |= idx << (bit & 31);
-          if (((bit & 31) + W) > 32) cw[t][(bit >> 5) + 1] |= idx >> (32 - (bit & 31));
+          if constexpr (!FULL) {
+            if (li >= nval) r = 0.f;
+          }
           rs[t] += r * r;
-          const __bf16 h = (__bf16)r;
-          rh[t][li >> 3][li & 7] = h;
-          rl[t][li >> 3][li & 7] = (__bf16)(r - (float)h);
+          rr[jj] = r;
+        }
+        // hi / lo bf16 split of the residual, two coordinates per conversion
+#pragma unroll
+        for (int jj = 0; jj < 4; jj += 2) {
+          const int li = 4 * u + jj;
+          const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{rr[jj], rr[jj + 1]}, bf16x2));
+          const float h0 = __uint_as_float(hw << 16), h1 = __uint_as_float(hw & 0xffff0000u);
+          const uint32_t lw = __builtin_bit_cast(uint32_t,
+                                                 __builtin_convertvector(f32x2{rr[jj] - h0, rr[jj + 1] - h1}, bf16x2));
+          rh[t][li >> 3][(li & 7) >> 1] = hw;
+          rl[t][li >> 3][(li & 7) >> 1] = lw;
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // keep fragment loads from piling up
     }
 
+    if constexpr (W == 1) {
+#pragma unroll
+      for (int t = 0; t < NTL; ++t)
+#pragma unroll
+        for (int i = 0; i < CW; ++i) {
+          constexpr int NB = PER < 32 ? PER : 32;   // PER is 32 or less, or a multiple of 32
+          uint32_t v = nonneg_bits<NB>(cw[t][i]);
+          if constexpr (!FULL) {                    // padding coordinates get code 0
+            const int nv = nval - 32 * i;
+            v &= nv >= 32 ? 0xffffffffu : (nv > 0 ? (1u << nv) - 1u : 0u);
+          }
+          cw[t][i] = v;
+        }
+    }
     // a zero vector stores zero codes and gamma = 0 (its signs are cleared below)
 #pragma unroll
     for (int t = 0; t < NTL; ++t) {
@@ -309,24 +351,36 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
           const bf16x8 sh = frag(2, u * NK + k), sl = frag(3, u * NK + k);
 #pragma unroll
           for (int t = 0; t < NTL; ++t) {
-            z[t] = mfma(sh, rh[t][k], z[t]);
-            z[t] = mfma(sh, rl[t][k], z[t]);
-            z[t] = mfma(sl, rh[t][k], z[t]);
+            const bf16x8 bh = __builtin_bit_cast(bf16x8, rh[t][k]), bl = __builtin_bit_cast(bf16x8, rl[t][k]);
+            z[t] = mfma(sh, bh, z[t]);
+            z[t] = mfma(sh, bl, z[t]);
+            z[t] = mfma(sl, bh, z[t]);
           }
         }
 #pragma unroll
         for (int t = 0; t < NTL; ++t) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
+            // bit = [z >= 0] = NOT sign of z (z is never -0: the sums start at
+            // +0); collected with one alignbit, fixed per word below
             const int li = 4 * u + jj;
-            const bool b = (FULL || li < mval) && z[t][jj] >= 0.f;
-            sw[t][li >> 5] |= (b ? 1u : 0u) << (li & 31);
+            sw[t][li >> 5] = __builtin_amdgcn_alignbit(sw[t][li >> 5], __float_as_uint(z[t][jj]), 31);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int t = 0; t < NTL; ++t) {
+#pragma unroll
+        for (int i = 0; i < SW; ++i) {
+          constexpr int NB = PER < 32 ? PER : 32;
+          uint32_t v = nonneg_bits<NB>(sw[t][i]);
+          if constexpr (!FULL) {                    // rows past m are 0
+            const int mv = mval - 32 * i;
+            v &= mv >= 32 ? 0xffffffffu : (mv > 0 ? (1u << mv) - 1u : 0u);
+          }
+          sw[t][i] = v;
+        }
         if (!(nu[t] > 0.f)) {
 #pragma unroll
           for (int i = 0; i < SW; ++i) sw[t][i] = 0u;
