@@ -262,7 +262,7 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
             // idx = NOT sign bit: collected with one alignbit, fixed per word below
             cw[t][li >> 5] = __builtin_amdgcn_alignbit(cw[t][li >> 5], yb, 31);
           } else {
-            const uint32_t neg = (uint32_t)((int32_t)yb >> 31);
+            const uint32_t neg = (uint32_t)((int32_t)yb >> 31);     // all ones for y <= -0
             uint32_t idx = ((uint32_t)HALF + mm) ^ (neg & (uint32_t)(2 * HALF - 1));
             if constexpr (!FULL) {
               if (li >= nval) idx = 0u;      // padding coordinates
@@ -270,6 +270,11 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
             const int bit = li * W;
             cw[t][bit >> 5] |= idx << (bit & 31);
             if (((bit & 31) + W) > 32) cw[t][(bit >> 5) + 1] |= idx >> (32 - (bit & 31));
+            // packed here and now (an empty asm reads the word): otherwise the
+            // search results of many coordinates stay live, as lane masks in
+            // scalar registers, until the compiler's chosen packing spot, and
+            // spill
+            __asm__ volatile("" : "+v"(cw[t][bit >> 5]));
           }
           if constexpr (!FULL) {
             if (li >= nval) r = 0.f;
