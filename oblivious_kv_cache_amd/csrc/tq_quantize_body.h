@@ -135,10 +135,13 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
   // opaque in every tile iteration so that address arithmetic for all
   // fragments is not hoisted out of the loop into registers.
   int lofs = lane;
+  // second base for matrices 2 and 3 (the S' fragments): every fragment then
+  // lies within the 64 KB immediate-offset reach of one of the two bases
+  int lofs2 = lane + 2 * FR * 64;
   const Frag *const PiH = a.PiA_hi, *const PiL = a.PiA_lo, *const S2H = a.S2A_hi, *const S2L = a.S2A_lo;
   auto frag = [&](int which, int f) -> bf16x8 {
     if constexpr (USE_LDS) {
-      return as_bf(lds[(which * FR + f) * 64 + lofs]);
+      return as_bf(which < 2 ? lds[(which * FR + f) * 64 + lofs] : lds[((which - 2) * FR + f) * 64 + lofs2]);
     } else {
       const Frag *src = which == 0 ? PiH : which == 1 ? PiL : which == 2 ? S2H : S2L;
       return as_bf(src[f * 64 + lofs]);
@@ -156,7 +159,8 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
     // opaque so the per-coordinate compares are not hoisted out of the loop.
     int nval = a.d - grp * PER, mval = a.m - grp * PER, xval = a.d - grp * 8;
     lofs = lane;
-    __asm__ volatile("" : "+v"(nval), "+v"(mval), "+v"(xval), "+v"(lofs));
+    lofs2 = lane + 2 * FR * 64;
+    __asm__ volatile("" : "+v"(nval), "+v"(mval), "+v"(xval), "+v"(lofs), "+v"(lofs2));
     const int64_t vbase = tile * (16 * NTL);
     bf16x8 bx[NTL][NK];
     bf16x8 bxl[NTL][BF16IN ? 1 : NK];
