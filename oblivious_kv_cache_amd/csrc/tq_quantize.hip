@@ -4,21 +4,30 @@
 namespace tq {
 namespace {
 
+// Threads of a block.  The blocks that keep the fragments in LDS (128 KB at
+// d=128) are one per CU; with 3-bit codes and bf16 input a wave fits in 168
+// VGPRs, so 12 waves (3 per SIMD) share the fragments, else 8.
+__host__ __device__ constexpr int quant_threads(bool use_lds, int w, bool bf16in) {
+  return use_lds ? (w == 3 && bf16in ? 768 : 512) : 256;
+}
+
 template <int DPAD, bool BF16IN, bool USE_LDS, int NTL, int W, bool FULL>
-__global__ void __launch_bounds__(USE_LDS ? 512 : 256) quantize_kernel(QArgs a) {
+__global__ void __launch_bounds__(quant_threads(USE_LDS, W, BF16IN)) quantize_kernel(QArgs a) {
   constexpr int FR = (DPAD / 16) * (DPAD / 32);
   __shared__ Frag lds[USE_LDS ? 4 * FR * 64 : 1];
-  quantize_body<DPAD, BF16IN, USE_LDS, NTL, W, FULL>(a, lds, blockIdx.x, gridDim.x);
+  quantize_body<DPAD, BF16IN, USE_LDS, NTL, W, FULL, quant_threads(USE_LDS, W, BF16IN)>(a, lds, blockIdx.x,
+                                                                                     gridDim.x);
 }
 
 template <int DPAD, bool BF16IN, bool USE_LDS, int NTL, bool FULL>
 int launch_w(const QArgs &a, int w, int blocks, hipStream_t s) {
-  const int threads = USE_LDS ? 512 : 256;
   switch (w) {
-    case 1: quantize_kernel<DPAD, BF16IN, USE_LDS, NTL, 1, FULL><<<blocks, threads, 0, s>>>(a); break;
-    case 2: quantize_kernel<DPAD, BF16IN, USE_LDS, NTL, 2, FULL><<<blocks, threads, 0, s>>>(a); break;
-    case 3: quantize_kernel<DPAD, BF16IN, USE_LDS, NTL, 3, FULL><<<blocks, threads, 0, s>>>(a); break;
-    case 4: quantize_kernel<DPAD, BF16IN, USE_LDS, NTL, 4, FULL><<<blocks, threads, 0, s>>>(a); break;
+#define TQ_W(W_)                                                                                      \
+    case W_:                                                                                          \
+      quantize_kernel<DPAD, BF16IN, USE_LDS, NTL, W_, FULL><<<blocks, quant_threads(USE_LDS, W_, BF16IN), 0, s>>>(a); \
+      break;
+    TQ_W(1) TQ_W(2) TQ_W(3) TQ_W(4)
+#undef TQ_W
     default: return TQ_ENOTSUP;
   }
   return hip_status();
@@ -26,7 +35,7 @@ int launch_w(const QArgs &a, int w, int blocks, hipStream_t s) {
 
 template <int DPAD, bool USE_LDS, int NTL>
 int launch_d(const QArgs &a, int w, bool bf16, int cus, hipStream_t s) {
-  const int64_t per_block_tiles = USE_LDS ? 8 : 4;   // one tile per wave per pass
+  const int64_t per_block_tiles = quant_threads(USE_LDS, w, bf16) / 64;   // one tile per wave per pass
   const int64_t want = (a.ntiles + per_block_tiles - 1) / per_block_tiles;
   const int64_t cap = USE_LDS ? (int64_t)cus : (int64_t)cus * 4;
   const int blocks = (int)(want < cap ? (want > 0 ? want : 1) : cap);

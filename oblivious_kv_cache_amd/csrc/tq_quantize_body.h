@@ -79,9 +79,10 @@ __device__ __forceinline__ void zero_bytes(uint8_t *dst, int nb) {
 }
 
 // The kernel body, callable from a kernel that also runs other jobs: block
-// `block` of `nblocks` blocks working on this quantize job; `lds` holds the
-// operand fragments (USE_LDS: 4 FR x 64 Frags, filled here).
-template <int DPAD, bool BF16IN, bool USE_LDS, int NTL, int W, bool FULL>
+// `block` of `nblocks` blocks of NTHR threads working on this quantize job;
+// `lds` holds the operand fragments (USE_LDS: 4 FR x 64 Frags, filled here by
+// the block's NTHR threads).
+template <int DPAD, bool BF16IN, bool USE_LDS, int NTL, int W, bool FULL, int NTHR>
 __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int block, int nblocks) {
   constexpr int NT = DPAD / 16;       // 16-row output tiles (coordinates)
   constexpr int NK = DPAD / 32;       // 32-deep k blocks
@@ -107,7 +108,7 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
     // store: one memory round trip.  Clamped indices keep the loads free of
     // branches; a duplicate store of the last element rewrites the same value.
     constexpr int NF = FR * 64;
-    constexpr int ITER = (NF + 511) / 512;        // USE_LDS launches 512 threads
+    constexpr int ITER = (NF + NTHR - 1) / NTHR;
     // Without the sketch (MSE-only contexts) slots 2 and 3 receive a second
     // copy of Pi's fragments, unused: the loads stay unconditional.
     const Frag *const s0 = a.PiA_hi, *const s1 = a.PiA_lo;
@@ -115,7 +116,7 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
     Frag t0[ITER], t1[ITER], t2[ITER], t3[ITER];
 #pragma unroll
     for (int b = 0; b < ITER; ++b) {
-      const int i = min(b * 512 + (int)threadIdx.x, NF - 1);
+      const int i = min(b * NTHR + (int)threadIdx.x, NF - 1);
       t0[b] = s0[i];
       t1[b] = s1[i];
       t2[b] = s2[i];
@@ -123,7 +124,7 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
     }
 #pragma unroll
     for (int b = 0; b < ITER; ++b) {
-      const int i = min(b * 512 + (int)threadIdx.x, NF - 1);
+      const int i = min(b * NTHR + (int)threadIdx.x, NF - 1);
       lds[i] = t0[b];
       lds[NF + i] = t1[b];
       lds[2 * NF + i] = t2[b];
@@ -148,8 +149,8 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
     }
   };
 
-  const int64_t wave = ((int64_t)block * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)nblocks * blockDim.x) >> 6;
+  const int64_t wave = ((int64_t)block * NTHR + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)nblocks * NTHR) >> 6;
 
   for (int64_t tile = wave; tile < a.ntiles; tile += nwaves) {
     // The operand fragments are loop-invariant; a memory clobber per tile keeps
