@@ -57,15 +57,14 @@ struct ScoreArgs {
   float alpha;
 };
 
-// 16-key subtiles per wave iteration, i.e. per register set of the double
-// buffer (2 for 3-bit codes, whose larger records and A fragments would
-// otherwise hold the kernel to 3 waves per SIMD)
-__host__ __device__ constexpr int scores_spb(int cb16, int sb16, int w) { return w == 3 ? 2 : 4; }
+// 16-key subtiles per wave iteration: a 64-key tile fills one LDS slot of the
+// double buffer
+constexpr int kScoresSPB = 4;
 
 template <int CB16, int SB16, int W>
 __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
-  constexpr int SPB = scores_spb(CB16, SB16, W), KT = 16 * SPB;
+  constexpr int SPB = kScoresSPB, KT = 16 * SPB;
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   const int wv = threadIdx.x >> 6;
   const int64_t gidx = blockIdx.y;       // key group * hg + head group
@@ -121,59 +120,68 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
       if (head_ok && t < T) lrow[t] = l[s];      // cached: the softmax reads them next
     }
   };
-  // Full tiles (every key below T; only a group's last tile can be partial)
-  // take one 32-bit offset per stream and tile: the 16-key subtiles sit at
-  // fixed byte distances, which the loads and stores carry as immediate
-  // offsets.  No clamping, and the stores need no key guard.  The register
-  // set holds the key words of each subtile and the tile's norms one per lane
-  // (lane l: key t0 + l mod KT), handed to the lanes that need them by a
-  // cross-lane read when the tile is scored; the next lane group's first code
-  // word (3-bit codes) also comes from its lane, not from memory.  Fewer
-  // load instructions per key is what the memory pipeline rewards here: the
-  // kernel's time follows the number of loads, not their bytes.
-  struct FullBuf {
-    KeyWords<CB16, SB16, W> kw[SPB];
-    float nu, ga;
-  };
-  auto load_full = [&](FullBuf &b, int t0) {
-    const uint32_t t = (uint32_t)(t0 + col);
-    const uint8_t *cp = cbase + (t * (CB16 * 16) + (uint32_t)grp * (CB16 * 4));
-    const uint8_t *sp = sbase + (t * (SB16 * 16) + (uint32_t)grp * (SB16 * 4));
-#pragma unroll
-    for (int s = 0; s < SPB; ++s) {
-      KeyWords<CB16, SB16, W> &k = b.kw[s];
-      const uint8_t *c = cp + s * (16 * CB16 * 16), *g = sp + s * (16 * SB16 * 16);
-#pragma unroll
-      for (int i = 0; i < CB16; ++i) k.cw[i] = key_word<true>(reinterpret_cast<const uint32_t *>(c + 4 * i));
-#pragma unroll
-      for (int i = 0; i < SB16; ++i) k.sw[i] = key_word<true>(reinterpret_cast<const uint32_t *>(g + 4 * i));
-    }
-    const uint32_t tl = (uint32_t)(t0 + (lane % KT));
-    b.nu = load_f32(nbase, tl);
-    b.ga = load_f32(rbase, tl);
-  };
   // logits of the tile, [head][key] per wave: each lane then stores SPB
   // consecutive keys of its head with one wide store (one store instruction
   // per tile instead of one per 16-key subtile)
   __shared__ __align__(16) float lt[4][4][KT];
   typedef float fvec __attribute__((ext_vector_type(SPB)));
-  auto score_full = [&](FullBuf &b, int t0) {
+  // Full tiles (every key below T; only a group's last tile can be partial)
+  // are moved to LDS by the memory system itself: a tile's code bytes and
+  // its sign bytes are each one contiguous run, so a wave copies them into
+  // its own LDS slot with a few global_load_lds_dwordx4 instructions (16 B
+  // per lane, 1 KB each, non-temporal: read once) and then reads the MFMA
+  // operand words from LDS; the norms come one per lane into registers and
+  // are handed out by cross-lane reads.  Counters showed the kernel's time
+  // following the number of load instructions per key rather than bytes
+  // (the texture address unit was the busiest part), and this form needs
+  // the fewest: CB16 + SB16 + 2 per 64 keys, against 16 or more with one
+  // load of each record word per lane.
+  constexpr int CBY = CB16 * 16, SBY = SB16 * 16, TB = KT * (CBY + SBY);
+  __shared__ __align__(16) uint8_t kbA[4][TB];
+  __shared__ __align__(16) uint8_t kbB[4][TB];
+  auto dma = [&](uint8_t *dst, const uint8_t *src, int kb) {
+#pragma unroll
+    for (int i = 0; i < kb; ++i)
+      __builtin_amdgcn_global_load_lds(src + i * 1024 + lane * 16,
+                                       (__attribute__((address_space(3))) void *)(dst + i * 1024), 16, 0,
+                                       2 /* nt */);
+  };
+  auto load_dma = [&](uint8_t (&kb)[4][TB], float &nu, float &ga, int t0) {
+    dma(kb[wv], cbase + (uint32_t)t0 * CBY, KT * CBY / 1024);
+    dma(kb[wv] + KT * CBY, sbase + (uint32_t)t0 * SBY, KT * SBY / 1024);
+    const uint32_t tl = (uint32_t)(t0 + (lane % KT));
+    nu = load_f32(nbase, tl);
+    ga = load_f32(rbase, tl);
+  };
+  // the tile's words from LDS into registers (all subtiles), so that the
+  // slot can be refilled at once
+  auto read_dma = [&](uint8_t (&kb)[4][TB], KeyWords<CB16, SB16, W> (&kw)[SPB]) {
 #pragma unroll
     for (int s = 0; s < SPB; ++s) {
-      if constexpr (W == 3) {   // first code word of the next lane group (lane + 16), none for the last
-        const uint32_t nxt = (uint32_t)__shfl((int)b.kw[s].cw[0], (lane + 16) & 63);
-        b.kw[s].cw[CB16] = grp < 3 ? nxt : 0u;
+      const int k = 16 * s + col;
+      const uint8_t *rc = kb[wv] + k * CBY + grp * (CB16 * 4);
+      const uint8_t *rsg = kb[wv] + KT * CBY + k * SBY + grp * (SB16 * 4);
+#pragma unroll
+      for (int i = 0; i < CB16; ++i) kw[s].cw[i] = *reinterpret_cast<const uint32_t *>(rc + 4 * i);
+      if constexpr (W == 3) {   // first code word of the next lane group (in LDS after ours), none for the last
+        const uint32_t nxt = *reinterpret_cast<const uint32_t *>(rc + 4 * CB16);
+        kw[s].cw[CB16] = grp < 3 ? nxt : 0u;
       }
-      const float nu = __shfl(b.nu, 16 * s + col), ga = __shfl(b.ga, 16 * s + col);
-      const float l = tile_logit<CB16, SB16, W>(A, b.kw[s], nu, ga, a.alpha, hc, pm);
+#pragma unroll
+      for (int i = 0; i < SB16; ++i) kw[s].sw[i] = *reinterpret_cast<const uint32_t *>(rsg + 4 * i);
+    }
+  };
+  auto score_dma = [&](const KeyWords<CB16, SB16, W> (&kw)[SPB], float nub, float gab, int t0) {
+#pragma unroll
+    for (int s = 0; s < SPB; ++s) {
+      const float nu = __shfl(nub, 16 * s + col), ga = __shfl(gab, 16 * s + col);
+      const float l = tile_logit<CB16, SB16, W>(A, kw[s], nu, ga, a.alpha, hc, pm);
       lt[wv][grp][16 * s + col] = l;
     }
-    // one wave writes and reads its own rows: in-order LDS access, no barrier;
-    // the stores are cached (the softmax reads the logits next)
     const fvec v = *reinterpret_cast<const fvec *>(&lt[wv][grp][SPB * col]);
     float *dst = lrow + (uint32_t)(t0 + SPB * col);
     if (head_ok) {
-      if (a.wide) {             // rows and the logits base allow SPB-float stores
+      if (a.wide) {
         *reinterpret_cast<fvec *>(dst) = v;
       } else {
 #pragma unroll
@@ -185,19 +193,29 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   // first key of this wave's i-th tile
   auto key0 = [&](int i) { return (tile0 + i) * KT; };
   const int nfull = key0(ntile - 1) + KT > T ? ntile - 1 : ntile;
-  // two named register sets: the next tile's words load while this one is scored
-  KeyWords<CB16, SB16, W> k0[SPB];
-  float n0[SPB], g0[SPB];
-  FullBuf f0, f1;
-  if (nfull > 0) load_full(f0, key0(0));
+  // two slots, two tiles in flight: a slot is read into registers, refilled
+  // with the tile after next, and only then is its tile scored
+  float nA, gA, nB, gB;
+  KeyWords<CB16, SB16, W> kw[SPB];
+  if (nfull > 0) load_dma(kbA, nA, gA, key0(0));
+  if (nfull > 1) load_dma(kbB, nB, gB, key0(1));
   for (int it = 0; it < nfull; it += 2) {
-    if (it + 1 < nfull) load_full(f1, key0(it + 1));
-    score_full(f0, key0(it));
+    read_dma(kbA, kw);
+    float nu = nA, ga = gA;
+    __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): the slot's reads are done
+    if (it + 2 < nfull) load_dma(kbA, nA, gA, key0(it + 2));
+    score_dma(kw, nu, ga, key0(it));
     if (it + 1 >= nfull) break;
-    if (it + 2 < nfull) load_full(f0, key0(it + 2));
-    score_full(f1, key0(it + 1));
+    read_dma(kbB, kw);
+    nu = nB;
+    ga = gB;
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    if (it + 3 < nfull) load_dma(kbB, nB, gB, key0(it + 3));
+    score_dma(kw, nu, ga, key0(it + 1));
   }
   if (nfull < ntile) {          // the group's last tile, keys clamped and stores guarded
+    KeyWords<CB16, SB16, W> k0[SPB];
+    float n0[SPB], g0[SPB];
     load_tile(k0, n0, g0, key0(nfull));
     score_tile(k0, n0, g0, key0(nfull));
   }
@@ -285,7 +303,7 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   sa.cb = ctx->code_bytes;
   sa.sb = ctx->sign_bytes;
   sa.alpha = ctx->alpha;
-  const int spb = scores_spb(cb16, sb16, w);
+  const int spb = kScoresSPB;
   sa.wide = T % spb == 0 && reinterpret_cast<uintptr_t>(logits) % (4 * spb) == 0;
   // key tiles of 16 * spb per wave iteration; aim for ~TQ_SCORES_WAVES waves overall
   const int64_t kt = 16 * spb;
