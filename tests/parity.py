@@ -85,3 +85,25 @@ def check_quantized(p, gpu, ref, X=None, allow_frac=MAX_FRAC):
         if p.mode == "prod":
             assert not gpu["signs"][zero].any() and (gpu["rnorms"][zero] == 0).all()
     return stats
+
+
+# Top-k lists.  Several correct lists exist when scores tie within the
+# tolerance: at every rank r the oracle score of the GPU's id must be within
+# tolerance of the oracle's r-th score, and the GPU and oracle id sets may
+# differ only in ids whose oracle scores are within tolerance of the k-th.
+TK_ATOL, TK_RTOL = 1e-4, 1e-3
+
+
+def check_topk(gpu_ids, gpu_scores, oracle_scores, k):
+    """oracle_scores: [nq, n] float64 oracle estimator scores."""
+    ref_ids, ref_vals = O.topk(oracle_scores, k)
+    for qi in range(len(gpu_ids)):
+        g = gpu_ids[qi]
+        assert len(set(g.tolist())) == k, "duplicate ids"
+        sc = oracle_scores[qi]
+        tol = TK_ATOL + TK_RTOL * np.abs(ref_vals[qi])
+        assert (np.abs(sc[g] - ref_vals[qi]) <= tol).all(), (qi, sc[g] - ref_vals[qi])
+        assert (np.abs(gpu_scores[qi] - sc[g]) <= TK_ATOL + TK_RTOL * np.abs(sc[g])).all()
+        kth = ref_vals[qi][-1]
+        for i in set(g.tolist()) ^ set(ref_ids[qi].tolist()):
+            assert abs(sc[i] - kth) <= TK_ATOL + TK_RTOL * abs(kth), (qi, i, sc[i], kth)

@@ -1,10 +1,15 @@
-"""GPU parity at full workload size, on sampled outputs.
+"""GPU parity at full workload size, on sampled outputs, in the launch
+configurations bench.py times.
 
-Decode at 32K context: 32 x 8 KV heads x 32768 tokens x d=128 bf16 keys (4
-outlier channels per head), 32 query heads, b = 3 and 4, in the launch
-configuration bench.py times.  The whole cache is quantized and scored on the
-GPU; the oracle then quantizes a sample of the same key rows itself and
-recomputes the logits of those keys one by one.
+* Decode at 32K context: 32 x 8 KV heads x 32768 tokens x d=128 bf16 keys (4
+  outlier channels per head), 32 query heads, b = 2, 3, 4.  The whole cache is
+  quantized and scored on the GPU; the oracle then quantizes a sample of the
+  same key rows itself and recomputes the logits of those keys one by one.
+* Streaming quantize: 2^20 x 128 bf16 power-law vectors, b = 2, 3, 4; the
+  oracle quantizes a sample of the rows.
+* Vector search: 10^6 unit-norm d=200 power-law vectors, 10^4 queries, top-10,
+  b = 2 and 4; the oracle checks a sample of the database records, and a
+  sample of the queries' lists over 10^6 generator-made records.
 """
 
 import math
@@ -14,7 +19,7 @@ import pytest
 
 import oracle as O
 from oblivious_kv_cache_amd import workloads as wl
-from parity import assert_close, check_quantized
+from parity import assert_close, check_quantized, check_topk
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +34,7 @@ def tq():
     return binding
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_decode_32k_sampled(tq, bits):
     dev = torch.device("cuda")
     B, Hkv, T, d, Hq = 32, 8, 32768, 128, 32
@@ -70,3 +75,57 @@ def test_decode_32k_sampled(tq, bits):
     P = probs.cpu().numpy()
     assert np.allclose(P.sum(axis=-1), 1.0, atol=1e-3) and (P >= 0).all()
     assert np.array_equal(P.argmax(axis=-1), L.argmax(axis=-1))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_2p20_sampled(tq, bits):
+    dev = torch.device("cuda")
+    n, d = 1 << 20, 128
+    print(f"full-size quantize 2^20 x 128 bf16 power-law b={bits}", flush=True)
+    ctx = tq.Context(d, bits, 0)
+    X = wl.power_law_torch(n, d, seed=3, device=dev)
+    out = ctx.empty_records(n, dev)
+    tq.tq_quantize(ctx, X, out=out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(30 + bits)
+    rows = np.sort(np.concatenate([[0, 1, n - 1], rng.choice(np.arange(2, n - 1), 4000, replace=False)]))
+    idx_t = torch.as_tensor(rows, device=dev)
+    Xs = X.index_select(0, idx_t).float().cpu().numpy()
+    g = {k: v.index_select(0, idx_t).cpu().numpy() for k, v in out.items()}
+    p = O.make_params(d, bits, 0)
+    check_quantized(p, g, O.quantize(p, Xs, return_unpacked=True), Xs)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_topk_1e6_sampled(tq, bits):
+    # the database quantize at full size: the oracle quantizes a sample of the
+    # rows itself; the search at full size runs on generator-made records of
+    # the same layout, so the oracle scores exactly what the GPU searched
+    dev = torch.device("cuda")
+    nq, n, d, k = 10000, 1000000, 200, 10
+    print(f"full-size top-{k}: {nq} queries x {n} d={d} vectors, b={bits}", flush=True)
+    DB = wl.power_law_torch(n, d, seed=5, device=dev, dtype=torch.float32, unit=True)
+    Q = wl.power_law_torch(nq, d, seed=6, device=dev, dtype=torch.float32, unit=True)
+    ctx = tq.Context(d, bits, 0)
+    rec = tq.tq_quantize(ctx, DB)
+    torch.cuda.synchronize()
+    p = O.make_params(d, bits, 0)
+    rng = np.random.default_rng(40 + bits)
+    rows = np.sort(np.concatenate([[0, n - 1], rng.choice(np.arange(1, n - 1), 3000, replace=False)]))
+    idx_t = torch.as_tensor(rows, device=dev)
+    Xs = DB.index_select(0, idx_t).cpu().numpy()
+    g = {key: v.index_select(0, idx_t).cpu().numpy() for key, v in rec.items()}
+    check_quantized(p, g, O.quantize(p, Xs, return_unpacked=True), Xs)
+    del rec, DB
+
+    c, sg, nu, ga = wl.random_records(n, ctx.code_bytes, ctx.sign_bytes, 50 + bits)
+    rr = {"codes": c, "signs": sg, "norms": nu, "rnorms": ga}
+    drec = {key: torch.from_numpy(v).to(dev) for key, v in rr.items()}
+    ws = ctx.workspace(tq.TQ_OP_TOPK, nq, n, k, device=dev)
+    ids, sc = tq.tq_topk(ctx, Q, drec, k, ws=ws)
+    torch.cuda.synchronize()
+    qs = np.sort(np.concatenate([[0, nq - 1], rng.choice(np.arange(1, nq - 1), 10, replace=False)]))
+    Qs = Q.cpu().numpy()[qs].astype(np.float64)
+    want = np.concatenate([O.scores(p, Qs, c[s:s + 50000], sg[s:s + 50000], nu[s:s + 50000], ga[s:s + 50000])
+                           for s in range(0, n, 50000)], axis=1)
+    check_topk(ids.cpu().numpy()[qs], sc.cpu().numpy()[qs], want, k)

@@ -11,11 +11,11 @@ import pytest
 
 import oracle as O
 from oblivious_kv_cache_amd import workloads as wl
+from parity import check_topk
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-ATOL, RTOL = 1e-4, 1e-3
 
 
 @pytest.fixture(scope="module")
@@ -24,21 +24,6 @@ def tq():
         pytest.skip("no GPU")
     from oblivious_kv_cache_amd import binding
     return binding
-
-
-def check_topk(gpu_ids, gpu_scores, oracle_scores, k):
-    """oracle_scores: [nq, n] float64 oracle estimator scores."""
-    ref_ids, ref_vals = O.topk(oracle_scores, k)
-    for qi in range(len(gpu_ids)):
-        g = gpu_ids[qi]
-        assert len(set(g.tolist())) == k, "duplicate ids"
-        sc = oracle_scores[qi]
-        tol = ATOL + RTOL * np.abs(ref_vals[qi])
-        assert (np.abs(sc[g] - ref_vals[qi]) <= tol).all(), (qi, sc[g] - ref_vals[qi])
-        assert (np.abs(gpu_scores[qi] - sc[g]) <= ATOL + RTOL * np.abs(sc[g])).all()
-        kth = ref_vals[qi][-1]
-        for i in set(g.tolist()) ^ set(ref_ids[qi].tolist()):
-            assert abs(sc[i] - kth) <= ATOL + RTOL * abs(kth), (qi, i, sc[i], kth)
 
 
 def _setup(tq, d, bits, nq, n, seed, records="oracle"):
