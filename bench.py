@@ -268,6 +268,24 @@ def bench_decode_bits(tq, wl, dev, bits, steps=50):
     return r
 
 
+def bench_practical_bandwidth(torch, dev, scores_gbs, extra):
+    """What a plain streaming kernel reaches on this GPU: torch's elementwise
+    1 GiB -> 1 GiB copy (torch.neg), timed like the library's kernels, with
+    the HBM-bound kernels' algorithmic rates as fractions of it."""
+    log("practical bandwidth: 1 GiB -> 1 GiB copy (torch.neg)")
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = _time(torch, lambda: torch.neg(src, out=dst), 10)
+    del src, dst
+    copy_gbs = 2 * (1 << 30) / (copy_ms / 1e3) / 1e9
+    out = {"copy_gbs": copy_gbs, "copy_frac_of_peak": copy_gbs / HBM_PEAK_GBS,
+           "scores_frac_of_copy": scores_gbs / copy_gbs}
+    if "softmax_32k" in extra:
+        out["softmax_frac_of_copy"] = extra["softmax_32k"]["gbs"] / copy_gbs
+    log(f"  copy {copy_gbs:.0f} GB/s; scores kernel = {100 * scores_gbs / copy_gbs:.0f} % of it")
+    return out
+
+
 def bench_topk(tq, wl, dev, nq=10000, n=1000000, d=200, k=10):
     """Vector search: 10^6 unit-norm d=200 power-law database vectors, 10^4
     queries, top-10 by the estimator, recall of the exact fp32 top-1."""
@@ -433,6 +451,7 @@ def main():
         extra["quantize_2p20"] = qz
         extra["attend_128k"] = bench_attend(tq, wl, dev)
         extra["topk_1e6"] = bench_topk(tq, wl, dev)
+        extra["practical_bandwidth"] = bench_practical_bandwidth(torch, dev, achieved, extra)
 
     if args.calib_copy:
         log("calibration copy: torch.neg, 2^30 bytes read + 2^30 bytes written per launch")
