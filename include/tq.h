@@ -79,6 +79,11 @@ extern "C" {
 /* limits of the library */
 #define TQ_MAX_D       256   /* d in [8, 256], d % 8 == 0 */
 #define TQ_MAX_TOPK    64
+#define TQ_MAX_QPG     64    /* query heads per group: attention and decode steps */
+#define TQ_MAX_QPG_SCORES 65536  /* queries per group: tq_scores, tq_prep_queries,
+                                    tq_scores_prepared (many queries against one key
+                                    set, e.g. every position of a prefill); in addition
+                                    G * ceil(qpg / 4) <= 65535, else TQ_ENOTSUP */
 
 typedef struct tq_ctx tq_ctx;
 
@@ -152,7 +157,10 @@ int tq_workspace_size(const tq_ctx *ctx, int op, int64_t a, int64_t b, int64_t c
  *   logits [device] float [G][qpg][T]: raw inner-product estimates (no
  *          1/sqrt(d) scaling);
  *   ws     [device] >= tq_workspace_size(TQ_OP_SCORES, G, qpg) bytes.
- * Requires a prod-mode context; T >= 0, ldk >= T, 1 <= qpg <= 64. */
+ * Requires a prod-mode context; T >= 0, ldk >= T, 1 <= qpg <= TQ_MAX_QPG_SCORES
+ * (TQ_EINVAL), G * ceil(qpg / 4) <= 65535 (TQ_ENOTSUP).  Queries are scored in
+ * blocks of 4 against every key, so a large qpg (all positions of a prefill
+ * against the same keys) is one call. */
 int tq_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,
               const uint8_t *codes, const uint8_t *signs, const float *norms,
               const float *rnorms, float *logits, void *ws, size_t ws_bytes,

@@ -240,11 +240,11 @@ int tq_workspace_size(const tq_ctx *ctx, int op, int64_t a, int64_t b, int64_t c
   if (!ctx || !bytes || a < 0 || b < 0 || c < 0) return TQ_EINVAL;
   switch (op) {
     case TQ_OP_SCORES:
-      if (ctx->hp.mode != TQ_MODE_PROD || b < 1 || b > 64) return TQ_EINVAL;
+      if (ctx->hp.mode != TQ_MODE_PROD || b < 1 || b > TQ_MAX_QPG_SCORES) return TQ_EINVAL;
       *bytes = tq::scores_ws_bytes(ctx, a, (int)b);
       return TQ_OK;
     case TQ_OP_ATTEND:
-      if (ctx->hp.mode != TQ_MODE_PROD || b < 1 || b > 64) return TQ_EINVAL;
+      if (ctx->hp.mode != TQ_MODE_PROD || b < 1 || b > TQ_MAX_QPG) return TQ_EINVAL;
       *bytes = tq::attend_ws_bytes(ctx, a, (int)b, c);
       return TQ_OK;
     case TQ_OP_TOPK:
@@ -261,7 +261,7 @@ int tq_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, 
               const float *rnorms, float *logits, void *ws, size_t ws_bytes,
               hipStream_t stream) {
   if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
-  if (G < 0 || T < 0 || ldk < T || qpg < 1 || qpg > 64) return TQ_EINVAL;
+  if (G < 0 || T < 0 || ldk < T || qpg < 1 || qpg > TQ_MAX_QPG_SCORES) return TQ_EINVAL;
   if (G == 0 || T == 0) return TQ_OK;
   if (!q || !codes || !signs || !norms || !rnorms || !logits || !ws) return TQ_EINVAL;
   if (!aligned(codes, 16) || !aligned(signs, 16) || !aligned(norms, 4) || !aligned(rnorms, 4) ||
@@ -276,7 +276,7 @@ int tq_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, 
 int tq_prep_queries(const tq_ctx *ctx, const float *q, int64_t G, int qpg, void *ws,
                     size_t ws_bytes, hipStream_t stream) {
   if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
-  if (G < 0 || qpg < 1 || qpg > 64) return TQ_EINVAL;
+  if (G < 0 || qpg < 1 || qpg > TQ_MAX_QPG_SCORES) return TQ_EINVAL;
   if (G == 0) return TQ_OK;
   if (!q || !ws || !aligned(q, 4) || !aligned(ws, 16)) return TQ_EINVAL;
   if (ws_bytes < tq::scores_ws_bytes(ctx, G, qpg)) return TQ_EINVAL;
@@ -298,7 +298,7 @@ int tq_scores_prepared_timed(const tq_ctx *ctx, const void *ws, size_t ws_bytes,
                              const float *norms, const float *rnorms, float *logits,
                              hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
-  if (G < 0 || T < 0 || ldk < T || qpg < 1 || qpg > 64) return TQ_EINVAL;
+  if (G < 0 || T < 0 || ldk < T || qpg < 1 || qpg > TQ_MAX_QPG_SCORES) return TQ_EINVAL;
   if (G == 0 || T == 0) return TQ_OK;
   if (!ws || !codes || !signs || !norms || !rnorms || !logits) return TQ_EINVAL;
   if (!aligned(codes, 16) || !aligned(signs, 16) || !aligned(norms, 4) || !aligned(rnorms, 4) ||
@@ -328,7 +328,7 @@ int tq_attend(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t G,
   if (!kctx || !vctx || kctx->hp.mode != TQ_MODE_PROD || vctx->hp.mode != TQ_MODE_MSE)
     return TQ_EINVAL;
   if (kctx->hp.d != vctx->hp.d) return TQ_EINVAL;
-  if (G < 0 || T < 1 || ldk < T || qpg < 1 || qpg > 64) return TQ_EINVAL;
+  if (G < 0 || T < 1 || ldk < T || qpg < 1 || qpg > TQ_MAX_QPG) return TQ_EINVAL;
   if (G == 0) return TQ_OK;
   if (!q || !kcodes || !ksigns || !knorms || !krnorms || !vcodes || !vnorms || !out || !ws)
     return TQ_EINVAL;
@@ -355,7 +355,7 @@ int check_decode(const tq_ctx *kctx, const tq_ctx *vctx, const float *q, int64_t
   if (!kctx || kctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
   if (vctx && (vctx->hp.mode != TQ_MODE_MSE || vctx->hp.d != kctx->hp.d)) return TQ_EINVAL;
   const int d = kctx->hp.d;
-  if (G < 0 || qpg < 1 || qpg > 64 || pos < 0 || ldk < pos + 1) return TQ_EINVAL;
+  if (G < 0 || qpg < 1 || qpg > TQ_MAX_QPG || pos < 0 || ldk < pos + 1) return TQ_EINVAL;
   if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EINVAL;
   if (ldx < d || (dtype == TQ_BF16 ? (ldx % 8) : (ldx % 4))) return TQ_EINVAL;
   if (!q || !new_k || !kcodes || !ksigns || !knorms || !krnorms || !ws) return TQ_EINVAL;

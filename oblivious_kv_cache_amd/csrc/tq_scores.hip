@@ -52,7 +52,7 @@ struct ScoreArgs {
   float *logits;
   const uint8_t *ws;
   int64_t T, ldk;
-  int qpg, hg, tiles_per_wave, cb, sb;
+  int qpg, hg, hq, tiles_per_wave, cb, sb;   // hq: blocks of NQ head groups per key group
   int wide;                 // T and the logits base allow one 4*spb-byte store per lane
   float alpha;
 };
@@ -61,26 +61,37 @@ struct ScoreArgs {
 // double buffer
 constexpr int kScoresSPB = 4;
 
-template <int CB16, int SB16, int W>
+// NQ groups of 4 queries (head groups) per wave: each key tile's bit-plane
+// operands are built once for all of them (many queries per key group, e.g.
+// every position of a prefill, are bound by that VALU work, not by bytes).
+template <int CB16, int SB16, int W, int NQ>
 __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
   constexpr int SPB = kScoresSPB, KT = 16 * SPB;
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   const int wv = threadIdx.x >> 6;
-  const int64_t gidx = blockIdx.y;       // key group * hg + head group
-  const int64_t kg = gidx / a.hg;
-  const int hgi = (int)(gidx - kg * a.hg);
+  const int64_t gy = blockIdx.y;         // key group * hq + block of NQ head groups
+  const int64_t kg = gy / a.hq;
+  const int hb = (int)(gy - kg * a.hq);
 
-  const uint8_t *prep = a.ws + gidx * prep_stride(NM);
-  i32x4 A[NM];
+  // with an odd head-group count the last block's second group repeats the
+  // first (its logits are computed and not stored)
+  i32x4 A[NQ][NM];
+  HeadConsts hc[NQ];
+  bool head_ok[NQ];
+  float *lrow[NQ];
 #pragma unroll
-  for (int mu = 0; mu < NM; ++mu) A[mu] = reinterpret_cast<const i32x4 *>(prep)[mu * 64 + lane];
-  const float *cst = reinterpret_cast<const float *>(prep + NM * 1024) + grp * 4;
-  const HeadConsts hc = HeadConsts::load(cst);
+  for (int g = 0; g < NQ; ++g) {
+    const int hgi = min(hb * NQ + g, a.hg - 1);
+    const uint8_t *prep = a.ws + (kg * a.hg + hgi) * prep_stride(NM);
+#pragma unroll
+    for (int mu = 0; mu < NM; ++mu) A[g][mu] = reinterpret_cast<const i32x4 *>(prep)[mu * 64 + lane];
+    hc[g] = HeadConsts::load(reinterpret_cast<const float *>(prep + NM * 1024) + grp * 4);
+    const int head = hgi * 4 + grp;
+    head_ok[g] = hb * NQ + g < a.hg && head < a.qpg;
+    lrow[g] = a.logits + ((int64_t)kg * a.qpg + (head_ok[g] ? head : 0)) * a.T;
+  }
   const ParityMasks<CB16, W> pm = parity_masks<CB16, W>(grp);
-  const int head = hgi * 4 + grp;
-  const bool head_ok = head < a.qpg;
-  float *lrow = a.logits + ((int64_t)kg * a.qpg + (head_ok ? head : 0)) * a.T;
 
   // Record strides are compile-time (code_bytes = 16 CB16, sign_bytes = 16 SB16)
   // and per-token offsets are 32-bit from per-group base pointers, which keeps
@@ -108,22 +119,25 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
                         int t0) {
     // the four 16-key logits first, then the guarded stores; materialising l
     // keeps the norm loads from being sunk into the stores' branches
-    float l[SPB];
+    float l[SPB][NQ];
 #pragma unroll
     for (int s = 0; s < SPB; ++s) {
-      l[s] = tile_logit<CB16, SB16, W>(A, kw[s], nu[s], ga[s], a.alpha, hc, pm);
-      __asm__ volatile("" : "+v"(l[s]));
+      tile_logits<CB16, SB16, W, NQ>(A, kw[s], nu[s], ga[s], a.alpha, hc, pm, l[s]);
+#pragma unroll
+      for (int g = 0; g < NQ; ++g) __asm__ volatile("" : "+v"(l[s][g]));
     }
 #pragma unroll
-    for (int s = 0; s < SPB; ++s) {
-      const int t = t0 + 16 * s + col;
-      if (head_ok && t < T) lrow[t] = l[s];      // cached: the softmax reads them next
-    }
+    for (int g = 0; g < NQ; ++g)
+#pragma unroll
+      for (int s = 0; s < SPB; ++s) {
+        const int t = t0 + 16 * s + col;
+        if (head_ok[g] && t < T) lrow[g][t] = l[s][g];      // cached: the softmax reads them next
+      }
   };
   // logits of the tile, [head][key] per wave: each lane then stores SPB
   // consecutive keys of its head with one wide store (one store instruction
   // per tile instead of one per 16-key subtile)
-  __shared__ __align__(16) float lt[4][4][KT];
+  __shared__ __align__(16) float lt[4][NQ][4][KT];
   typedef float fvec __attribute__((ext_vector_type(SPB)));
   // Full tiles (every key below T; only a group's last tile can be partial)
   // are moved to LDS by the memory system itself: a tile's code bytes and
@@ -175,17 +189,22 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
 #pragma unroll
     for (int s = 0; s < SPB; ++s) {
       const float nu = __shfl(nub, 16 * s + col), ga = __shfl(gab, 16 * s + col);
-      const float l = tile_logit<CB16, SB16, W>(A, kw[s], nu, ga, a.alpha, hc, pm);
-      lt[wv][grp][16 * s + col] = l;
-    }
-    const fvec v = *reinterpret_cast<const fvec *>(&lt[wv][grp][SPB * col]);
-    float *dst = lrow + (uint32_t)(t0 + SPB * col);
-    if (head_ok) {
-      if (a.wide) {
-        *reinterpret_cast<fvec *>(dst) = v;
-      } else {
+      float l[NQ];
+      tile_logits<CB16, SB16, W, NQ>(A, kw[s], nu, ga, a.alpha, hc, pm, l);
 #pragma unroll
-        for (int i = 0; i < SPB; ++i) dst[i] = v[i];
+      for (int g = 0; g < NQ; ++g) lt[wv][g][grp][16 * s + col] = l[g];
+    }
+#pragma unroll
+    for (int g = 0; g < NQ; ++g) {
+      const fvec v = *reinterpret_cast<const fvec *>(&lt[wv][g][grp][SPB * col]);
+      float *dst = lrow[g] + (uint32_t)(t0 + SPB * col);
+      if (head_ok[g]) {
+        if (a.wide) {
+          *reinterpret_cast<fvec *>(dst) = v;
+        } else {
+#pragma unroll
+          for (int i = 0; i < SPB; ++i) dst[i] = v[i];
+        }
       }
     }
   };
@@ -221,18 +240,33 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   }
 }
 
+// Two head groups per wave where both groups' operand fragments fit in
+// registers beside the rest (up to 12 MFMAs per 16 keys).
+constexpr int kScoresNQ2MaxNM = 12;
+
 // With events, the dispatch itself records them (hipExtLaunchKernel): they
 // bracket exactly this kernel's execution.
-int dispatch(const ScoreArgs &a, dim3 grid, int cb16, int sb16, int w, hipStream_t s, hipEvent_t e0,
-             hipEvent_t e1) {
-#define TQ_CASE(C, S, W_)                                                               \
-  if (cb16 == C && sb16 == S && w == W_) {                                              \
-    if (e0 || e1)                                                                       \
-      hipExtLaunchKernelGGL(scores_kernel<C, S, W_>, grid, dim3(256), 0, s, e0, e1, 0, a); \
-    else                                                                                \
-      scores_kernel<C, S, W_><<<grid, 256, 0, s>>>(a);                                  \
-    return hip_status();                                                                \
+template <int C, int S, int W_, int NQ>
+int launch_one(const ScoreArgs &a, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(scores_kernel<C, S, W_, NQ>, grid, dim3(256), 0, s, e0, e1, 0, a);
+  else
+    scores_kernel<C, S, W_, NQ><<<grid, 256, 0, s>>>(a);
+  return hip_status();
+}
+
+template <int C, int S, int W_>
+int launch_geometry(const ScoreArgs &a, dim3 grid, int nq, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if constexpr (ScoreShape<C, S, W_>::NM <= kScoresNQ2MaxNM) {
+    if (nq == 2) return launch_one<C, S, W_, 2>(a, grid, s, e0, e1);
   }
+  return launch_one<C, S, W_, 1>(a, grid, s, e0, e1);
+}
+
+int dispatch(const ScoreArgs &a, dim3 grid, int cb16, int sb16, int w, int nq, hipStream_t s, hipEvent_t e0,
+             hipEvent_t e1) {
+#define TQ_CASE(C, S, W_) \
+  if (cb16 == C && sb16 == S && w == W_) return launch_geometry<C, S, W_>(a, grid, nq, s, e0, e1);
   TQ_FOR_EACH_GEOMETRY(TQ_CASE)
 #undef TQ_CASE
   return TQ_ENOTSUP;
@@ -288,7 +322,10 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   if (st != TQ_OK) return st;
   const int hg = (qpg + 3) / 4;
   const int cb16 = ctx->code_bytes / 16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
-  const int64_t groups = G * hg;
+  // NQ head groups per wave (2 where it fits); blocks along y: key group x NQ-group block
+  const int nq = hg >= 2 && mfma_count(cb16, sb16, w) <= kScoresNQ2MaxNM ? 2 : 1;
+  const int hq = (hg + nq - 1) / nq;
+  const int64_t groups = G * hq;
   ScoreArgs sa{};
   sa.codes = codes;
   sa.signs = signs;
@@ -300,6 +337,7 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   sa.ldk = ldk;
   sa.qpg = qpg;
   sa.hg = hg;
+  sa.hq = hq;
   sa.cb = ctx->code_bytes;
   sa.sb = ctx->sign_bytes;
   sa.alpha = ctx->alpha;
@@ -309,11 +347,14 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   const int64_t kt = 16 * spb;
   const int64_t tiles = (T + kt - 1) / kt;
   int64_t tpw = (tiles * groups + TQ_SCORES_WAVES - 1) / TQ_SCORES_WAVES;
+  // no more per wave than the four waves of a block share (many head groups
+  // over a short context would otherwise leave waves of a block idle)
+  if (tpw > (tiles + 3) / 4) tpw = (tiles + 3) / 4;
   if (tpw < 1) tpw = 1;
   if (tpw > 256) tpw = 256;
   const int64_t chunks = (tiles + 4 * tpw - 1) / (4 * tpw);
   sa.tiles_per_wave = (int)tpw;
-  return dispatch(sa, dim3((unsigned)chunks, (unsigned)groups), cb16, sb16, w, stream, ev_start, ev_stop);
+  return dispatch(sa, dim3((unsigned)chunks, (unsigned)groups), cb16, sb16, w, nq, stream, ev_start, ev_stop);
 }
 
 int launch_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,

@@ -75,6 +75,41 @@ def test_scores_random_records(tq, d, bits, G, qpg, T, ldk):
     assert_close(got, _oracle_grouped(p, Q, rec, G, T, ldk), what="logits")
 
 
+@pytest.mark.parametrize("d,bits,G,qpg,T,ldk", [
+    # many queries per key group (every position of a prefill against one key
+    # set): two head groups per wave, odd head-group counts (the last wave's
+    # second group repeats the first and is not stored), ragged T
+    (128, 3, 2, 100, 300, 300), (128, 2, 1, 257, 129, 130), (64, 3, 3, 36, 1000, 1000),
+    (128, 4, 1, 12, 64, 64), (128, 3, 1, 1024, 70, 70),
+    # geometry with more than 12 MFMAs per 16 keys: one head group per wave
+    (200, 4, 1, 72, 200, 200),
+])
+def test_scores_many_queries_per_group(tq, d, bits, G, qpg, T, ldk):
+    ctx = tq.Context(d, bits, 0)
+    p = O.make_params(d, bits, 0)
+    codes, signs, norms, rnorms = wl.random_records(G * ldk, ctx.code_bytes, ctx.sign_bytes, seed=d + bits + qpg)
+    rec = {"codes": codes, "signs": signs, "norms": norms, "rnorms": rnorms}
+    Q = wl.gaussian((G, qpg, d), 26)
+    print(f"scores many queries d={d} b={bits} G={G} qpg={qpg} T={T} ldk={ldk}", flush=True)
+    got = _score(tq, ctx, Q, rec, G, T, ldk)
+    assert_close(got, _oracle_grouped(p, Q, rec, G, T, ldk), what="logits")
+
+
+def test_scores_query_count_limits(tq):
+    ctx = tq.Context(128, 3, 0)
+    rec = ctx.empty_records(5)
+    with pytest.raises(tq.TQError) as e:                 # qpg above the library's limit
+        ctx.workspace(tq.TQ_OP_SCORES, 1, 65537)
+    assert e.value.status == tq.TQ_EINVAL
+    # G * ceil(qpg / 4) block rows above the grid's limit: refused before any launch
+    q = torch.zeros((5, 65536, 128), device="cuda")
+    logits = torch.full((5, 65536, 1), 7.0, device="cuda")
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_scores(ctx, q, rec, T=1, ldk=1, logits=logits)
+    assert e.value.status == tq.TQ_ENOTSUP
+    assert (logits == 7.0).all()
+
+
 def test_scores_zero_norm_keys_and_large_queries(tq):
     d, bits = 128, 3
     ctx = tq.Context(d, bits, 0)
