@@ -268,6 +268,46 @@ def bench_decode_bits(tq, wl, dev, bits, steps=50):
     return r
 
 
+def bench_many_queries(tq, wl, dev, G=8, heads=4, npos=2048, T=2048, d=128, bits=3):
+    """Scores with many queries per key group: every position of a 2048-token
+    prefill (4 query heads each) against the group's 2048 keys, 8 KV groups,
+    b=3: 134M logits per call.  Bound by the bit-plane VALU work and the logits
+    writes, not by key bytes (the keys are re-read from cache)."""
+    import torch
+    qpg = heads * npos
+    log(f"many queries per group: {G} groups x {qpg} queries x {T} keys, b={bits}")
+    ctx = tq.Context(d, bits, 0)
+    K, _ = wl.outlier_keys_torch(1, G, T, d, seed=8, device=dev)
+    rec = tq.tq_quantize(ctx, K.view(G * T, d))
+    del K
+    q = wl.gaussian_torch((G, qpg, d), 9, dev)
+    ws = tq.tq_prep_queries(ctx, q)
+    logits = torch.empty((G, qpg, T), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        tq.tq_scores_prepared(ctx, ws, G, qpg, rec, T=T, ldk=T, logits=logits)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for e in ev:
+        e[0].record()
+        e[1].record()
+    for e in ev:
+        tq.tq_scores_prepared(ctx, ws, G, qpg, rec, T=T, ldk=T, logits=logits, events=e)
+    prep_ms = _time(torch, lambda: tq.tq_prep_queries(ctx, q, ws), 5)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    n = G * qpg * T
+    cb16, sb16, w = ctx.code_bytes // 16, ctx.sign_bytes // 16, ctx.w
+    nm = 2 * cb16 + (2 * ((cb16 + 2) // 3) if w == 3 else 0) + 2 * sb16
+    mfma_ops = n / 64 * nm * 2 * 16 * 16 * 64          # NM int8 MFMAs per 16 keys x 4 queries
+    out = {"scores_ms": ms, "prep_ms": prep_ms, "logits_per_s": n / (ms / 1e3),
+           "logits_write_gbs": 4 * n / (ms / 1e3) / 1e9,
+           "int8_mfma_tops": mfma_ops / (ms / 1e3) / 1e12,
+           "int8_mfma_frac": mfma_ops / (ms / 1e3) / 1e12 / INT8_PEAK_TOPS}
+    log(f"  scores {ms * 1e3:.1f} us ({n / (ms / 1e3):.3e} logits/s, int8 MFMA "
+        f"{100 * out['int8_mfma_frac']:.0f} % of peak), query prep {prep_ms * 1e3:.1f} us")
+    del logits, ws, q, rec
+    return out
+
+
 def bench_practical_bandwidth(torch, dev, scores_gbs, extra):
     """What a plain streaming kernel reaches on this GPU: torch's elementwise
     1 GiB -> 1 GiB copy (torch.neg), timed like the library's kernels, with
@@ -451,6 +491,7 @@ def main():
         extra["quantize_2p20"] = qz
         extra["attend_128k"] = bench_attend(tq, wl, dev)
         extra["topk_1e6"] = bench_topk(tq, wl, dev)
+        extra["many_queries_2k"] = bench_many_queries(tq, wl, dev)
         extra["practical_bandwidth"] = bench_practical_bandwidth(torch, dev, achieved, extra)
 
     if args.calib_copy:

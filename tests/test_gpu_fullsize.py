@@ -7,6 +7,9 @@ configurations bench.py times.
   same key rows itself and recomputes the logits of those keys one by one.
 * Streaming quantize: 2^20 x 128 bf16 power-law vectors, b = 2, 3, 4; the
   oracle quantizes a sample of the rows.
+* Many queries per key group: 8 groups x 2048 keys, 4 heads x 2048 positions
+  of queries per group, b=3; the oracle quantizes the keys itself and
+  recomputes a sample of (query, key) logits.
 * Vector search: 10^6 unit-norm d=200 power-law vectors, 10^4 queries, top-10,
   b = 2 and 4; the oracle checks a sample of the database records, and a
   sample of the queries' lists over 10^6 generator-made records.
@@ -129,3 +132,33 @@ def test_topk_1e6_sampled(tq, bits):
     want = np.concatenate([O.scores(p, Qs, c[s:s + 50000], sg[s:s + 50000], nu[s:s + 50000], ga[s:s + 50000])
                            for s in range(0, n, 50000)], axis=1)
     check_topk(ids.cpu().numpy()[qs], sc.cpu().numpy()[qs], want, k)
+
+
+def test_many_queries_2k_sampled(tq):
+    dev = torch.device("cuda")
+    G, qpg, T, d, bits = 8, 8192, 2048, 128, 3
+    print(f"full-size many queries: {G} groups x {qpg} queries x {T} keys, b={bits}", flush=True)
+    ctx = tq.Context(d, bits, 0)
+    K, _ = wl.outlier_keys_torch(1, G, T, d, seed=8, device=dev)
+    Kf = K.view(G * T, d)
+    rec = tq.tq_quantize(ctx, Kf)
+    q = wl.gaussian_torch((G, qpg, d), 9, dev)
+    ws = tq.tq_prep_queries(ctx, q)
+    logits = tq.tq_scores_prepared(ctx, ws, G, qpg, rec, T=T, ldk=T)
+    torch.cuda.synchronize()
+    p = O.make_params(d, bits, 0)
+    X = Kf.float().cpu().numpy()
+    ref = O.quantize(p, X, return_unpacked=True)
+    g = {k: v.cpu().numpy() for k, v in rec.items()}
+    check_quantized(p, g, ref, X)
+    same = np.all(g["codes"] == ref["codes"], axis=1) & np.all(g["signs"] == ref["signs"], axis=1)
+    rng = np.random.default_rng(61)
+    Q = q.cpu().numpy()
+    L = logits.cpu().numpy()
+    for grp in (0, 5):
+        qs = np.sort(np.concatenate([[0, 1, qpg - 1], rng.choice(np.arange(2, qpg - 1), 61, replace=False)]))
+        sl = slice(grp * T, (grp + 1) * T)
+        want = O.scores(p, Q[grp][qs].astype(np.float64), ref["codes"][sl], ref["signs"][sl],
+                        ref["norms"][sl], ref["rnorms"][sl])
+        keep = same[sl]
+        assert_close(L[grp][qs][:, keep], want[:, keep], what=f"logits group {grp}")
