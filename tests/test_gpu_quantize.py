@@ -75,6 +75,21 @@ def test_quantize_fp32_two_tile_path(tq, bits):
     check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
 
 
+@pytest.mark.parametrize("n", [700, 5000])
+def test_quantize_bf16_tiny_vectors(tq, n):
+    # lengths ~1e-19 and ~1e-35 (squares far below the fp32 normal range, some
+    # inputs themselves denormal) among ordinary vectors, on both tile sizes
+    X = wl.gaussian((n, 128), 27)
+    X[: n // 5] *= 1e-20
+    X[n // 5: 2 * n // 5: 3] *= 1e-36
+    X = wl.bf16_round(X)
+    print(f"quantize bf16 tiny vectors n={n}", flush=True)
+    ctx, g, xin = _run(tq, 128, 3, X, dtype=torch.bfloat16)
+    p = O.make_params(128, 3, 0)
+    check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
+    assert (g["norms"][: n // 5] > 0).all()
+
+
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_quantize_mse_mode(tq, bits):
     X = wl.bf16_round(wl.gaussian((777, 128), 4))
