@@ -83,6 +83,10 @@ def test_scores_random_records(tq, d, bits, G, qpg, T, ldk):
     (128, 4, 1, 12, 64, 64), (128, 3, 1, 1024, 70, 70),
     # geometry with more than 12 MFMAs per 16 keys: one head group per wave
     (200, 4, 1, 72, 200, 200),
+    # 1024 head groups or more (query prep over many blocks per CU), at
+    # b = 2, 3, 4, d = 64 and 128, with a partial last head group
+    (128, 3, 2, 2048, 100, 100), (64, 2, 4, 1024, 70, 70), (128, 4, 1, 4096, 40, 40),
+    (128, 3, 1, 4099, 33, 33),
 ])
 def test_scores_many_queries_per_group(tq, d, bits, G, qpg, T, ldk):
     ctx = tq.Context(d, bits, 0)
