@@ -62,6 +62,8 @@ extern "C" {
 #define TQ_ENOTSUP  (-2)   /* valid request the library does not implement */
 #define TQ_ENOMEM   (-3)   /* host or device allocation failed (init only) */
 #define TQ_EHIP     (-4)   /* a HIP runtime call or kernel launch failed */
+#define TQ_ESCRATCH (-5)   /* the request needs more scratch memory than the
+                              library's static buffer (TQ_SCRATCH_BYTES) holds */
 
 /* input element types for tq_quantize */
 #define TQ_F32   0
@@ -272,6 +274,21 @@ int tq_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n,
             const uint8_t *codes, const uint8_t *signs, const float *norms,
             const float *rnorms, int k, int64_t *ids, float *scores,
             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* tq_scores for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, checks, kernels and results as tq_scores, but the prepared
+ * queries live in a static device buffer of TQ_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends, so the call takes no
+ * workspace and allocates nothing.  Requests whose prepared queries,
+ * tq_workspace_size(TQ_OP_SCORES, G, qpg), exceed TQ_SCRATCH_BYTES return
+ * TQ_ESCRATCH before anything is launched.  Every call on one GPU shares that
+ * GPU's buffer: calls that overlap in time on one GPU (on different streams
+ * or from different threads) race and must be serialised by the caller. */
+#define TQ_SCRATCH_BYTES (16 << 20)
+int tq_scores_static(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,
+                     const uint8_t *codes, const uint8_t *signs, const float *norms,
+                     const float *rnorms, float *logits, hipStream_t stream);
 
 /* Static string for a status code. */
 const char *tq_strerror(int status);

@@ -172,11 +172,36 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
     ctx->S2A_hi = dfr + 2 * nfr;
     ctx->S2A_lo = dfr + 3 * nfr;
   }
+  // the static scratch buffer of this device is located once, at init
+  if (tq::scratch_attach(ctx->device) == nullptr) {
+    (void)hipFree(ctx->dmem);
+    delete ctx;
+    return TQ_EHIP;
+  }
   *out = ctx;
   return TQ_OK;
 }
 
 }  // namespace
+
+namespace tq {
+
+// Argument checks of tq_scores apart from its workspace (shared with the
+// static-scratch variant).  TQ_OK with G == 0 or T == 0 means nothing to do.
+int check_scores_call(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,
+                      const uint8_t *codes, const uint8_t *signs, const float *norms,
+                      const float *rnorms, const float *logits) {
+  if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
+  if (G < 0 || T < 0 || ldk < T || qpg < 1 || qpg > TQ_MAX_QPG_SCORES) return TQ_EINVAL;
+  if (G == 0 || T == 0) return TQ_OK;
+  if (!q || !codes || !signs || !norms || !rnorms || !logits) return TQ_EINVAL;
+  if (!aligned(codes, 16) || !aligned(signs, 16) || !aligned(norms, 4) || !aligned(rnorms, 4) ||
+      !aligned(q, 4) || !aligned(logits, 4))
+    return TQ_EINVAL;
+  return current_device_matches(ctx);
+}
+
+}  // namespace tq
 
 extern "C" {
 
@@ -260,16 +285,10 @@ int tq_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, 
               const uint8_t *codes, const uint8_t *signs, const float *norms,
               const float *rnorms, float *logits, void *ws, size_t ws_bytes,
               hipStream_t stream) {
-  if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
-  if (G < 0 || T < 0 || ldk < T || qpg < 1 || qpg > TQ_MAX_QPG_SCORES) return TQ_EINVAL;
-  if (G == 0 || T == 0) return TQ_OK;
-  if (!q || !codes || !signs || !norms || !rnorms || !logits || !ws) return TQ_EINVAL;
-  if (!aligned(codes, 16) || !aligned(signs, 16) || !aligned(norms, 4) || !aligned(rnorms, 4) ||
-      !aligned(q, 4) || !aligned(logits, 4) || !aligned(ws, 16))
-    return TQ_EINVAL;
+  int st = tq::check_scores_call(ctx, q, G, qpg, T, ldk, codes, signs, norms, rnorms, logits);
+  if (st != TQ_OK || G == 0 || T == 0) return st;
+  if (!ws || !aligned(ws, 16)) return TQ_EINVAL;
   if (ws_bytes < tq::scores_ws_bytes(ctx, G, qpg)) return TQ_EINVAL;
-  const int st = current_device_matches(ctx);
-  if (st != TQ_OK) return st;
   return tq::launch_scores(ctx, q, G, qpg, T, ldk, codes, signs, norms, rnorms, logits, ws, stream);
 }
 
@@ -471,6 +490,7 @@ const char *tq_strerror(int status) {
     case TQ_ENOTSUP: return "not supported";
     case TQ_ENOMEM: return "out of memory";
     case TQ_EHIP: return "HIP runtime error";
+    case TQ_ESCRATCH: return "request needs more memory than the library's static scratch buffer holds";
     default: return "unknown status";
   }
 }

@@ -96,6 +96,14 @@ int launch_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const 
                 const uint8_t *signs, const float *norms, const float *rnorms, int k,
                 int64_t *ids, float *scores, void *ws, hipStream_t stream);
 
+// tq_scores argument checks apart from the workspace (tq_api.cpp)
+int check_scores_call(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,
+                      const uint8_t *codes, const uint8_t *signs, const float *norms,
+                      const float *rnorms, const float *logits);
+// Device address of the static scratch buffer on `device` (tq_static.hip),
+// looked up once per device with that device current; nullptr on failure.
+void *scratch_attach(int device);
+
 inline int hip_status() { return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP; }
 
 }  // namespace tq
