@@ -104,7 +104,7 @@ def cpu_baseline(bits, budget_s=12.0):
                       f"(fp64 NumPy oracle, {elapsed:.1f} s; host cores {cores}, BLAS threads {blas_threads})"}
 
 
-def cpu_quantize_baseline(bits, n=16384):
+def cpu_quantize_baseline(bits, n=1 << 20):
     import oracle as O
     from oblivious_kv_cache_amd import workloads as wl
     p = O.make_params(128, bits, 0)
@@ -334,8 +334,10 @@ def bench_topk(tq, wl, dev, nq=10000, n=1000000, d=200, k=10):
     DB = wl.power_law_torch(n, d, seed=5, device=dev, dtype=torch.float32, unit=True)
     Q = wl.power_law_torch(nq, d, seed=6, device=dev, dtype=torch.float32, unit=True)
     top1 = torch.empty(nq, dtype=torch.int64, device=dev)
-    for s0 in range(0, nq, 256):                      # exact fp32 brute force
-        top1[s0:s0 + 256] = (Q[s0:s0 + 256] @ DB.T).argmax(dim=1)
+    DB64 = DB.double()
+    for s0 in range(0, nq, 256):                      # exact brute force, fp64 dot products
+        top1[s0:s0 + 256] = (Q[s0:s0 + 256].double() @ DB64.T).argmax(dim=1)
+    del DB64
     out = {}
     for bits in (2, 4):
         ctx = tq.Context(d, bits, 0)
@@ -363,12 +365,124 @@ def bench_topk(tq, wl, dev, nq=10000, n=1000000, d=200, k=10):
     return out
 
 
+def bench_tiny(tq, wl, dev, reps=50):
+    """The small oracle case: 4096 fp32 N(0,1) keys, d=128, b=3, 16 fp32
+    queries: quantize the keys, score them, softmax (one call each, on one
+    stream).  Latency-bound at this size: reported, not judged."""
+    import torch
+    K, Q = wl.tiny_case(seed=0)
+    ctx = tq.Context(128, 3, 0)
+    k = torch.from_numpy(K).to(dev)
+    q = torch.from_numpy(Q).to(dev).view(1, 16, 128)
+    rec = ctx.empty_records(4096, dev)
+    ws = ctx.workspace(tq.TQ_OP_SCORES, 1, 16, device=dev)
+    logits = torch.empty((1, 16, 4096), dtype=torch.float32, device=dev)
+    probs = torch.empty_like(logits)
+
+    def run():
+        tq.tq_quantize(ctx, k, out=rec)
+        tq.tq_scores(ctx, q, rec, T=4096, ldk=4096, logits=logits, ws=ws)
+        tq.tq_softmax(logits, 1.0 / math.sqrt(128), probs=probs)
+
+    ms = _time(torch, run, reps)
+    qms = _time(torch, lambda: tq.tq_quantize(ctx, k, out=rec), reps)
+    sms = _time(torch, lambda: tq.tq_scores(ctx, q, rec, T=4096, ldk=4096, logits=logits, ws=ws), reps)
+    r = {"ms_per_call": ms, "quantize_ms": qms, "scores_ms": sms,
+         "logits_per_s": 16 * 4096 / (ms / 1e3), "vec_per_s": 4096 / (qms / 1e3)}
+    log(f"  tiny case: quantize+scores+softmax {ms * 1e3:.1f} us (quantize {qms * 1e3:.1f} us, "
+        f"scores {sms * 1e3:.1f} us)")
+    ctx.close()
+    return r
+
+
+def bench_softmax_cold(tq, dev, rows=1024, T=32768, nbuf=4, reps=20):
+    """Softmax over logits that are not cache-resident: the rows come from
+    nbuf rotating buffers (537 MB in all, twice the 256 MB Infinity Cache),
+    so every call reads its logits from HBM."""
+    import torch
+    bufs = [torch.randn((rows, T), device=dev) for _ in range(nbuf)]
+    outs = [torch.empty_like(b) for b in bufs]
+    i = [0]
+
+    def run():
+        j = i[0] % nbuf
+        tq.tq_softmax(bufs[j], 0.088, probs=outs[j])
+        i[0] += 1
+
+    ms = _time(torch, run, reps)
+    by = 2 * rows * T * 4
+    del bufs, outs
+    return {"ms": ms, "bytes": by, "gbs": by / (ms / 1e3) / 1e9, "hbm_frac": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+
+def run_config(args):
+    """One of the five workloads on its own (--config 1, 3, 4 or 5), one JSON
+    line.  Config 2 (decode 32K) is the default run in main()."""
+    import torch
+    from oblivious_kv_cache_amd import binding as tq
+    from oblivious_kv_cache_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    line = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+    if args.config == 1:
+        r = bench_tiny(tq, wl, dev, reps=max(args.steps, 10))
+        line.update({"metric": "tiny case: logits/s of quantize + scores + softmax", "value": r["logits_per_s"],
+                     "unit": "logits/s", "ms_per_step": r["ms_per_call"], "dtype": "int8-mfma/f32",
+                     "config": {"workload": "4096 fp32 keys d=128 b=3, 16 queries"}, "extra": r})
+    elif args.config == 3:
+        d, b = 128, args.bits
+        Xs = [wl.power_law_torch(1 << 20, d, seed=3 + i, device=dev) for i in range(2)]
+        c2 = tq.Context(d, b, seed=0)
+        out = c2.empty_records(1 << 20, dev)
+        it = [0]
+
+        def run():
+            tq.tq_quantize(c2, Xs[it[0] % 2], out=out)
+            it[0] += 1
+
+        ms = _time(torch, run, max(args.steps, 10))
+        vps = (1 << 20) / (ms / 1e3)
+        hw = vps * (2 + 3) * 2 * d * d / 1e12
+        line.update({"metric": "quantize vec/s (2^20 bf16 d=128)", "value": vps, "unit": "vec/s",
+                     "ms_per_step": ms, "dtype": "bf16-mfma/f32",
+                     "config": {"workload": f"2^20 x 128 bf16 power-law vectors, b={b}"},
+                     "roofline": {"bound": "mfma", "achieved": hw, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": hw / BF16_PEAK_TFLOPS, "traffic": None}})
+        if not args.no_cpu:
+            v = cpu_quantize_baseline(b)
+            line["cpu_baseline"] = {"value": v, "unit": "vec/s", "cores": _host_threads(), "kind": "oracle",
+                                    "sample": "2^20 power-law vectors, d=128"}
+    elif args.config == 4:
+        r = bench_attend(tq, wl, dev)
+        line.update({"metric": "attention 128K: tokens/s (logits + softmax + value sum)",
+                     "value": r["tokens_per_s"], "unit": "tokens/s", "ms_per_step": r["ms"], "dtype": "int8-mfma/f32",
+                     "config": {"workload": "4 x 8 KV heads x 131072 tokens, d=128, K b=3 prod, V b=3 mse, GQA 4"},
+                     "roofline": {"bound": "hbm", "achieved": r["alg_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": r["hbm_frac"], "traffic": None}, "extra": r})
+        if not args.no_cpu:
+            line["cpu_baseline"] = cpu_attend_baseline()
+    elif args.config == 5:
+        r = bench_topk(tq, wl, dev)
+        key = f"b{args.bits if args.bits in (2, 4) else 2}"
+        line.update({"metric": "vector search: query-vector pairs/s (top-10 over 10^6 d=200)",
+                     "value": r[key]["pairs_per_s"], "unit": "pairs/s", "ms_per_step": r[key]["ms"],
+                     "dtype": "int8-mfma/f32", "config": {"workload": f"10^4 queries x 10^6 d=200, {key}, top-10"},
+                     "extra": r})
+        if not args.no_cpu:
+            line["cpu_baseline"] = cpu_topk_baseline()
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--bits", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=(1, 2, 3, 4, 5),
+                    help="workload: 1 tiny oracle case, 2 decode 32K (default, the headline metric), "
+                         "3 streaming quantize, 4 attention 128K, 5 vector search")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -379,6 +493,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library runs "
               "on a single GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    if args.config != 2:
+        run_config(args)
+        return
 
     import torch
     from oblivious_kv_cache_amd import binding as tq
@@ -454,7 +571,13 @@ def main():
         sm_bytes = 2 * n_logits * 4
         extra["softmax_32k"] = {"ms": sm_ms, "bytes": sm_bytes, "gbs": sm_bytes / (sm_ms / 1e3) / 1e9,
                                 "hbm_frac": sm_bytes / (sm_ms / 1e3) / 1e9 / HBM_PEAK_GBS}
-        log(f"  softmax: {sm_ms * 1e3:.1f} us, {extra['softmax_32k']['gbs']:.0f} GB/s")
+        log(f"  softmax: {sm_ms * 1e3:.1f} us, {extra['softmax_32k']['gbs']:.0f} GB/s (logits just written: "
+            "partly cache-resident)")
+        extra["softmax_32k_cold"] = bench_softmax_cold(tq, dev)
+        log(f"  softmax cold: {extra['softmax_32k_cold']['ms'] * 1e3:.1f} us, "
+            f"{extra['softmax_32k_cold']['gbs']:.0f} GB/s")
+        log("tiny case (4096 keys, 16 queries)")
+        extra["tiny_4096"] = bench_tiny(tq, wl, dev)
         for b in (2, 4):
             if b != bits:
                 extra[f"decode_32k_b{b}"] = bench_decode_bits(tq, wl, dev, b)

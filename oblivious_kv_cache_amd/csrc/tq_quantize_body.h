@@ -208,6 +208,50 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
       ss[t] += __shfl_xor(ss[t], 16);
       ss[t] += __shfl_xor(ss[t], 32);
     }
+    // A vector shorter than 2^-64 is rotated as x * 2^64 (exact: a power of
+    // two), so that neither its inputs nor the products of the rotation fall
+    // into the float32 denormal range and 1/nu cannot overflow; nu itself is
+    // the unscaled length.  Such vectors are rare, so the wave takes this
+    // branch only when one of its lanes has one.
+    float xsc[NTL];
+    bool any_tiny = false;
+#pragma unroll
+    for (int t = 0; t < NTL; ++t) {
+      const bool tiny = ss[t] > 0.0 && ss[t] < 0x1.0p-128;
+      xsc[t] = tiny ? 0x1.0p64f : 1.f;
+      any_tiny |= tiny;
+    }
+    if (__builtin_amdgcn_ballot_w64(any_tiny) != 0) {
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          if constexpr (BF16IN) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bx[t][k][e] = (__bf16)((float)bx[t][k][e] * xsc[t]);
+          } else {
+            // the hi/lo split is redone from the scaled float32 inputs
+            const int j0 = k * 32 + grp * 8;
+            const bool in = valid[t] && (FULL || k * 32 < xval);
+            float4 lo4 = make_float4(0.f, 0.f, 0.f, 0.f), hi4 = lo4;
+            if (in) {
+              const float4 *p = reinterpret_cast<const float4 *>(
+                  reinterpret_cast<const float *>(a.x) + vi[t] * a.ldx + j0);
+              lo4 = p[0];
+              hi4 = p[1];
+            }
+            const float xs[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float v = xs[e] * xsc[t];
+              const __bf16 h = (__bf16)v;
+              bx[t][k][e] = h;
+              bxl[t][k][e] = (__bf16)(v - (float)h);
+            }
+          }
+        }
+      }
+    }
 
     // Per vector: 1/nu, and state for the codes and the residual.
     uint32_t cw[NTL][CW];
@@ -217,7 +261,7 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
     for (int t = 0; t < NTL; ++t) {
       const double nud = sqrt(ss[t]);
       nu[t] = (float)nud;
-      inv[t] = nud > 0.0 ? (float)(1.0 / nud) : 0.f;
+      inv[t] = nud > 0.0 ? (float)(1.0 / (nud * (double)xsc[t])) : 0.f;
       rs[t] = 0.f;
 #pragma unroll
       for (int i = 0; i < CW; ++i) cw[t][i] = 0u;

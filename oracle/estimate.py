@@ -89,13 +89,25 @@ def topk(score_matrix, k):
     return ids, vals
 
 
-def exact_top1(Q, X, chunk=4096):
-    """Exact inner-product top-1 per query (float64 dots; ties -> lower id)."""
+def exact_top1(Q, X, chunk=4096, db_chunk=65536):
+    """Exact inner-product top-1 per query (float64 dots; ties -> lower id).
+
+    The database is visited in chunks in increasing id order; a later chunk
+    replaces the running best only with a strictly larger dot product, so
+    ties keep the lower id exactly as one argmax over all ids would."""
     Q = np.asarray(Q, np.float64)
-    best = np.empty(Q.shape[0], np.int64)
+    X = np.asarray(X)
+    best = np.zeros(Q.shape[0], np.int64)
+    bestv = np.full(Q.shape[0], -np.inf)
     for s in range(0, Q.shape[0], chunk):
-        sc = Q[s:s + chunk] @ np.asarray(X, np.float64).T
-        best[s:s + chunk] = np.argmax(sc, axis=1)   # first maximum = lower id
+        q = Q[s:s + chunk]
+        for c0 in range(0, X.shape[0], db_chunk):
+            sc = q @ X[c0:c0 + db_chunk].astype(np.float64).T
+            j = np.argmax(sc, axis=1)                # first maximum = lower id
+            v = sc[np.arange(len(q)), j]
+            up = v > bestv[s:s + chunk]
+            best[s:s + chunk][up] = c0 + j[up]
+            bestv[s:s + chunk][up] = v[up]
     return best
 
 

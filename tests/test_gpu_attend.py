@@ -110,3 +110,19 @@ def test_attend_128k_sampled(tq):
         assert_close(logits[g].cpu().numpy(), lw, what=f"logits g{g}")
         assert_close(probs[g].cpu().numpy(), pw, atol=1e-7, rtol=1e-3, what=f"probs g{g}")
         assert_close(out[g].cpu().numpy(), ow, what=f"out g{g}")
+
+
+def test_attend_deterministic(tq):
+    # bitwise-identical repeats: split-K partials are combined in a fixed order
+    d, G, qpg, T = 128, 3, 4, 5000
+    kctx, vctx = tq.Context(d, 3, 0), tq.Context(d, 3, 1, tq.TQ_MODE_MSE)
+    kc, ks, kn, kr = wl.random_records(G * T, kctx.code_bytes, kctx.sign_bytes, seed=60)
+    vc, _, vn, _ = wl.random_records(G * T, vctx.code_bytes, 16, seed=61)
+    krec = _dev({"codes": kc, "signs": ks, "norms": kn, "rnorms": kr}, ("codes", "signs", "norms", "rnorms"))
+    vrec = _dev({"codes": vc, "norms": vn}, ("codes", "norms"))
+    q = torch.from_numpy(wl.gaussian((G, qpg, d), 62)).cuda()
+    runs = [tq.tq_attend(kctx, vctx, q, krec, vrec, 0.088, want_logits=True, want_probs=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)

@@ -67,12 +67,22 @@ def test_decode_32k_sampled(tq, bits):
     assert same.mean() > 0.99
     Q = q.cpu().numpy().astype(np.float64)
     L = logits.cpu().numpy()
+    wants = []
     for gi, grp in enumerate(groups):
         sl = slice(gi * len(toks), (gi + 1) * len(toks))
         want = O.scores(p, Q[grp], ref["codes"][sl], ref["signs"][sl], ref["norms"][sl], ref["rnorms"][sl])
+        wants.append(want)
         got = L[grp][:, toks]
         keep = same[sl]
         assert_close(got[:, keep], want[:, keep], what=f"logits group {grp}")
+    # every sampled key, band cases included: the sampled records are replaced
+    # by the oracle's own and the whole cache is scored again in the same
+    # launch configuration
+    for key in ("codes", "signs", "norms", "rnorms"):
+        cache[key].index_copy_(0, idx_t, torch.from_numpy(np.ascontiguousarray(ref[key])).to(dev))
+    L2 = tq.tq_scores(ctx, q, cache, T=T, ldk=T).cpu().numpy()
+    for gi, grp in enumerate(groups):
+        assert_close(L2[grp][:, toks], wants[gi], what=f"logits group {grp} (oracle records)")
     # softmax at full size: properties that hold at any size (values are
     # checked against the oracle on generator inputs in test_gpu_scores)
     P = probs.cpu().numpy()
@@ -155,6 +165,9 @@ def test_many_queries_2k_sampled(tq):
     rng = np.random.default_rng(61)
     Q = q.cpu().numpy()
     L = logits.cpu().numpy()
+    # the oracle's own records, every key, in the same launch configuration
+    orec = {k: torch.from_numpy(np.ascontiguousarray(ref[k])).to(dev) for k in ("codes", "signs", "norms", "rnorms")}
+    L2 = tq.tq_scores_prepared(ctx, ws, G, qpg, orec, T=T, ldk=T).cpu().numpy()
     for grp in (0, 5):
         qs = np.sort(np.concatenate([[0, 1, qpg - 1], rng.choice(np.arange(2, qpg - 1), 61, replace=False)]))
         sl = slice(grp * T, (grp + 1) * T)
@@ -162,3 +175,81 @@ def test_many_queries_2k_sampled(tq):
                         ref["norms"][sl], ref["rnorms"][sl])
         keep = same[sl]
         assert_close(L[grp][qs][:, keep], want[:, keep], what=f"logits group {grp}")
+        assert_close(L2[grp][qs], want, what=f"logits group {grp} (oracle records)")
+
+
+def _oracle_topk_chunked(p, Q, rec, k, chunk=50000):
+    """Oracle top-k lists (score desc, id asc) over a large database, scored
+    in chunks.  Within a chunk only the scores at or above the chunk's k-th
+    largest can enter (ties kept), so the running merge keeps exactly what one
+    sort of every score would."""
+    nq = Q.shape[0]
+    best_s = np.full((nq, 0), -np.inf)
+    best_i = np.zeros((nq, 0), np.int64)
+    n = rec["norms"].shape[0]
+    for c0 in range(0, n, chunk):
+        sl = slice(c0, min(n, c0 + chunk))
+        S = O.scores(p, Q, rec["codes"][sl], rec["signs"][sl], rec["norms"][sl], rec["rnorms"][sl])
+        kth = np.partition(S, S.shape[1] - k, axis=1)[:, S.shape[1] - k] if S.shape[1] > k else S.min(axis=1)
+        ns, ni = [], []
+        for qi in range(nq):
+            sel = np.nonzero(S[qi] >= kth[qi])[0]
+            s_all = np.concatenate([best_s[qi], S[qi, sel]])
+            i_all = np.concatenate([best_i[qi], c0 + sel])
+            order = np.lexsort((i_all, -s_all))[:k]
+            ns.append(s_all[order])
+            ni.append(i_all[order])
+        best_s, best_i = np.stack(ns), np.stack(ni)
+        print(f"  oracle scores: {sl.stop} / {n} vectors", flush=True)
+    return best_i, best_s
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_topk_1e6_recall_vs_oracle(tq, bits):
+    """Vector search at full size on the oracle's own quantized database:
+    10^6 unit-norm d=200 power-law vectors (oracle-quantized, searched by the
+    GPU), 10^4 queries on the GPU; the oracle scores a seeded subset of 1000
+    queries, builds their top-10 lists and the exact top-1 (fp64 dot
+    products), and the recall 1@k of the GPU's lists must equal the oracle's
+    query by query, except where the exact top-1 ties the oracle's k-th score
+    within the tolerance."""
+    dev = torch.device("cuda")
+    nq, n, d, k = 10000, 1000000, 200, 10
+    print(f"recall vs oracle: {nq} queries x {n} d={d} vectors, b={bits}", flush=True)
+    DB = wl.power_law_torch(n, d, seed=5, device=dev, dtype=torch.float32, unit=True)
+    Q = wl.power_law_torch(nq, d, seed=6, device=dev, dtype=torch.float32, unit=True)
+    X = DB.cpu().numpy()
+    Qn = Q.cpu().numpy()
+    del DB
+    p = O.make_params(d, bits, 0)
+    print("  oracle quantizes the database", flush=True)
+    rec = O.quantize(p, X)
+    ctx = tq.Context(d, bits, 0)
+    drec = {key: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for key, v in rec.items()}
+    ids, sc = tq.tq_topk(ctx, Q, drec, k)
+    ids, sc = ids.cpu().numpy(), sc.cpu().numpy()
+    del drec
+    qs = np.sort(np.random.default_rng(70 + bits).choice(nq, 1000, replace=False))
+    Qs = Qn[qs].astype(np.float64)
+    ref_i, ref_s = _oracle_topk_chunked(p, Qs, rec, k)
+    print("  oracle exact top-1 (fp64)", flush=True)
+    top1 = O.exact_top1(Qs, X)
+    g_ids = ids[qs]
+    # the GPU's lists against the oracle's scores of the same ids (tie rule)
+    for qi in range(len(qs)):
+        g = g_ids[qi]
+        gs = O.scores(p, Qs[qi:qi + 1], rec["codes"][g], rec["signs"][g], rec["norms"][g], rec["rnorms"][g])[0]
+        tol = 1e-4 + 1e-3 * np.abs(ref_s[qi])
+        assert (np.abs(gs - ref_s[qi]) <= tol).all(), (qi, gs - ref_s[qi])
+        assert (np.abs(sc[qs[qi]] - gs) <= 1e-4 + 1e-3 * np.abs(gs)).all()
+    # recall 1@k, query by query
+    for kk in (1, 2, 4, 8, 10):
+        in_g = (g_ids[:, :kk] == top1[:, None]).any(axis=1)
+        in_o = (ref_i[:, :kk] == top1[:, None]).any(axis=1)
+        for qi in np.nonzero(in_g != in_o)[0]:
+            t = top1[qi]
+            st = O.scores(p, Qs[qi:qi + 1], rec["codes"][t:t + 1], rec["signs"][t:t + 1], rec["norms"][t:t + 1],
+                          rec["rnorms"][t:t + 1])[0, 0]
+            kth = ref_s[qi, kk - 1]
+            assert abs(st - kth) <= 1e-4 + 1e-3 * abs(kth), (kk, qi, st, kth)
+        print(f"  recall 1@{kk}: gpu {in_g.mean():.4f} oracle {in_o.mean():.4f}", flush=True)

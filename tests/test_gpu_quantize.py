@@ -75,19 +75,23 @@ def test_quantize_fp32_two_tile_path(tq, bits):
     check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
 
 
-@pytest.mark.parametrize("n", [700, 5000])
-def test_quantize_bf16_tiny_vectors(tq, n):
-    # lengths ~1e-19 and ~1e-35 (squares far below the fp32 normal range, some
-    # inputs themselves denormal) among ordinary vectors, on both tile sizes
+@pytest.mark.parametrize("n,bf16", [(700, True), (5000, True), (700, False), (5000, False)])
+def test_quantize_tiny_vectors(tq, n, bf16):
+    # lengths ~1e-19, ~1e-35 and ~1e-39 (squares far below the fp32 normal
+    # range; at ~1e-39 every input is denormal and 1/nu would overflow
+    # float32) among ordinary vectors, on both tile sizes
     X = wl.gaussian((n, 128), 27)
     X[: n // 5] *= 1e-20
     X[n // 5: 2 * n // 5: 3] *= 1e-36
-    X = wl.bf16_round(X)
-    print(f"quantize bf16 tiny vectors n={n}", flush=True)
-    ctx, g, xin = _run(tq, 128, 3, X, dtype=torch.bfloat16)
+    X[2 * n // 5: 3 * n // 5: 7] *= 1e-40
+    if bf16:
+        X = wl.bf16_round(X)
+    print(f"quantize {'bf16' if bf16 else 'fp32'} tiny vectors n={n}", flush=True)
+    ctx, g, xin = _run(tq, 128, 3, X, dtype=torch.bfloat16 if bf16 else torch.float32)
     p = O.make_params(128, 3, 0)
     check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
-    assert (g["norms"][: n // 5] > 0).all()
+    assert (g["norms"][: 3 * n // 5] > 0).all()
+    assert np.isfinite(g["rnorms"]).all()
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])

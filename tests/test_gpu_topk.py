@@ -112,3 +112,12 @@ def test_topk_errors(tq):
         tq.tq_topk(ctx, q, rec, 11)          # k > n
     with pytest.raises(tq.TQError):
         tq.tq_topk(ctx, q, rec, 65)          # k > TQ_MAX_TOPK
+
+
+@pytest.mark.parametrize("k", [10, 64])
+def test_topk_deterministic(tq, k):
+    # bitwise-identical repeats (ids and scores), including the candidate merge
+    p, ctx, rec, Q = _setup(tq, 200, 2, 21, 30000, seed=77, records="random")
+    a = _run(tq, ctx, Q, rec, k)
+    b = _run(tq, ctx, Q, rec, k)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -58,8 +58,10 @@ def test_exact_top1_and_recall():
     Q = rng.standard_normal((40, 16))
     top1 = O.exact_top1(Q, X, chunk=7)
     assert np.array_equal(top1, np.argmax(Q @ X.T, axis=1))
+    assert np.array_equal(O.exact_top1(Q, X, chunk=7, db_chunk=33), top1)   # chunked database
     X2 = np.vstack([X, X[:1]])                        # duplicate row -> tie, lower id wins
     assert (O.exact_top1(X[:1], X2) == 0).all()
+    assert (O.exact_top1(X[:1], X2, db_chunk=100) == 0).all()   # the tie spans two chunks
     ids, _ = O.topk(Q @ X.T, 10)
     assert O.recall_at_k(ids, top1, 1) == 1.0
     noisy = Q @ X.T + rng.standard_normal((40, 500)) * 2
