@@ -108,6 +108,26 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
     }
     ctx->basis[p] = (float)(acc / L);
   }
+  // the same expansion with every odd monomial of up to 4 code bits: the w
+  // single bits, then the products of three bits (w = 3: {012}; w = 4:
+  // {012, 013, 023, 123}); used by the value sum of the attention kernel
+  {
+    static const int tri[4][3] = {{0, 1, 2}, {0, 1, 3}, {0, 2, 3}, {1, 2, 3}};
+    const int ntri = w == 3 ? 1 : w == 4 ? 4 : 0;
+    for (int p = 0; p < w + ntri; ++p) {
+      double acc = 0.0;
+      for (int idx = 0; idx < L; ++idx) {
+        double s = 1.0;
+        if (p < w) {
+          s = ((idx >> p) & 1) ? 1.0 : -1.0;
+        } else {
+          for (int b = 0; b < 3; ++b) s *= ((idx >> tri[p - w][b]) & 1) ? 1.0 : -1.0;
+        }
+        acc += hp.c[idx] * s;
+      }
+      ctx->vbasis[p] = (float)(acc / L);
+    }
+  }
 
   if (hipGetDevice(&ctx->device) != hipSuccess) {
     delete ctx;

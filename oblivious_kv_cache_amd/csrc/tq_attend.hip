@@ -8,17 +8,35 @@
 //   out   = sum_t p_t * nu_t * Pi_v^T c_v[idx_t]
 //         = Pi_v^T ( sum_t p_t nu_t c_v[idx_t] )     (rotate back once).
 // Split over token chunks like flash-decoding on one GPU:
-//   partial kernel (block = one chunk of one query group):
+//   partial kernel (block = one query group x a run of chunks, online softmax):
 //     A. int8-MFMA logits of the chunk into LDS (and to the optional logits
-//        output);
-//     B. chunk max m and sum l of exp(z - m) per head, weights
-//        w_t = exp(z_t - m) nu_t in LDS;
-//     C. value codes of the chunk staged in LDS with 16-byte loads; lanes own
-//        8 rotated coordinates (one record byte run each), token streams
-//        split across lane groups and waves; centroids from an LDS table;
-//     D. stream partials summed through LDS; (m, l, acc[d]) written out.
-//   combine kernel: merges chunks with the usual max rescaling, divides by
-//     the total, applies Pi_v^T; optionally normalises the logits to probs.
+//        output); the chunk's value records staged in LDS;
+//     B. chunk max, running max M, rescale factor f = exp(M_old - M_new);
+//        weights w_t = exp(z_t - M) nu_t turned into int8 fixed-point digits
+//        (the A operand of the value sum); the staged value records
+//        transposed into bit-plane words (32 tokens per word);
+//     C. the value sum on int8 MFMA over bit planes (below);
+//     D. per-block partials (M, sum of exp, rotated accumulator).
+//   combine kernel: merges the partials with the usual max rescaling,
+//     divides by the total, applies Pi_v^T; optionally normalises the logits
+//     to probs.
+//
+// Value sum on matrix cores.  The value codebook is antisymmetric, so a
+// centroid is an odd multilinear polynomial of the sign variables
+// s_p = 2 bit_p - 1 of its code bits: c = sum_P A_P prod_{p in P} s_p over the
+// single bits and (w >= 3) the triples of bits, where a product of three signs
+// is 2 (parity of the three bits) - 1.  Hence for coordinate i
+//   sum_t w_t c[idx_t,i] = sum_P A_P (2 V_P,i - W),
+//   V_P,i = sum_t w_t beta_P(t,i),   W = sum_t w_t,
+// with beta_P the bit (or bit parity) P of token t's code i.  V is an int8
+// matrix product over tokens: the A operand holds the weights of 64 tokens as
+// four base-128 digits per head (16 rows = 4 heads x 4 digits, scaled per
+// chunk), the B operand the bits of 64 tokens of 16 coordinates, built from
+// one 32-token plane word per lane as (word & 0x01010101 << j) -- bit j of
+// each byte -- exactly as the key estimator builds its B from record words.
+// The plane words come from the staged value records by 32 x 32 bit
+// transposes.  W is the same product against an all-ones B, so 2 V - W is
+// exact in int32 before the digits are recombined in fp32.
 #include <algorithm>
 #include <cfloat>
 
@@ -29,10 +47,13 @@ namespace {
 
 constexpr int CH = 512;            // tokens per chunk
 constexpr int NT = 256;            // threads per partial block
-constexpr int VB_MAX = 64;         // value code bytes per token handled (d <= 128 at 4 bits; 170 at 3)
+constexpr int NB32 = CH / 32;      // 32-token plane words per bit row and chunk
 #ifndef TQ_ATT_BLOCKS
 #define TQ_ATT_BLOCKS 512          // partial blocks per call (2 per CU are resident)
 #endif
+
+// odd monomials of the code bits of a w-bit value code: w singles + triples
+__host__ __device__ constexpr int value_planes(int vw) { return vw + (vw == 3 ? 1 : vw == 4 ? 4 : 0); }
 
 struct AttArgs {
   const uint8_t *kcodes, *ksigns;
@@ -43,39 +64,95 @@ struct AttArgs {
   float *logits;                   // optional [G][qpg][T]
   float *part;                     // [G*hg][nsplit][4][d + 2]
   int64_t T, ldk;
-  int qpg, hg, nchunk, nsplit, cps, d, kcb, ksb, vcb, vw;
+  int qpg, hg, nchunk, nsplit, cps, d, kcb, ksb, vcb;
   float alpha, scale;
-  float vc[16];                    // value centroids
+  float vbasis[8];                 // value codebook: odd-monomial coefficients
 };
 
+// 32 x 32 bit transpose in registers: afterwards bit i of x[q] is what bit q
+// of x[i] was.  Five rounds swap the off-diagonal blocks of size J.
+template <int J>
+__device__ __forceinline__ void transpose_round(uint32_t (&x)[32]) {
+  constexpr uint32_t M = J == 4 ? 0x0f0f0f0fu : J == 2 ? 0x33333333u : 0x55555555u;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    if ((k & J) == 0) {
+      const uint32_t lo = x[k], hi = x[k + J];
+      if constexpr (J == 16) {          // whole 16-bit halves: byte permutes
+        x[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        x[k + J] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+      } else if constexpr (J == 8) {    // whole bytes: byte permutes
+        x[k] = __builtin_amdgcn_perm(hi, lo, 0x06020400u);
+        x[k + J] = __builtin_amdgcn_perm(hi, lo, 0x07030501u);
+      } else {                          // bit fields: two bitfield selects
+        x[k] = (lo & M) | ((hi << J) & ~M);
+        x[k + J] = ((lo >> J) & M) | (hi & ~M);
+      }
+    }
+  }
+}
+__device__ __forceinline__ void transpose32(uint32_t (&x)[32]) {
+  transpose_round<16>(x);
+  transpose_round<8>(x);
+  transpose_round<4>(x);
+  transpose_round<2>(x);
+  transpose_round<1>(x);
+}
+
 // One block = one query group x one split (a run of `cps` chunks of CH
-// tokens), with an online softmax over the chunks: the running max M and the
-// value accumulators (rotated coordinates, in registers) are rescaled by
-// exp(M_old - M_new) whenever a chunk raises the max.  The key words, value
-// codes and value norms of chunk c+1 are loaded into registers while chunk c
-// is processed, so every block keeps its next ~50 KB in flight.
+// tokens).  Wave wv owns the 64-token blocks wv and wv + 4 of every chunk and
+// everything computed from them: their logits, staged value records, plane
+// words, fixed-point weights and value sums, with an online softmax of its
+// own (running max M and sum of exp per head; the value accumulators are
+// rescaled by exp(M_old - M_new) whenever its tokens raise the max).  The
+// waves therefore never wait for each other inside the chunk loop; their
+// four partial softmax states are merged once at the end.  The key words,
+// value records and value norms of the wave's next tokens are loaded into
+// registers while the current ones are processed.
 #ifndef TQ_ATT_WAVES_PER_EU
 #define TQ_ATT_WAVES_PER_EU 2
 #endif
-template <int CB16, int SB16, int W, int VR>      // VR = value code bytes / 8 = 16-byte units per thread per chunk
+template <int CB16, int SB16, int W, int VW>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(TQ_ATT_WAVES_PER_EU)))
 attend_partial_kernel(AttArgs a) {
   constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
   using KW = KeyWords<CB16, SB16, W>;
-  __shared__ __align__(16) float zt[CH][4];         // scaled logits, then weights, [token][head]
-  __shared__ __align__(16) uint8_t vbytes[CH * VB_MAX + 16];
-  __shared__ float vnu[CH];
-  __shared__ float2 lut2[256];                       // (c[a], c[b]) for the code pair a | b << vw
-  __shared__ float red[4][NT / 64];
-  __shared__ float accs[NT / 64][4][128];          // per-wave partials (d <= 128)
+  constexpr int NPL = value_planes(VW);
+  constexpr int VBMAX = 16 * VW;                  // value record bytes (d <= 128)
+  constexpr int VR = VBMAX / 8;                   // 16-byte value units per lane per chunk, at most
+  constexpr int NPMAX = VBMAX * 8;                // bit rows of a value record
+  constexpr int WT = 128;                         // tokens of a wave per chunk
+  // plane-word rows: bit row P of a 32-token block at plane_index(P), a skew
+  // of 4 words per coordinate tile (16 VW rows) and a block stride of TSTR
+  // words (4 mod 32) spread the LDS banks of both the transposing lanes and
+  // the MFMA operand readers; the rows of the next coordinate tile are then
+  // 16 VW + 4 words on
+  auto plane_index = [](int P) { return P + 4 * (P / (16 * VW)); };
+  constexpr int TSTR = NPMAX + NPMAX / (4 * VW) + 4;
+  // fixed-point weights U = w S 2^(21 - j), [head][token] with a skew of 4
+  // words per 32 tokens
+  constexpr int UST = WT + WT / 8 + 4;
+  auto uidx = [](int t) { return t + 4 * (t >> 5); };
+  struct WaveLds {
+    float zt[WT][4];                              // scaled logits [token][head]
+    uint32_t vrec[WT * VBMAX / 4];                // staged value records, token-major
+    uint32_t tpl[WT / 32 * TSTR];                 // plane words [32-token block][bit row]
+    uint32_t ufix[4 * UST];                       // fixed-point weights
+    float vacc[4][128 + 16];                      // value sums [head][rotated coordinate]
+  };
+  __shared__ __align__(16) WaveLds wl[NT / 64];
+  __shared__ float fin[NT / 64][4][2];            // per wave and head: running max, sum of exp
 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4, wv = tid >> 6;
+  WaveLds &L = wl[wv];
   const int64_t gidx = blockIdx.y, kg = gidx / a.hg;
   const int hgi = (int)(gidx - kg * a.hg);
   const int c_begin = blockIdx.x * a.cps;
   const int c_end = min(c_begin + a.cps, a.nchunk);
   const int d = a.d;
   const int64_t T = a.T;
+  const int vcb = a.vcb, nd = vcb / 4;                 // value record dwords
+  const int nct = (d + 15) / 16;                       // 16-coordinate tiles
 
   const uint8_t *prep = a.prep + gidx * prep_stride(NM);
   i32x4 A[NM];
@@ -88,35 +165,28 @@ attend_partial_kernel(AttArgs a) {
   const uint8_t *kcb = a.kcodes + kg * a.ldk * a.kcb;
   const uint8_t *ksb = a.ksigns + kg * a.ldk * a.ksb;
   const float *knb = a.knorms + kg * a.ldk, *krb = a.krnorms + kg * a.ldk;
-  const uint8_t *vcb = a.vcodes + kg * a.ldk * a.vcb;
+  const uint8_t *vcbp = a.vcodes + kg * a.ldk * a.vcb;
   const float *vnb = a.vnorms + kg * a.ldk;
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-  {
-    const int vw = a.vw, np = 1 << (2 * vw);
-    __shared__ float lut[16];
-    if (tid < 16) lut[tid] = a.vc[tid & 15];
-    __syncthreads();
-    for (int i = tid; i < np; i += NT) lut2[i] = make_float2(lut[i & ((1 << vw) - 1)], lut[i >> vw]);
-  }
-  for (int i = tid; i < (NT / 64) * 4 * 128; i += NT) (&accs[0][0][0])[i] = 0.f;
-
-  // registers of the chunk in flight: key words per 16-key subtile; key norms
-  // one per lane (lane l: key l of each of the wave's two 64-key tiles),
-  // handed to the lanes that need them by cross-lane reads
+  // registers of the wave's tokens in flight: key words per 16-key subtile,
+  // key norms one per lane (handed out by cross-lane reads), the value
+  // records of the wave's two 64-token blocks (VR 16-byte units per lane)
+  // and the value norms of tokens lane and lane + 64
   KW kw[2][4];
-  float knu[2], kga[2];
+  float knu[2], kga[2], vn[2];
   u32x4 vr[VR];
-  float vn[CH / NT];
+  const int vunits = 4 * vcb;                        // 16-byte units of a 64-token block
   auto issue = [&](int c) {
     // 32-bit offsets from the group's base pointers (the host checks that a
     // group's records span less than 4 GB) keep the address math short
-    const int tbeg = c * CH, tlast = (int)T - 1;
+    const int tlast = (int)T - 1;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
+      const int tb = c * CH + (wv + 4 * tt) * 64;   // first token of the block
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t t = (uint32_t)min(tbeg + (wv + 4 * tt) * 64 + 16 * s + col, tlast);
+        const uint32_t t = (uint32_t)min(tb + 16 * s + col, tlast);
         const uint8_t *cp = kcb + (t * (CB16 * 16) + (uint32_t)grp * (CB16 * 4));
         const uint8_t *sp = ksb + (t * (SB16 * 16) + (uint32_t)grp * (SB16 * 4));
 #pragma unroll
@@ -124,46 +194,54 @@ attend_partial_kernel(AttArgs a) {
 #pragma unroll
         for (int i = 0; i < SB16; ++i) kw[tt][s].sw[i] = key_word<true>(reinterpret_cast<const uint32_t *>(sp + 4 * i));
       }
-      const uint32_t tl = (uint32_t)min(tbeg + (wv + 4 * tt) * 64 + lane, tlast);
+      const uint32_t tl = (uint32_t)min(tb + lane, tlast);
       knu[tt] = load_f32(knb, tl);
       kga[tt] = load_f32(krb, tl);
+      vn[tt] = vnb[tl];
+      // value records: clamped 16-byte units (units past the cache end
+      // repeat the last real one; their tokens get zero weight)
+      const int tbc = min(tb, tlast);              // a block past the cache end reads its last token
+      const uint32_t lim = (uint32_t)(min(64, (int)T - tbc) * (vcb / 16)) - 1u;
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(vcbp + (uint32_t)tbc * vcb);
+#pragma unroll
+      for (int b = 0; b < VR / 2; ++b)
+        if (b * 64 < vunits) vr[tt * (VR / 2) + b] = __builtin_nontemporal_load(src + min((uint32_t)(b * 64 + lane), lim));
     }
-    // value codes: clamped 16-byte units (units past the cache end repeat the
-    // last real one and are never read back)
-    const uint32_t lim = (uint32_t)(min(CH, (int)T - tbeg) * (VR / 2)) - 1u;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(vcb + (uint32_t)tbeg * (VR * 8));
-#pragma unroll
-    for (int b = 0; b < VR; ++b) vr[b] = __builtin_nontemporal_load(src + min((uint32_t)(b * NT + tid), lim));
-#pragma unroll
-    for (int b = 0; b < CH / NT; ++b) vn[b] = vnb[(uint32_t)min(tbeg + b * NT + tid, tlast)];
   };
 
-  // value-stream geometry: lanes own 8 rotated coordinates (one byte run of a
-  // record); token streams are split across lane groups and waves
-  // (d <= 128: at least 4 streams fit in a wave; 16 streams per block)
-  constexpr int SPW = 4, NSTREAM = SPW * (NT / 64);
-  const int lpt = d / 8;
-  const int stream = lane / lpt, j = lane - stream * lpt;
-  const bool active = stream < SPW;
-  const int sid = wv * SPW + stream;
-  const int vw = a.vw, boff = j * vw;
-  const int dw0 = boff >> 2, sh = 8 * (boff & 3);
+  // B operand masks of the value sum: lane group g takes bits 4 (g & 1) + e
+  // of each byte of its plane word (dword e of the operand)
+  const int vhalf = grp & 1;
+  const uint32_t bm0 = 0x01010101u << (4 * vhalf), bm1 = bm0 << 1, bm2 = bm0 << 2, bm3 = bm0 << 3;
+  auto vplanes = [&](uint32_t w) { return i32x4{(int)(w & bm0), (int)(w & bm1), (int)(w & bm2), (int)(w & bm3)}; };
+  // within-wave ordering of LDS accesses between lanes (the waves never wait
+  // for each other)
+  // (the LDS executes a wave's instructions in order, so the compiler only
+  // has to keep the accesses on their side of this point)
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 
   float M[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};
-  float acc[4][8];
+  float *vac = &L.vacc[grp][col];                  // coordinate 16 ct + col of head grp: vac[16 ct]
 #pragma unroll
-  for (int h = 0; h < 4; ++h)
+  for (int ct = 0; ct < 8; ++ct) vac[16 * ct] = 0.f;
+  int pr0[VW];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  for (int p = 0; p < VW; ++p) pr0[p] = plane_index(col * VW + p);
+  // A operand of the value sum: lane (row m = 4 h + digit, group g) holds, at
+  // dword e and byte b, digit (m & 3) of head (m >> 2) for the wave's token
+  // 64 tt + 32 (g >> 1) + 8 b + 4 (g & 1) + e, negated for bit 7 (B byte -128)
+  const int ah = col >> 2, ash = 21 - 7 * (col & 3);
 
   issue(c_begin);
   for (int c = c_begin; c < c_end; ++c) {
     const int64_t tbeg = (int64_t)c * CH;
-    const int nval = (int)min((int64_t)CH, T - tbeg);
-    // ---- A: logits of the chunk; value codes and norms to LDS
-    // all eight 16-key logits first (independent MFMA chains interleave),
-    // then the stores
+    // ---- A: logits of the wave's tokens into LDS; value records staged
     float lg[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -177,137 +255,198 @@ attend_partial_kernel(AttArgs a) {
         lg[tt][s] = tile_logit<CB16, SB16, W>(A, kw[tt][s], nu, ga, a.alpha, hc, pm);
         __asm__ volatile("" : "+v"(lg[tt][s]));
       }
+    float mz = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int tl = (wv + 4 * tt) * 64 + 16 * s + col;
-        zt[tl][grp] = tl < nval ? a.scale * lg[tt][s] : -INFINITY;
+        const int64_t t = tbeg + (wv + 4 * tt) * 64 + 16 * s + col;
+        const float z = t < T ? a.scale * lg[tt][s] : -INFINITY;
+        L.zt[tt * 64 + 16 * s + col][grp] = z;
+        mz = fmaxf(mz, z);
+        if (a.logits && head < a.qpg && t < T) a.logits[(kg * a.qpg + head) * T + t] = lg[tt][s];
       }
-    if (a.logits && head < a.qpg) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int tl = (wv + 4 * tt) * 64 + 16 * s + col;
-          if (tl < nval) a.logits[(kg * a.qpg + head) * T + tbeg + tl] = lg[tt][s];
-        }
-    }
-#pragma unroll
-    for (int b = 0; b < VR; ++b)
-      reinterpret_cast<u32x4 *>(vbytes)[b * NT + tid] = vr[b];
-#pragma unroll
-    for (int b = 0; b < CH / NT; ++b) vnu[b * NT + tid] = b * NT + tid < nval ? vn[b] : 0.f;
+      for (int b = 0; b < VR / 2; ++b)
+        if (b * 64 + lane < vunits) reinterpret_cast<u32x4 *>(L.vrec)[tt * vunits + b * 64 + lane] = vr[tt * (VR / 2) + b];
+    const float vnl0 = vn[0], vnl1 = vn[1];
+    const bool v0 = tbeg + wv * 64 + lane < T, v1 = tbeg + (wv + 4) * 64 + lane < T;
     if (c + 1 < c_end) issue(c + 1);
-    __syncthreads();
+    wave_sync();
 
-    // ---- B: chunk max, new running max, weights w_t = exp(z_t - M) nu_t
+    // ---- B: the wave's running max per head (row grp of every lane holds
+    // head grp), rescale factors; plane words of the staged value records;
+    // fixed-point weights
+    mz = row_max(mz);
     float f[4];
-    {
-      const float4 z0 = *reinterpret_cast<const float4 *>(&zt[tid][0]);
-      const float4 z1 = *reinterpret_cast<const float4 *>(&zt[tid + NT][0]);
-      const float mx[4] = {fmaxf(z0.x, z1.x), fmaxf(z0.y, z1.y), fmaxf(z0.z, z1.z), fmaxf(z0.w, z1.w)};
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float t = wave_max(mx[h]);
-        if (lane == 0) red[h][wv] = t;
-      }
-      __syncthreads();
-      float p0[4], p1[4];
-      const float za[4] = {z0.x, z0.y, z0.z, z0.w}, zb[4] = {z1.x, z1.y, z1.z, z1.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        float mc = red[h][0];
-#pragma unroll
-        for (int i = 1; i < NT / 64; ++i) mc = fmaxf(mc, red[h][i]);
-        const float mn = fmaxf(M[h], mc);
-        f[h] = M[h] == -INFINITY ? 0.f : __expf(M[h] - mn);
-        M[h] = mn;
-        p0[h] = __expf(za[h] - mn);
-        p1[h] = __expf(zb[h] - mn);
-        lsum[h] = fmaf(lsum[h], f[h], p0[h] + p1[h]);
-      }
-      const float n0 = vnu[tid], n1 = vnu[tid + NT];
-      *reinterpret_cast<float4 *>(&zt[tid][0]) = make_float4(p0[0] * n0, p0[1] * n0, p0[2] * n0, p0[3] * n0);
-      *reinterpret_cast<float4 *>(&zt[tid + NT][0]) = make_float4(p1[0] * n1, p1[1] * n1, p1[2] * n1, p1[3] * n1);
+    for (int h = 0; h < 4; ++h) {
+      const float mc = lane_f(mz, 16 * h);
+      const float mn = fmaxf(M[h], mc);
+      f[h] = M[h] == -INFINITY ? 0.f : __expf(M[h] - mn);
+      M[h] = mn;
+      lsum[h] *= f[h];
     }
-    __syncthreads();
-
-    // ---- C: rescale the accumulators, add this chunk's weighted centroids
+    // weights w = exp(z - M) nu <= numax, in units of numax / 127: u = w S,
+    // S = 127 / numax, so u <= 127.  The A operand carries u 2^-j (the B byte
+    // of bit j of a plane word is 2^j) as four base-128 digits: the bits of
+    // U = u 2^(21 - j), an integer below 2^28.
+    const float numax = wave_max(fmaxf(v0 ? vnl0 : 0.f, v1 ? vnl1 : 0.f));
+    const float S = numax > 0.f ? 127.f / numax : 1.f;
+    {
+      // lane (record dword k, 32-token block beta) transposes dword k of 32
+      // tokens.  Word i is read from token (i + 3 beta) mod 32 (so that the
+      // lanes spread over the LDS banks) and the transposed words are rotated
+      // back.
+      const int ntr = nd * (WT / 32);
+      if (lane < ntr) {
+        const int k = lane % nd, beta = lane / nd, rot = (3 * beta) & 31;
+        uint32_t x[32];
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
+        for (int i = 0; i < 32; ++i) x[i] = L.vrec[(32 * beta + ((i + rot) & 31)) * nd + k];
+        transpose32(x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= f[h];
-    if (active) {
-      // every token of the chunk: past nval the weights are 0 and the staged
-      // codes are copies of real ones; a fixed trip count lets the LDS reads
-      // of several tokens be in flight together
-#pragma unroll 4
-      for (int k = 0; k < CH / NSTREAM; ++k) {
-        const int t = sid + NSTREAM * k;
-        const uint32_t *rec = reinterpret_cast<const uint32_t *>(vbytes + t * a.vcb);
-        const uint32_t bits = __builtin_amdgcn_alignbit(rec[dw0 + 1], rec[dw0], sh);
-        const float4 wq = *reinterpret_cast<const float4 *>(&zt[t][0]);
+        for (int i = 0; i < 8; ++i) {
+          u32x4 v;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float2 cv = lut2[__builtin_amdgcn_ubfe(bits, e * vw, 2 * vw)];
-          acc[0][e] = fmaf(wq.x, cv.x, acc[0][e]);
-          acc[1][e] = fmaf(wq.y, cv.x, acc[1][e]);
-          acc[2][e] = fmaf(wq.z, cv.x, acc[2][e]);
-          acc[3][e] = fmaf(wq.w, cv.x, acc[3][e]);
-          acc[0][e + 1] = fmaf(wq.x, cv.y, acc[0][e + 1]);
-          acc[1][e + 1] = fmaf(wq.y, cv.y, acc[1][e + 1]);
-          acc[2][e + 1] = fmaf(wq.z, cv.y, acc[2][e + 1]);
-          acc[3][e + 1] = fmaf(wq.w, cv.y, acc[3][e + 1]);
+          for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_alignbit(x[4 * i + e], x[4 * i + e], (32 - rot) & 31);
+          *reinterpret_cast<u32x4 *>(&L.tpl[beta * TSTR + plane_index(32 * k + 4 * i)]) = v;
         }
       }
     }
-    __syncthreads();      // zt, vbytes and red are rewritten by the next chunk
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = tt * 64 + lane;
+      const float4 z4 = *reinterpret_cast<const float4 *>(&L.zt[t][0]);
+      const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
+      const float sc = (tt ? vnl1 : vnl0) * S * __builtin_amdgcn_ldexpf(1.f, 21 - (lane & 7));
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        // 0 for masked tokens (z = -inf; M is -inf too while none of the
+        // wave's tokens has been real)
+        const float pz = zz[h] == -INFINITY ? 0.f : __expf(zz[h] - M[h]);
+        lsum[h] += pz;
+        L.ufix[h * UST + uidx(t)] = (uint32_t)rintf(pz * sc);
+      }
+    }
+    wave_sync();
+
+    // ---- C: the value sum of the wave's 128 tokens on int8 MFMA
+    {
+      const float fg = grp == 0 ? f[0] : grp == 1 ? f[1] : grp == 2 ? f[2] : f[3];
+      const float invS = 1.f / S;
+      i32x4 Aw[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int tb = tt * 64 + 32 * (grp >> 1) + 4 * (grp & 1);
+        uint32_t dw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const u32x4 u = *reinterpret_cast<const u32x4 *>(&L.ufix[ah * UST + uidx(tb + 8 * b)]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dw[e] |= __builtin_amdgcn_ubfe(u[e], ash, 7) << (8 * b);
+        }
+        // bytes of bit 7 (dword 3 of the odd lane groups) negated bytewise
+        if (grp & 1) dw[3] = (0x80808080u - dw[3]) ^ 0x80808080u;
+        Aw[tt] = i32x4{(int)dw[0], (int)dw[1], (int)dw[2], (int)dw[3]};
+      }
+      // W = sum of the weights (all-ones B), the offset of every plane, as
+      // digit pairs; K = sum of the plane coefficients
+      const i32x4 ones = vplanes(0xffffffffu);
+      i32x4 accW = mfma8(Aw[0], ones, i32x4{0, 0, 0, 0});
+      accW = mfma8(Aw[1], ones, accW);
+      float K = 0.f;
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) K += a.vbasis[pl];
+      const float KWh = K * (float)(accW[0] * 128 + accW[1]), KWl = K * (float)(accW[2] * 128 + accW[3]);
+      const uint32_t *tw0 = &L.tpl[(grp >> 1) * TSTR];
+      const uint32_t *tw1 = &L.tpl[(2 + (grp >> 1)) * TSTR];
+      // fixed trip count (the tiles past d are skipped) so that the MFMAs of
+      // one tile overlap the recombination of the previous one
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        if (ct >= nct) break;
+        // bit rows of coordinate 16 ct + col.  Rows past the record hold no
+        // bit of a real coordinate: they only reach coordinates >= d, whose
+        // sums are never used, and lie inside the row (16 nct VW <= NPMAX)
+        int pr[VW];
+#pragma unroll
+        for (int p = 0; p < VW; ++p) pr[p] = pr0[p] + (16 * VW + 4) * ct;
+        i32x4 pacc[NPL];
+#pragma unroll
+        for (int pl = 0; pl < NPL; ++pl) pacc[pl] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const uint32_t *tw = tt ? tw1 : tw0;
+          uint32_t pw[VW];
+#pragma unroll
+          for (int p = 0; p < VW; ++p) pw[p] = tw[pr[p]];
+#pragma unroll
+          for (int p = 0; p < VW; ++p) pacc[p] = mfma8(Aw[tt], vplanes(pw[p]), pacc[p]);
+          if constexpr (VW == 3) {
+            pacc[3] = mfma8(Aw[tt], vplanes(pw[0] ^ pw[1] ^ pw[2]), pacc[3]);
+          } else if constexpr (VW == 4) {
+            pacc[4] = mfma8(Aw[tt], vplanes(pw[0] ^ pw[1] ^ pw[2]), pacc[4]);
+            pacc[5] = mfma8(Aw[tt], vplanes(pw[0] ^ pw[1] ^ pw[3]), pacc[5]);
+            pacc[6] = mfma8(Aw[tt], vplanes(pw[0] ^ pw[2] ^ pw[3]), pacc[6]);
+            pacc[7] = mfma8(Aw[tt], vplanes(pw[1] ^ pw[2] ^ pw[3]), pacc[7]);
+          }
+        }
+        // sum_P A_P (2 V_P - W): digit pairs (d0 * 128 + d1, d2 * 128 + d3) of
+        // every plane are exact in int32 and in fp32 (below 2^23)
+        float sh = 0.f, sl = 0.f;
+#pragma unroll
+        for (int pl = 0; pl < NPL; ++pl) {
+          sh = fmaf(a.vbasis[pl], (float)(pacc[pl][0] * 128 + pacc[pl][1]), sh);
+          sl = fmaf(a.vbasis[pl], (float)(pacc[pl][2] * 128 + pacc[pl][3]), sl);
+        }
+        const float v = fmaf(fmaf(2.f, sl, -KWl), 0x1.0p-21f, fmaf(2.f, sh, -KWh) * 0x1.0p-7f);
+        vac[16 * ct] = fmaf(v, invS, vac[16 * ct] * fg);
+      }
+    }
+    wave_sync();          // the wave's zt, vrec, tpl and ufix are rewritten for its next tokens
   }
 
-  // ---- D: block totals: sums over threads, accumulators over token streams
+  // ---- D: merge the four waves' softmax states: every wave's sums are
+  // rescaled to the block max of each head
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     const float t = wave_sum(lsum[h]);
-    if (lane == 0) red[h][wv] = t;
-  }
-  const bool by_group = (lpt == 16);          // d == 128: the 4 streams are the 4 lane groups
-  if (by_group) {
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = acc[h][e];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[h][e] = v;
-      }
-  }
-  if (active && (!by_group || stream == 0)) {
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (by_group) accs[wv][h][8 * j + e] = acc[h][e];
-        else atomicAdd(&accs[wv][h][8 * j + e], acc[h][e]);
-      }
+    if (lane == 0) {
+      fin[wv][h][0] = M[h];
+      fin[wv][h][1] = t;
+    }
   }
   __syncthreads();
   float *out = a.part + (gidx * a.nsplit + blockIdx.x) * 4 * (d + 2);
   for (int i = tid; i < 4 * d; i += NT) {
     const int h = i / d, cc = i - h * d;
+    float mb = fin[0][h][0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) mb = fmaxf(mb, fin[w][h][0]);
     float v = 0.f;
 #pragma unroll
-    for (int s = 0; s < NT / 64; ++s) v += accs[s][h][cc];
+    for (int w = 0; w < NT / 64; ++w) {
+      const float mw = fin[w][h][0];
+      v += mw == -INFINITY ? 0.f : wl[w].vacc[h][cc] * __expf(mw - mb);
+    }
     out[h * (d + 2) + cc] = v;
   }
   if (tid < 4) {
+    const int h = tid;
+    float mb = fin[0][h][0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) mb = fmaxf(mb, fin[w][h][0]);
     float l = 0.f;
 #pragma unroll
-    for (int i = 0; i < NT / 64; ++i) l += red[tid][i];
-    const float mt = tid == 0 ? M[0] : tid == 1 ? M[1] : tid == 2 ? M[2] : M[3];
-    out[tid * (d + 2) + d] = mt;
-    out[tid * (d + 2) + d + 1] = l;
+    for (int w = 0; w < NT / 64; ++w) {
+      const float mw = fin[w][h][0];
+      l += mw == -INFINITY ? 0.f : fin[w][h][1] * __expf(mw - mb);
+    }
+    out[h * (d + 2) + d] = mb;
+    out[h * (d + 2) + d + 1] = l;
   }
 }
 
@@ -396,17 +535,16 @@ __global__ void __launch_bounds__(256) attend_probs_kernel(const float *logits, 
 }
 
 // Key geometries d <= 128 produces (one sign word per lane group) x value
-// code sizes 16, 32, 48, 64 bytes.
-int dispatch(const AttArgs &a, dim3 grid, int cb16, int sb16, int w, hipStream_t s) {
-  const int vr = a.vcb / 8;
+// code widths 1..4.
+int dispatch(const AttArgs &a, dim3 grid, int cb16, int sb16, int w, int vw, hipStream_t s) {
 #define TQ_CASE_V(C, S, W_, V)                                         \
-  if (vr == V) {                                                       \
+  if (vw == V) {                                                       \
     attend_partial_kernel<C, S, W_, V><<<grid, NT, 0, s>>>(a);         \
     return hip_status();                                               \
   }
 #define TQ_CASE(C, S, W_)                                              \
   if (cb16 == C && sb16 == S && w == W_) {                             \
-    TQ_CASE_V(C, S, W_, 2) TQ_CASE_V(C, S, W_, 4) TQ_CASE_V(C, S, W_, 6) TQ_CASE_V(C, S, W_, 8) \
+    TQ_CASE_V(C, S, W_, 1) TQ_CASE_V(C, S, W_, 2) TQ_CASE_V(C, S, W_, 3) TQ_CASE_V(C, S, W_, 4) \
     return TQ_ENOTSUP;                                                 \
   }
   TQ_CASE(1, 1, 1) TQ_CASE(1, 1, 2) TQ_CASE(2, 1, 2) TQ_CASE(1, 1, 3) TQ_CASE(2, 1, 3) TQ_CASE(3, 1, 3)
@@ -431,8 +569,8 @@ size_t attend_ws_bytes(const tq_ctx *k, int64_t G, int qpg, int64_t T) {
 int check_attend(const tq_ctx *kc, const tq_ctx *vc, int64_t G, int qpg, int64_t T, int64_t ldk,
                  bool want_probs) {
   const int d = kc->hp.d;
-  if (d > 128 || d % 16 != 0) return TQ_ENOTSUP;       // value path: 8 coordinates per lane
-  if (vc->code_bytes > VB_MAX || (vc->code_bytes * CH) % 16 != 0) return TQ_ENOTSUP;
+  if (d > 128) return TQ_ENOTSUP;                      // the fused kernel holds 8 coordinate tiles
+  if (vc->hp.w < 1 || vc->hp.w > 4 || vc->code_bytes > 16 * vc->hp.w) return TQ_ENOTSUP;
   const int64_t groups = G * ((qpg + 3) / 4);
   if (groups > 65535 || T > 0x7fffffff - CH || G * qpg > 0x7fffffff) return TQ_ENOTSUP;
   const int64_t rec_max = std::max<int64_t>(std::max(kc->code_bytes, kc->sign_bytes), vc->code_bytes);
@@ -489,11 +627,10 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   a.kcb = kc->code_bytes;
   a.ksb = kc->sign_bytes;
   a.vcb = vc->code_bytes;
-  a.vw = vc->hp.w;
   a.alpha = kc->alpha;
   a.scale = scale;
-  for (int i = 0; i < 16; ++i) a.vc[i] = vc->cf[i];
-  st = dispatch(a, dim3((unsigned)a.nsplit, (unsigned)groups), cb16, sb16, w, stream);
+  for (int i = 0; i < 8; ++i) a.vbasis[i] = vc->vbasis[i];
+  st = dispatch(a, dim3((unsigned)a.nsplit, (unsigned)groups), cb16, sb16, w, vc->hp.w, stream);
   if (st != TQ_OK) return st;
   CombArgs c{};
   c.part = part;

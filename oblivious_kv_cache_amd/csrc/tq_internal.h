@@ -42,6 +42,7 @@ struct tq_ctx {
   float tpos[8] = {};  // positive thresholds t_{L/2 + j}
   float cf[16] = {};   // all centroids, fp32
   float basis[4] = {}; // odd-basis coefficients of the codebook (see tq_scores.hip)
+  float vbasis[8] = {}; // all odd monomials of up to 4 code bits: w singles, then triples
   // device constants (one allocation owned by the context)
   void *dmem = nullptr;
   float *Pi32 = nullptr;    // [d][d] row-major
