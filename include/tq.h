@@ -72,6 +72,7 @@ extern "C" {
 /* modes */
 #define TQ_MODE_PROD 0     /* (bits-1)-bit codes + 1-bit QJL sketch, m = d */
 #define TQ_MODE_MSE  1     /* bits-bit codes only (no sketch)              */
+#define TQ_MODE_POLAR 2    /* bits-bit codes of the recursive polar angles  */
 
 /* ops for tq_workspace_size */
 #define TQ_OP_SCORES  1
@@ -112,6 +113,27 @@ int tq_init(int d, int bits, uint64_t seed, tq_ctx **out);
 /* Same, MSE-only mode: 2^bits levels, no sketch; bits in {1,2,3,4}. */
 int tq_init_mse(int d, int bits, uint64_t seed, tq_ctx **out);
 
+/* PolarQuant context (MSE-only stage; xujun.org note 189244, 第一步：PolarQuant;
+ * suzuke blog, 第二步): y = Pi x / |x| is written in recursive polar
+ * coordinates -- level 1 pairs coordinates (2i, 2i+1) into (radius, angle in
+ * [0, 2 pi)), every further level pairs two radii into (radius, angle in
+ * [0, pi/2]), down to the radius |y| = 1 -- and each of the d - 1 angles takes
+ * a bits-bit code from its level's Lloyd-Max codebook (level 1: uniform
+ * cells; level l >= 2: the law with sin^2 ~ Beta(k/2, k/2), k = 2^(l-1)).
+ * d in {32, 64, 128, 256}, bits in {1,2,3,4}.  Records: d slots of bits bits
+ * (code_bytes = roundup16(d bits / 8)) + the float32 length; slots
+ * [q d/4, (q+1) d/4) hold the subtree of coordinate quarter q level by level,
+ * then a spare slot holding the top angle (q = 0), the level log2(d)-1 angle
+ * of quarters 0/1 (q = 1) or 2/3 (q = 2), or zero (q = 3).  Such a context
+ * takes tq_quantize (signs and rnorms NULL) and tq_dequant; the estimator
+ * calls (tq_scores, tq_attend, tq_topk, decode steps) return TQ_EINVAL. */
+int tq_init_polar(int d, int bits, uint64_t seed, tq_ctx **out);
+
+/* Host-only: the float64 angle codebooks a PolarQuant context holds, per level
+ * l = 1..log2(d): c [log2 d][2^bits] centroids, t [log2 d][2^bits - 1]
+ * thresholds (radians).  Either pointer may be NULL. */
+int tq_polar_codebook(int d, int bits, double *c, double *t);
+
 /* Release a context (NULL is a no-op). */
 void tq_free(tq_ctx *ctx);
 
@@ -121,11 +143,14 @@ int tq_layout(const tq_ctx *ctx, tq_layout_t *out);
 /* Host-only: compute the float64 parameters a context would hold, without a
  * GPU.  Pi [d*d] row-major, S [m*d] row-major (prod mode), c [2^w] ascending
  * centroids, t [2^w - 1] ascending thresholds (already scaled by 1/sqrt(d)).
- * Any output pointer may be NULL.  mode = TQ_MODE_PROD or TQ_MODE_MSE. */
+ * Any output pointer may be NULL.  mode = TQ_MODE_PROD or TQ_MODE_MSE (else
+ * TQ_EINVAL; see tq_polar_codebook for PolarQuant). */
 int tq_host_params(int d, int bits, uint64_t seed, int mode,
                    double *Pi, double *S, double *c, double *t);
 
-/* Host copies of a context's float64 parameters (any pointer may be NULL). */
+/* Host copies of a context's float64 parameters (any pointer may be NULL);
+ * for a PolarQuant context c and t are the per-level angle codebooks of
+ * tq_polar_codebook (log2(d) x 2^bits and log2(d) x (2^bits - 1) doubles). */
 int tq_get_params(const tq_ctx *ctx, double *Pi, double *S, double *c, double *t);
 
 /* Quantize n vectors (online append: any n >= 0).

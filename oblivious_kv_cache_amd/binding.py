@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(_HERE, "lib", "libtq.so"
 TQ_OK, TQ_EINVAL, TQ_ENOTSUP, TQ_ENOMEM, TQ_EHIP, TQ_ESCRATCH = 0, -1, -2, -3, -4, -5
 TQ_SCRATCH_BYTES = 16 << 20
 TQ_F32, TQ_BF16 = 0, 1
-TQ_MODE_PROD, TQ_MODE_MSE = 0, 1
+TQ_MODE_PROD, TQ_MODE_MSE, TQ_MODE_POLAR = 0, 1, 2
 TQ_OP_SCORES, TQ_OP_ATTEND, TQ_OP_TOPK = 1, 2, 3
 TQ_MAX_D, TQ_MAX_TOPK = 256, 64
 
@@ -26,7 +26,7 @@ EXPORTS = [
     "tq_quantize", "tq_workspace_size", "tq_scores", "tq_prep_queries", "tq_scores_prepared",
     "tq_scores_prepared_timed",
     "tq_softmax", "tq_attend", "tq_decode_prep", "tq_decode_step", "tq_dequant", "tq_topk",
-    "tq_scores_static", "tq_strerror",
+    "tq_scores_static", "tq_init_polar", "tq_polar_codebook", "tq_strerror",
 ]
 
 
@@ -62,6 +62,8 @@ def _load():
     sig = {
         "tq_init": (I, [I, I, U64, ctypes.POINTER(P)]),
         "tq_init_mse": (I, [I, I, U64, ctypes.POINTER(P)]),
+        "tq_init_polar": (I, [I, I, U64, ctypes.POINTER(P)]),
+        "tq_polar_codebook": (I, [I, I, D, D]),
         "tq_free": (None, [P]),
         "tq_layout": (I, [P, ctypes.POINTER(tq_layout_t)]),
         "tq_host_params": (I, [I, I, U64, I, D, D, D, D]),
@@ -189,12 +191,23 @@ def tq_host_params(d, bits, seed, mode=TQ_MODE_PROD):
     return Pi, S[:m], c, t
 
 
+def tq_polar_codebook(d, bits):
+    """Host-only float64 angle codebooks of a PolarQuant context: (c [L, 2^bits],
+    t [L, 2^bits - 1]) for levels 1..L = log2(d)."""
+    import numpy as np
+    L = max(int(d).bit_length() - 1, 1)
+    c = np.zeros((L, 2 ** bits))
+    t = np.zeros((L, max(2 ** bits - 1, 1)))
+    _check(LIB.tq_polar_codebook(int(d), int(bits), _dp(c), _dp(t)), "tq_polar_codebook")
+    return c, t[:, : 2 ** bits - 1]
+
+
 class Context:
     """Owns a ``tq_ctx *`` (device constants for one (d, bits, seed, mode))."""
 
     def __init__(self, d, bits, seed=0, mode=TQ_MODE_PROD):
         h = ctypes.c_void_p()
-        fn = LIB.tq_init if mode == TQ_MODE_PROD else LIB.tq_init_mse
+        fn = {TQ_MODE_PROD: LIB.tq_init, TQ_MODE_MSE: LIB.tq_init_mse, TQ_MODE_POLAR: LIB.tq_init_polar}[mode]
         _check(fn(int(d), int(bits), int(seed), ctypes.byref(h)), "tq_init")
         self.handle = h
         lay = tq_layout_t()
@@ -218,9 +231,13 @@ class Context:
     def params(self):
         import numpy as np
         d, m, L = self.d, self.m, 2 ** self.w
-        Pi, S, c, t = np.zeros((d, d)), np.zeros((max(m, 1), d)), np.zeros(L), np.zeros(L - 1)
+        nl = d.bit_length() - 1 if self.mode == TQ_MODE_POLAR else 1   # polar: a codebook per level
+        Pi, S = np.zeros((d, d)), np.zeros((max(m, 1), d))
+        c, t = np.zeros(nl * L), np.zeros(max(nl * (L - 1), 1))
         _check(LIB.tq_get_params(self.handle, _dp(Pi), _dp(S), _dp(c), _dp(t)), "tq_get_params")
-        return Pi, S[:m], c, t
+        if self.mode == TQ_MODE_POLAR:
+            return Pi, S[:m], c.reshape(nl, L), t[: nl * (L - 1)].reshape(nl, L - 1)
+        return Pi, S[:m], c, t[: L - 1]
 
     def workspace(self, op, a, b, c=0, device="cuda"):
         n = ctypes.c_size_t()

@@ -142,7 +142,13 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
   const size_t nfr = (size_t)(dpad / 16) * (dpad / 32) * 64;
   const size_t bytes_f32 = sizeof(float) * ((size_t)2 * d * d + (size_t)2 * m * d);
   const size_t bytes_fr = sizeof(Frag) * nfr * (m ? 4 : 2);
-  const size_t total = (bytes_f32 + 255) / 256 * 256 + bytes_fr;
+  // polar mode: per level, the angle thresholds [L][levels-1] and the
+  // (cos, sin) of the angle centroids [L][levels][2], float32
+  const bool polar = mode == TQ_MODE_POLAR;
+  const int nlev = polar ? (int)std::lround(std::log2((double)d)) : 0;
+  const size_t n_thr = polar ? (size_t)nlev * (L - 1) : 0, n_cs = polar ? (size_t)nlev * L * 2 : 0;
+  const size_t bytes_pol = sizeof(float) * (n_thr + n_cs);
+  const size_t total = (bytes_f32 + 255) / 256 * 256 + bytes_fr + bytes_pol;
   std::vector<uint8_t> host(total, 0);
   float *Pi32 = reinterpret_cast<float *>(host.data());
   float *PiT32 = Pi32 + (size_t)d * d;
@@ -170,6 +176,14 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
       }
     build_frags(hp, dpad, Sp.data(), m, d, true, fr + 2 * nfr, fr + 3 * nfr);
   }
+  float *pol = reinterpret_cast<float *>(host.data() + (bytes_f32 + 255) / 256 * 256 + bytes_fr);
+  if (polar) {
+    for (size_t i = 0; i < n_thr; ++i) pol[i] = (float)hp.t[i];
+    for (size_t i = 0; i < (size_t)nlev * L; ++i) {
+      pol[n_thr + 2 * i] = (float)std::cos(hp.c[i]);
+      pol[n_thr + 2 * i + 1] = (float)std::sin(hp.c[i]);
+    }
+  }
   if (hipMalloc(&ctx->dmem, total) != hipSuccess) {
     (void)hipGetLastError();
     delete ctx;
@@ -191,6 +205,10 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
   if (m) {
     ctx->S2A_hi = dfr + 2 * nfr;
     ctx->S2A_lo = dfr + 3 * nfr;
+  }
+  if (polar) {
+    ctx->polar_thr = reinterpret_cast<float *>(base + (bytes_f32 + 255) / 256 * 256 + bytes_fr);
+    ctx->polar_cs = ctx->polar_thr + n_thr;
   }
   // the static scratch buffer of this device is located once, at init
   if (tq::scratch_attach(ctx->device) == nullptr) {
@@ -233,6 +251,19 @@ int tq_init_mse(int d, int bits, uint64_t seed, tq_ctx **out) {
   return make_ctx(d, bits, seed, TQ_MODE_MSE, out);
 }
 
+int tq_init_polar(int d, int bits, uint64_t seed, tq_ctx **out) {
+  return make_ctx(d, bits, seed, TQ_MODE_POLAR, out);
+}
+
+int tq_polar_codebook(int d, int bits, double *c, double *t) {
+  tq::HostParams hp;
+  const int st = tq::build_host_params(d, bits, 0, TQ_MODE_POLAR, hp);
+  if (st != TQ_OK) return st;
+  if (c) std::memcpy(c, hp.c.data(), hp.c.size() * sizeof(double));
+  if (t) std::memcpy(t, hp.t.data(), hp.t.size() * sizeof(double));
+  return TQ_OK;
+}
+
 void tq_free(tq_ctx *ctx) {
   if (!ctx) return;
   if (ctx->dmem) (void)hipFree(ctx->dmem);
@@ -271,6 +302,7 @@ int tq_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t 
   if (n == 0) return TQ_OK;
   if (!x || !codes || !norms) return TQ_EINVAL;
   if (prod ? (!signs || !rnorms) : (signs || rnorms)) return TQ_EINVAL;
+  const bool polar = ctx->hp.mode == TQ_MODE_POLAR;
   if (ldx < ctx->hp.d) return TQ_EINVAL;
   if (dtype == TQ_BF16 ? (ldx % 8) : (ldx % 4)) return TQ_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || (signs && !aligned(signs, 16)) ||
@@ -278,6 +310,7 @@ int tq_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t 
     return TQ_EINVAL;
   const int st = current_device_matches(ctx);
   if (st != TQ_OK) return st;
+  if (polar) return tq::launch_polar_quantize(ctx, x, dtype, n, ldx, ldr, codes, norms, stream);
   return tq::launch_quantize(ctx, x, dtype, n, ldx, ldr, codes, signs, norms, rnorms, stream);
 }
 

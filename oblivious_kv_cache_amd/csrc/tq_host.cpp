@@ -98,7 +98,84 @@ double Phi(double x) {
   return 0.5 * std::erfc(-x * 0.70710678118654752440084436210485);
 }
 
+// Gauss-Legendre rule of n nodes on [-1, 1] (Newton iteration on P_n from
+// the Tricomi initial guesses).
+void gauss_legendre(int n, std::vector<double> &x, std::vector<double> &w) {
+  x.assign(n, 0.0);
+  w.assign(n, 0.0);
+  const double pi = 3.14159265358979323846264338327950288;
+  for (int i = 0; i < n; ++i) {
+    double z = std::cos(pi * (i + 0.75) / (n + 0.5)), dp = 1.0;
+    for (int it = 0; it < 100; ++it) {
+      double p0 = 1.0, p1 = z;
+      for (int k = 2; k <= n; ++k) {
+        const double p2 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+        p0 = p1;
+        p1 = p2;
+      }
+      dp = n * (z * p1 - p0) / (z * z - 1.0);
+      const double dz = p1 / dp;
+      z -= dz;
+      if (std::fabs(dz) < 1e-16) break;
+    }
+    x[i] = z;
+    w[i] = 2.0 / ((1.0 - z * z) * dp * dp);
+  }
+}
+
 }  // namespace
+
+// Lloyd-Max quantizer with L levels for the angle of a level-l node of the
+// recursive polar transform (l >= 2): the two child radii are lengths of
+// independent k-dimensional Gaussian vectors, k = 2^(l-1), so sin^2(phi) is
+// Beta(k/2, k/2) and phi has density 2 sin^(k-1) cos^(k-1) / B(k/2, k/2) on
+// [0, pi/2] (xujun.org note 189244, 第一步：PolarQuant: the angle laws are
+// known and concentrated; suzuke blog, 第二步: a Max-Lloyd codebook per
+// angle).  Cells are integrated by a 64-node Gauss-Legendre rule; the
+// iteration starts from evenly spaced centroids and the result is made
+// symmetric about pi/4.
+void lloyd_max_polar_angle(int level, int L, std::vector<double> &c, std::vector<double> &t) {
+  static std::vector<double> gx, gw;
+  if (gx.empty()) gauss_legendre(64, gx, gw);
+  const double half_pi = 1.57079632679489661923132169163975144;
+  const double k = std::ldexp(1.0, level - 1);
+  const double logB = 2.0 * std::lgamma(0.5 * k) - std::lgamma(k);
+  auto dens = [&](double ph) {
+    const double sn = std::sin(ph), cs = std::cos(ph);
+    if (!(sn > 0.0) || !(cs > 0.0)) return 0.0;
+    return 2.0 * std::exp((k - 1.0) * (std::log(sn) + std::log(cs)) - logB);
+  };
+  c.resize(L);
+  for (int i = 0; i < L; ++i) c[i] = (i + 0.5) * half_pi / L;
+  std::vector<double> edge(L + 1), next(L);
+  for (int it = 0; it < 100000; ++it) {
+    edge[0] = 0.0;
+    edge[L] = half_pi;
+    for (int i = 1; i < L; ++i) edge[i] = 0.5 * (c[i - 1] + c[i]);
+    double delta = 0.0;
+    for (int i = 0; i < L; ++i) {
+      const double a = edge[i], b = edge[i + 1], hw = 0.5 * (b - a), mid = 0.5 * (b + a);
+      double m0 = 0.0, m1 = 0.0;
+      for (size_t q = 0; q < gx.size(); ++q) {
+        const double ph = hw * gx[q] + mid, f = dens(ph) * gw[q];
+        m0 += f;
+        m1 += f * ph;
+      }
+      next[i] = m0 > 0.0 ? m1 / m0 : mid;
+      delta = std::fmax(delta, std::fabs(next[i] - c[i]));
+    }
+    c.swap(next);
+    if (delta < 1e-14) break;
+  }
+  for (int i = 0; i < L / 2; ++i) {            // symmetric about pi/4
+    const double a = 0.5 * (c[i] + (half_pi - c[L - 1 - i]));
+    c[i] = a;
+    c[L - 1 - i] = half_pi - a;
+  }
+  t.resize(L - 1);
+  for (int i = 0; i + 1 < L; ++i) t[i] = 0.5 * (c[i] + c[i + 1]);
+  if (L % 2 == 0) t[L / 2 - 1] = 0.5 * half_pi;
+}
 
 void lloyd_max_unit_gaussian(int L, std::vector<double> &c, std::vector<double> &t) {
   // Alternate the nearest-neighbour condition (thresholds at midpoints) and
@@ -131,7 +208,13 @@ void lloyd_max_unit_gaussian(int L, std::vector<double> &c, std::vector<double> 
 
 int build_host_params(int d, int bits, uint64_t seed, int mode, HostParams &hp) {
   if (d < 8 || d > TQ_MAX_D || d % 8 != 0) return TQ_EINVAL;
-  if (mode == TQ_MODE_PROD) {
+  if (mode == TQ_MODE_POLAR) {
+    // d a power of two of at least 32 (four lane groups of at least 8
+    // coordinates each own a subtree of the recursive transform)
+    if (d < 32 || d > 256 || (d & (d - 1)) != 0 || bits < 1 || bits > 4) return TQ_EINVAL;
+    hp.w = bits;
+    hp.m = 0;
+  } else if (mode == TQ_MODE_PROD) {
     if (bits < 2 || bits > 4) return TQ_EINVAL;
     hp.w = bits - 1;
     hp.m = d;
@@ -160,6 +243,22 @@ int build_host_params(int d, int bits, uint64_t seed, int mode, HostParams &hp) 
   if (hp.m) normals(seed, 1, hp.S.size(), hp.S.data());
 
   std::vector<double> c, t;
+  if (mode == TQ_MODE_POLAR) {
+    // per level l = 1..log2 d: level 1 uniform on [0, 2 pi) (cells of width
+    // 2 pi / 2^bits, centroids at their middles), levels >= 2 Lloyd-Max
+    const int nl = (int)std::lround(std::log2((double)d)), n = hp.levels;
+    const double two_pi = 6.283185307179586476925286766559;
+    hp.c.assign((size_t)nl * n, 0.0);
+    hp.t.assign((size_t)nl * (n - 1), 0.0);
+    for (int i = 0; i < n; ++i) hp.c[i] = (i + 0.5) * two_pi / n;
+    for (int i = 1; i < n; ++i) hp.t[i - 1] = i * two_pi / n;
+    for (int level = 2; level <= nl; ++level) {
+      lloyd_max_polar_angle(level, n, c, t);
+      for (int i = 0; i < n; ++i) hp.c[(size_t)(level - 1) * n + i] = c[i];
+      for (int i = 0; i + 1 < n; ++i) hp.t[(size_t)(level - 1) * (n - 1) + i] = t[i];
+    }
+    return TQ_OK;
+  }
   lloyd_max_unit_gaussian(hp.levels, c, t);
   const double s = 1.0 / std::sqrt((double)d);
   hp.c.resize(c.size());
@@ -173,6 +272,9 @@ int build_host_params(int d, int bits, uint64_t seed, int mode, HostParams &hp) 
 
 extern "C" int tq_host_params(int d, int bits, uint64_t seed, int mode, double *Pi, double *S,
                               double *c, double *t) {
+  // prod and MSE-only contexts (a PolarQuant context's codebooks come from
+  // tq_polar_codebook: their size differs)
+  if (mode != TQ_MODE_PROD && mode != TQ_MODE_MSE) return TQ_EINVAL;
   tq::HostParams hp;
   const int st = tq::build_host_params(d, bits, seed, mode, hp);
   if (st != TQ_OK) return st;

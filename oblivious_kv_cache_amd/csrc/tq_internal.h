@@ -15,12 +15,14 @@ struct HostParams {
   uint64_t seed = 0;
   std::vector<double> Pi;  // [d][d] row-major
   std::vector<double> S;   // [m][d] row-major
-  std::vector<double> c;   // [levels] ascending, for N(0, 1/d)
-  std::vector<double> t;   // [levels-1] ascending
+  std::vector<double> c;   // [levels] ascending, for N(0, 1/d); polar mode:
+                           // [log2 d][levels], the angle codebook of every level
+  std::vector<double> t;   // [levels-1] ascending; polar mode: [log2 d][levels-1]
 };
 
 int build_host_params(int d, int bits, uint64_t seed, int mode, HostParams &hp);
 void lloyd_max_unit_gaussian(int L, std::vector<double> &c, std::vector<double> &t);
+void lloyd_max_polar_angle(int level, int L, std::vector<double> &c, std::vector<double> &t);
 
 // 16-byte MFMA operand fragment (8 x bf16 or 16 x int8 per lane).
 struct alignas(16) Frag {
@@ -51,6 +53,8 @@ struct tq_ctx {
   float *ST32 = nullptr;    // [d][m] = S^T
   tq::Frag *PiA_hi = nullptr, *PiA_lo = nullptr;   // quantize GEMM-1 operand fragments
   tq::Frag *S2A_hi = nullptr, *S2A_lo = nullptr;   // quantize GEMM-2 operand fragments
+  float *polar_thr = nullptr;   // polar mode: angle thresholds [log2 d][levels - 1]
+  float *polar_cs = nullptr;    // polar mode: (cos, sin) of angle centroids [log2 d][levels][2]
 };
 
 namespace tq {
@@ -59,6 +63,8 @@ namespace tq {
 int launch_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t ldx,
                     int64_t ldr, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
                     hipStream_t stream);
+int launch_polar_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t ldx,
+                          int64_t ldr, uint8_t *codes, float *norms, hipStream_t stream);
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t G, int qpg);
 int launch_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,
                   const uint8_t *codes, const uint8_t *signs, const float *norms,

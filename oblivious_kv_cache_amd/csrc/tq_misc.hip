@@ -2,6 +2,11 @@
 //
 //   prod: x_hat = nu (Pi^T c[idx] + alpha gamma S^T (2 bits - 1))
 //   mse:  x_hat = nu Pi^T c[idx]
+//   polar: x_hat = nu Pi^T y_hat, y_hat the unit vector whose recursive polar
+//          angles are the codes' centroid angles: coordinate i is the product,
+//          over the levels l = 1..L of its path to the root, of the cosine
+//          (child 0) or sine (child 1, bit l-1 of i) of the angle of node
+//          i >> l (xujun.org note 189244, 第一步：PolarQuant)
 // (suzuke blog "turboquant-compressing-ai-consciousness", 技術上怎麼做到的 /
 // 第三步: the stage-1 approximation plus the residual correction).  Not on the
 // timed path: a block per vector, decoded codes staged in LDS, then a
@@ -20,7 +25,21 @@ struct DqArgs {
   int d, m, w, cb, sb;
   float alpha;
   float c[16];
+  const float *pcs;   // polar mode: (cos, sin) of the angle centroids [L][2^w][2]; else null
+  int nlev;           // polar mode: L = log2 d
 };
+
+// Record slot of the angle of node j at level l (polar layout: slots
+// [q P, (q+1) P) of quarter q, P = d/4, hold its subtree level by level, then
+// a spare slot: the top angle in quarter 0, the level L-1 angles in quarters
+// 1 and 2).
+__device__ __forceinline__ int polar_slot(int d, int L, int level, int j) {
+  const int P = d >> 2;
+  if (level == L) return P - 1;
+  if (level == L - 1) return (j + 1) * P + P - 1;
+  const int nq = P >> level, q = j / nq;
+  return q * P + (P - (P >> (level - 1))) + (j - q * nq);
+}
 
 __global__ void __launch_bounds__(256) dequant_kernel(DqArgs a) {
   __shared__ float cv[TQ_MAX_D];
@@ -28,12 +47,23 @@ __global__ void __launch_bounds__(256) dequant_kernel(DqArgs a) {
   const int tid = threadIdx.x;
   for (int64_t v = blockIdx.x; v < a.n; v += gridDim.x) {
     const uint8_t *rec = a.codes + v * a.cb;
-    if (tid < a.d) {
-      const int bit = tid * a.w, byte = bit >> 3;
+    auto code_at = [&](int slot) {
+      const int bit = slot * a.w, byte = bit >> 3;
       uint32_t word = rec[byte];
       if (byte + 1 < a.cb) word |= (uint32_t)rec[byte + 1] << 8;
-      const uint32_t idx = (word >> (bit & 7)) & ((1u << a.w) - 1u);
-      cv[tid] = a.c[idx];
+      return (word >> (bit & 7)) & ((1u << a.w) - 1u);
+    };
+    if (tid < a.d) {
+      if (a.pcs) {
+        float yv = 1.f;
+        for (int level = 1; level <= a.nlev; ++level) {
+          const uint32_t code = code_at(polar_slot(a.d, a.nlev, level, tid >> level));
+          yv *= a.pcs[(((level - 1) << a.w) + (int)code) * 2 + ((tid >> (level - 1)) & 1)];
+        }
+        cv[tid] = yv;
+      } else {
+        cv[tid] = a.c[code_at(tid)];
+      }
     }
     if (a.signs && tid < a.m) {
       const uint8_t b = a.signs[v * a.sb + (tid >> 3)];
@@ -75,6 +105,9 @@ int launch_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs
   a.sb = ctx->sign_bytes;
   a.alpha = ctx->alpha;
   for (int k = 0; k < 16; ++k) a.c[k] = ctx->cf[k];
+  a.pcs = ctx->hp.mode == TQ_MODE_POLAR ? ctx->polar_cs : nullptr;
+  a.nlev = 0;
+  while ((1 << a.nlev) < a.d) ++a.nlev;
   const int64_t blocks = n < 65536 ? n : 65536;
   dequant_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a);
   return hip_status();

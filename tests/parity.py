@@ -107,3 +107,30 @@ def check_topk(gpu_ids, gpu_scores, oracle_scores, k):
         kth = ref_vals[qi][-1]
         for i in set(g.tolist()) ^ set(ref_ids[qi].tolist()):
             assert abs(sc[i] - kth) <= TK_ATOL + TK_RTOL * abs(kth), (qi, i, sc[i], kth)
+
+
+def check_polar(p, gpu, X, allow_frac=MAX_FRAC):
+    """PolarQuant records against the oracle (oracle/polar.py): norms within one
+    float32 ulp; slot codes bit-exact except an angle whose rotated point lies
+    within 1e-5 (unit-sphere scale) of a decision boundary of its level (then
+    the neighbouring code, or across the 0 = 2 pi wrap at level 1), such
+    slots below 1e-4 of all; the spare slot of quarter 3 and the padding zero."""
+    import oracle.polar as PQ
+    ref = PQ.quantize(p, X)
+    g_idx = O.unpack_bits(gpu["codes"], p.bits, p.d)
+    gn, rn = gpu["norms"].astype(np.float32), ref["norms"].astype(np.float32)
+    assert (np.abs(gn.astype(np.float64) - rn) <= np.spacing(np.maximum(np.abs(rn), 1e-30))).all()
+    diff = g_idx != ref["idx"]
+    n = 2 ** p.bits
+    for v, s in zip(*np.nonzero(diff)):
+        m = PQ.slot_margins(p, X[v])[s]
+        assert m < BAND, f"vector {v} slot {s}: code {g_idx[v, s]} vs {ref['idx'][v, s]}, margin {m:.3e}"
+        dist = abs(int(g_idx[v, s]) - int(ref["idx"][v, s]))
+        assert dist == 1 or dist == n - 1, (v, s, dist)
+    assert diff.sum() <= allow_frac * diff.size, f"{diff.sum()} angle-code mismatches of {diff.size}"
+    bits = np.unpackbits(gpu["codes"], axis=1, bitorder="little")
+    assert not bits[:, p.bits * p.d:].any(), "nonzero code padding"
+    assert not g_idx[:, p.d - 1].any(), "spare slot of the last quarter"
+    zero = ref["norms"] == 0
+    assert not gpu["codes"][zero].any()
+    return int(diff.sum())

@@ -88,3 +88,18 @@ def test_argument_validation_before_any_device_work():
     L.tq_free(None)                           # null-safe
     assert tq.tq_strerror(tq.TQ_EINVAL) == "invalid argument"
     assert tq.tq_strerror(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("d,bits", [(32, 1), (64, 3), (128, 2), (128, 4), (256, 3)])
+def test_polar_codebooks_match_oracle(d, bits):
+    # the library's own Lloyd-Max iteration for the angle laws (C++, its own
+    # Gauss-Legendre rule) against the oracle's
+    import oracle.polar as PQ
+    from oblivious_kv_cache_amd import binding as tq
+    c, t = tq.tq_polar_codebook(d, bits)
+    books = PQ.codebooks(d, bits)
+    assert c.shape == (len(books), 2 ** bits)
+    for level, (bc, bt) in enumerate(books):
+        assert np.abs(c[level] - bc).max() < 1e-12 and np.abs(t[level] - bt).max() < 1e-12
+    with pytest.raises(tq.TQError):
+        tq.tq_polar_codebook(96, bits)          # not a power of two
