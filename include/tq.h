@@ -80,8 +80,8 @@ extern "C" {
 #define TQ_OP_TOPK    3
 
 /* limits of the library */
-#define TQ_MAX_D       256   /* d in [8, 256], d % 8 == 0 */
-#define TQ_MAX_TOPK    64
+#define TQ_MAX_D       1024  /* d in [8, 1024], d % 8 == 0 */
+#define TQ_MAX_TOPK    1024
 #define TQ_MAX_QPG     64    /* query heads per group: attention and decode steps */
 #define TQ_MAX_QPG_SCORES 65536  /* queries per group: tq_scores, tq_prep_queries,
                                     tq_scores_prepared (many queries against one key

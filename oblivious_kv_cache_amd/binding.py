@@ -19,7 +19,7 @@ TQ_SCRATCH_BYTES = 16 << 20
 TQ_F32, TQ_BF16 = 0, 1
 TQ_MODE_PROD, TQ_MODE_MSE, TQ_MODE_POLAR = 0, 1, 2
 TQ_OP_SCORES, TQ_OP_ATTEND, TQ_OP_TOPK = 1, 2, 3
-TQ_MAX_D, TQ_MAX_TOPK = 256, 64
+TQ_MAX_D, TQ_MAX_TOPK = 1024, 1024
 
 EXPORTS = [
     "tq_init", "tq_init_mse", "tq_free", "tq_layout", "tq_host_params", "tq_get_params",

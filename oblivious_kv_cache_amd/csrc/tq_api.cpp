@@ -45,17 +45,21 @@ int current_device_matches(const tq_ctx *ctx) {
 //   GEMM 2: A = S'[sigma(u, r)][g * P + 8 k + e]      (S' = S Pi^T, P = dpad/4)
 // with the row permutation sigma(u, r) = (r / 4) * P + 4 u + (r % 4), which
 // hands lane group g the coordinates [g P, (g+1) P).
+//
+// For d > 256 (the kernel that stages vectors in LDS) there is no
+// permutation: row = 16 u + r and column 32 k + 8 g + e for both GEMMs.
 void build_frags(const tq::HostParams &hp, int dpad, const double *M, int rows, int cols,
                  bool gemm2, Frag *hi, Frag *lo) {
   const int NT = dpad / 16, NK = dpad / 32, P = dpad / 4;
+  const bool plain = dpad > 256;
   for (int u = 0; u < NT; ++u)
     for (int k = 0; k < NK; ++k)
       for (int l = 0; l < 64; ++l) {
         const int r = l % 16, g = l / 16;
-        const int row = (r / 4) * P + 4 * u + (r % 4);
+        const int row = plain ? 16 * u + r : (r / 4) * P + 4 * u + (r % 4);
         uint16_t h8[8], l8[8];
         for (int e = 0; e < 8; ++e) {
-          const int c = gemm2 ? g * P + 8 * k + e : 32 * k + 8 * g + e;
+          const int c = (gemm2 && !plain) ? g * P + 8 * k + e : 32 * k + 8 * g + e;
           double v = 0.0;
           if (row < rows && c < cols) v = M[(size_t)row * cols + c];
           split_bf16(v, h8[e], l8[e]);
@@ -83,7 +87,7 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
   }
   const tq::HostParams &hp = ctx->hp;
   const int m = hp.m, w = hp.w, L = hp.levels;
-  ctx->dpad = d <= 32 ? 32 : d <= 64 ? 64 : d <= 128 ? 128 : 256;
+  ctx->dpad = d <= 32 ? 32 : d <= 64 ? 64 : d <= 128 ? 128 : d <= 256 ? 256 : (d + 31) / 32 * 32;
   ctx->code_bytes = ((d * w + 7) / 8 + 15) / 16 * 16;
   ctx->sign_bytes = m ? ((m + 7) / 8 + 15) / 16 * 16 : 0;
   ctx->alpha = m ? (float)(std::sqrt(M_PI / 2.0) / m) : 0.f;

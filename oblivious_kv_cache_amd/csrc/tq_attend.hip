@@ -555,6 +555,129 @@ int dispatch(const AttArgs &a, dim3 grid, int cb16, int sb16, int w, int vw, hip
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// ------------------------------------------------------------ d > 128
+// Vectors longer than 128 coordinates take three steps: the logits by the
+// scores kernels (into the logits output, or the workspace), a value-sum
+// kernel that reads them back with the same online softmax per run of chunks
+// and accumulates sum_t exp(z_t - M) nu_t c_v[idx_t] on the VALU, and the
+// combine (and probs) kernels above.  Block = (query group of 4 heads, run of
+// chunks); thread = (token lane, 4 consecutive coordinates), so that the
+// codes of its coordinates are one bit field of a record word pair.
+constexpr int VT = 64;             // tokens per value tile
+
+struct VsumArgs {
+  const float *logits;             // [G][qpg][T]
+  const uint8_t *vcodes;
+  const float *vnorms;
+  float *part;                     // [G*hg][nsplit][4][d + 2]
+  int64_t T, ldk;
+  int qpg, hg, cps, nsplit, d, vw, vcb;
+  float scale;
+  float cf[16];                    // value centroids
+};
+
+__global__ void __launch_bounds__(256) attend_vsum_kernel(VsumArgs a) {
+  extern __shared__ __align__(16) uint32_t vrec[];   // [VT][vcb / 4] the tile's value records
+  __shared__ float4 wt[VT];                          // per token: exp(z - M) nu for the 4 heads
+  __shared__ float cbk[16];
+  __shared__ float fsc[4];
+  __shared__ float4 red[256 * 4];                    // per thread: 4 coordinates x 4 heads
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t gy = blockIdx.y;                     // key group * hg + head group
+  const int64_t kg = gy / a.hg;
+  const int hgi = (int)(gy - kg * a.hg);
+  const int d = a.d, vw = a.vw, vcw = a.vcb / 4;
+  const int nq4 = d / 4, nl = 256 / nq4;             // coordinate quads, token lanes
+  const int qi = tid % nq4, tl = tid / nq4;
+  const bool act = tl < nl;
+  if (tid < 16) cbk[tid] = a.cf[tid];
+  const int head = hgi * 4 + wv;                     // wave wv keeps head wv's softmax state
+  const bool hok = head < a.qpg;
+  const float *lrow = a.logits + (kg * a.qpg + (hok ? head : 0)) * a.T;
+  const uint8_t *vbase = a.vcodes + kg * a.ldk * a.vcb;
+  const float *nbase = a.vnorms + kg * a.ldk;
+  float M = -INFINITY, S = 0.f;
+  float4 acc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int64_t t_begin = (int64_t)blockIdx.x * a.cps * CH;
+  const int64_t t_end = min(t_begin + (int64_t)a.cps * CH, a.T);
+  const uint32_t cmask = (1u << vw) - 1u;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += VT) {
+    const int ntok = (int)min((int64_t)VT, t_end - t0);
+    for (int i = tid; i < VT * vcw; i += 256) {
+      const int tok = i / vcw;
+      vrec[i] = tok < ntok ? reinterpret_cast<const uint32_t *>(vbase + (t0 + tok) * a.vcb)[i - tok * vcw] : 0u;
+    }
+    const bool tv = hok && lane < ntok;
+    const float z = tv ? a.scale * lrow[t0 + lane] : -INFINITY;
+    const float Mn = fmaxf(M, wave_max(z));
+    const float f = M == -INFINITY ? 0.f : __expf(M - Mn);
+    const float pz = z == -INFINITY ? 0.f : __expf(z - Mn);
+    S = fmaf(S, f, wave_sum(pz));
+    M = Mn;
+    const float nu = lane < ntok ? nbase[t0 + lane] : 0.f;
+    reinterpret_cast<float *>(&wt[lane])[wv] = pz * nu;
+    if (lane == 0) fsc[wv] = f;
+    __syncthreads();
+    const float4 fs = make_float4(fsc[0], fsc[1], fsc[2], fsc[3]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e].x *= fs.x;
+      acc[e].y *= fs.y;
+      acc[e].z *= fs.z;
+      acc[e].w *= fs.w;
+    }
+    if (act) {
+      const int bit = 4 * qi * vw, wi = bit >> 5, sh = bit & 31;
+      for (int tok = tl; tok < ntok; tok += nl) {
+        const float4 w4 = wt[tok];
+        const uint32_t *rw = vrec + tok * vcw;
+        uint32_t bits = rw[wi] >> sh;
+        // the field's bits lie inside the record, so word wi + 1 exists here
+        if (sh + 4 * vw > 32) bits |= rw[wi + 1] << (32 - sh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float c = cbk[(bits >> (e * vw)) & cmask];
+          acc[e].x = fmaf(c, w4.x, acc[e].x);
+          acc[e].y = fmaf(c, w4.y, acc[e].y);
+          acc[e].z = fmaf(c, w4.z, acc[e].z);
+          acc[e].w = fmaf(c, w4.w, acc[e].w);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // token lanes summed in a fixed order; partials out
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[tid * 4 + e] = acc[e];
+  __syncthreads();
+  float *pp = a.part + (gy * a.nsplit + blockIdx.x) * (int64_t)(4 * (d + 2));
+  if (act && tl == 0) {
+    for (int l = 1; l < nl; ++l)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float4 v = red[(l * nq4 + qi) * 4 + e];
+        acc[e].x += v.x;
+        acc[e].y += v.y;
+        acc[e].z += v.z;
+        acc[e].w += v.w;
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * qi + e;
+      pp[0 * (d + 2) + i] = acc[e].x;
+      pp[1 * (d + 2) + i] = acc[e].y;
+      pp[2 * (d + 2) + i] = acc[e].z;
+      pp[3 * (d + 2) + i] = acc[e].w;
+    }
+  }
+  if (lane == 0) {
+    pp[wv * (d + 2) + d] = M;
+    pp[wv * (d + 2) + d + 1] = S;
+  }
+}
+
 }  // namespace
 
 size_t attend_ws_bytes(const tq_ctx *k, int64_t G, int qpg, int64_t T) {
@@ -562,15 +685,18 @@ size_t attend_ws_bytes(const tq_ctx *k, int64_t G, int qpg, int64_t T) {
   const int nm = mfma_count(k->code_bytes / 16, k->sign_bytes / 16, k->hp.w);
   const int64_t nchunk = (T + CH - 1) / CH;
   const int d = k->hp.d;
+  // d > 128: the logits of the three-step path as well
+  const int64_t lg = d > 128 ? align256(G * qpg * T * 4) : 0;
   return (size_t)(align256(G * hg * prep_stride(nm)) + align256(G * hg * nchunk * 4 * (d + 2) * 4) +
-                  align256(G * qpg * 2 * 4));
+                  align256(G * qpg * 2 * 4) + lg);
 }
 
 int check_attend(const tq_ctx *kc, const tq_ctx *vc, int64_t G, int qpg, int64_t T, int64_t ldk,
                  bool want_probs) {
   const int d = kc->hp.d;
-  if (d > 128) return TQ_ENOTSUP;                      // the fused kernel holds 8 coordinate tiles
-  if (vc->hp.w < 1 || vc->hp.w > 4 || vc->code_bytes > 16 * vc->hp.w) return TQ_ENOTSUP;
+  if (vc->hp.w < 1 || vc->hp.w > 4) return TQ_ENOTSUP;
+  // the fused kernel (d <= 128) holds a value record in 16 w bytes
+  if (d <= 128 && vc->code_bytes > 16 * vc->hp.w) return TQ_ENOTSUP;
   const int64_t groups = G * ((qpg + 3) / 4);
   if (groups > 65535 || T > 0x7fffffff - CH || G * qpg > 0x7fffffff) return TQ_ENOTSUP;
   const int64_t rec_max = std::max<int64_t>(std::max(kc->code_bytes, kc->sign_bytes), vc->code_bytes);
@@ -602,6 +728,36 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
     st = launch_prep(kc, q, groups, qpg, hg, G * qpg, prep, stream);
     if (st != TQ_OK) return st;
   }
+  // splits per query group: about TQ_ATT_BLOCKS blocks in all, equal runs of chunks
+  int64_t want = (TQ_ATT_BLOCKS + groups - 1) / groups;
+  if (want > nchunk) want = nchunk;
+  if (want < 1) want = 1;
+  const int cps = (int)((nchunk + want - 1) / want);
+  const int nsplit = (int)((nchunk + cps - 1) / cps);
+  if (d > 128) {
+    float *lg = logits ? logits
+                       : reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(mstat) + align256(G * qpg * 2 * 4));
+    st = launch_scores_prepared(kc, prep, G, qpg, T, ldk, kcodes, ksigns, knorms, krnorms, lg, stream);
+    if (st != TQ_OK) return st;
+    VsumArgs v{};
+    v.logits = lg;
+    v.vcodes = vcodes;
+    v.vnorms = vnorms;
+    v.part = part;
+    v.T = T;
+    v.ldk = ldk;
+    v.qpg = qpg;
+    v.hg = hg;
+    v.cps = cps;
+    v.nsplit = nsplit;
+    v.d = d;
+    v.vw = vc->hp.w;
+    v.vcb = vc->code_bytes;
+    v.scale = scale;
+    for (int i = 0; i < 16; ++i) v.cf[i] = vc->cf[i];
+    attend_vsum_kernel<<<dim3((unsigned)nsplit, (unsigned)groups), 256, (size_t)VT * vc->code_bytes, stream>>>(v);
+    if (hip_status() != TQ_OK) return TQ_EHIP;
+  } else {
   AttArgs a{};
   a.kcodes = kcodes;
   a.ksigns = ksigns;
@@ -617,12 +773,8 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   a.qpg = qpg;
   a.hg = hg;
   a.nchunk = (int)nchunk;
-  // splits per query group: about TQ_ATT_BLOCKS blocks in all, equal runs of chunks
-  int64_t want = (TQ_ATT_BLOCKS + groups - 1) / groups;
-  if (want > nchunk) want = nchunk;
-  if (want < 1) want = 1;
-  a.cps = (int)((nchunk + want - 1) / want);
-  a.nsplit = (int)((nchunk + a.cps - 1) / a.cps);
+  a.cps = cps;
+  a.nsplit = nsplit;
   a.d = d;
   a.kcb = kc->code_bytes;
   a.ksb = kc->sign_bytes;
@@ -632,6 +784,7 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   for (int i = 0; i < 8; ++i) a.vbasis[i] = vc->vbasis[i];
   st = dispatch(a, dim3((unsigned)a.nsplit, (unsigned)groups), cb16, sb16, w, vc->hp.w, stream);
   if (st != TQ_OK) return st;
+  }
   CombArgs c{};
   c.part = part;
   c.Piv = vc->Pi32;
@@ -640,7 +793,7 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   c.G = G;
   c.qpg = qpg;
   c.hg = hg;
-  c.nchunk = a.nsplit;
+  c.nchunk = nsplit;
   c.d = d;
   attend_combine_kernel<<<(unsigned)(G * qpg), CT, 0, stream>>>(c);
   if (hip_status() != TQ_OK) return TQ_EHIP;

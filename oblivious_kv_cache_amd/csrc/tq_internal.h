@@ -36,7 +36,7 @@ struct tq_ctx {
   tq::HostParams hp;
   int device = 0;
   int cus = 256;       // compute units of that device (grid sizing)
-  int dpad = 0;        // d rounded up to the quantize kernel's tile (32/64/128/256)
+  int dpad = 0;        // d rounded up to the quantize kernel's tile (32/64/128/256, then 32 k)
   int code_bytes = 0;
   int sign_bytes = 0;
   float alpha = 0.f;   // sqrt(pi/2) / m
@@ -63,6 +63,12 @@ namespace tq {
 int launch_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t ldx,
                     int64_t ldr, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
                     hipStream_t stream);
+// vectors longer than 256 coordinates (tq_big.hip)
+int launch_quantize_big(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t ldx,
+                        int64_t ldr, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
+                        hipStream_t stream);
+int launch_prep_big(const tq_ctx *ctx, const float *q, int64_t groups, int qpg, int hg,
+                    int64_t nq_total, uint8_t *ws, hipStream_t stream);
 int launch_polar_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t ldx,
                           int64_t ldr, uint8_t *codes, float *norms, hipStream_t stream);
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t G, int qpg);
@@ -112,5 +118,14 @@ int check_scores_call(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int
 void *scratch_attach(int device);
 
 inline int hip_status() { return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EHIP; }
+
+// Lets kernel fn take `bytes` of dynamic LDS (beyond the 64 KB allowed by
+// default; a CU has 160 KB).
+inline int allow_lds(const void *fn, size_t bytes) {
+  if (bytes <= 65536) return TQ_OK;
+  if (bytes > 163840) return TQ_ENOTSUP;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess ? TQ_OK
+                                                                                                        : TQ_EHIP;
+}
 
 }  // namespace tq

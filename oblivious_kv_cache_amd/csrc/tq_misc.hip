@@ -53,32 +53,34 @@ __global__ void __launch_bounds__(256) dequant_kernel(DqArgs a) {
       if (byte + 1 < a.cb) word |= (uint32_t)rec[byte + 1] << 8;
       return (word >> (bit & 7)) & ((1u << a.w) - 1u);
     };
-    if (tid < a.d) {
+    for (int j = tid; j < a.d; j += 256) {
       if (a.pcs) {
         float yv = 1.f;
         for (int level = 1; level <= a.nlev; ++level) {
-          const uint32_t code = code_at(polar_slot(a.d, a.nlev, level, tid >> level));
-          yv *= a.pcs[(((level - 1) << a.w) + (int)code) * 2 + ((tid >> (level - 1)) & 1)];
+          const uint32_t code = code_at(polar_slot(a.d, a.nlev, level, j >> level));
+          yv *= a.pcs[(((level - 1) << a.w) + (int)code) * 2 + ((j >> (level - 1)) & 1)];
         }
-        cv[tid] = yv;
+        cv[j] = yv;
       } else {
-        cv[tid] = a.c[code_at(tid)];
+        cv[j] = a.c[code_at(j)];
       }
     }
-    if (a.signs && tid < a.m) {
-      const uint8_t b = a.signs[v * a.sb + (tid >> 3)];
-      sv[tid] = ((b >> (tid & 7)) & 1) ? 1.f : -1.f;
+    if (a.signs) {
+      for (int k = tid; k < a.m; k += 256) {
+        const uint8_t b = a.signs[v * a.sb + (k >> 3)];
+        sv[k] = ((b >> (k & 7)) & 1) ? 1.f : -1.f;
+      }
     }
     __syncthreads();
-    if (tid < a.d) {
+    for (int j = tid; j < a.d; j += 256) {
       float acc = 0.f;
-      for (int i = 0; i < a.d; ++i) acc = fmaf(a.Pi[(int64_t)i * a.d + tid], cv[i], acc);
+      for (int i = 0; i < a.d; ++i) acc = fmaf(a.Pi[(int64_t)i * a.d + j], cv[i], acc);
       if (a.signs) {
         float acc2 = 0.f;
-        for (int k = 0; k < a.m; ++k) acc2 = fmaf(a.S[(int64_t)k * a.d + tid], sv[k], acc2);
+        for (int k = 0; k < a.m; ++k) acc2 = fmaf(a.S[(int64_t)k * a.d + j], sv[k], acc2);
         acc = fmaf(a.alpha * a.rnorms[v], acc2, acc);
       }
-      a.out[v * a.d + tid] = a.norms[v] * acc;
+      a.out[v * a.d + j] = a.norms[v] * acc;
     }
     __syncthreads();
   }

@@ -22,7 +22,7 @@ struct PrepArgs {
 // Shared memory of one query-prep group (about 48 KB at d <= 128)
 template <bool SPLIT>
 struct PrepSmem {
-  __align__(16) float qT[TQ_MAX_D][4];             // queries, [coordinate][head]
+  __align__(16) float qT[256][4];             // queries, [coordinate][head]
   __align__(16) float part[SPLIT ? 2 * 4 * 128 * 4 : 4];   // [matrix][row group][column][head]
   float vP[4][2 * 96 * 8];                         // code-bit + parity-bit coefficients
   float vQ[4][32 * 8];                             // sign-bit coefficients
@@ -45,7 +45,7 @@ struct PrepSmem {
 template <int JC, bool SPLIT>
 __device__ __forceinline__ void prep_body(const PrepArgs &a, PrepSmem<SPLIT> &sm, int gidx, int tid,
                                           bool live) {
-  float (&qT)[TQ_MAX_D][4] = sm.qT;
+  float (&qT)[256][4] = sm.qT;
   float *part = sm.part;
   float (&vP)[4][2 * 96 * 8] = sm.vP;
   float (&vQ)[4][32 * 8] = sm.vQ;

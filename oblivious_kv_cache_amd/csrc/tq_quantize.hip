@@ -76,7 +76,7 @@ int launch_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int6
       a.ntiles = (n + 15) / 16;
       return launch_d<256, false, 1>(a, w, bf16, ctx->cus, stream);
     default:
-      return TQ_ENOTSUP;
+      return launch_quantize_big(ctx, x, dtype, n, ldx, ldr, codes, signs, norms, rnorms, stream);
   }
 }
 

@@ -235,6 +235,94 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
+// Records of any geometry (vectors longer than 256 coordinates, or callers
+// that keep no per-geometry kernel): the record words are read one at a
+// time in a runtime loop and the A fragments come from LDS (Al = [nm][64]),
+// where the 4 waves of a block share them.  NK 16-key tiles are scored per
+// pass, so that every fragment read from LDS serves NK MFMAs.  cp[s] / sp[s]
+// point at the lane's first code / sign word of its key in tile s (lane
+// group g: record words g*cb16 .. g*cb16 + cb16 - 1).  The digit rows are
+// recombined in fp32 (their int32 sums reach ~2^24 at d = 1024, so the
+// int32 pair recombination of tile_logits could overflow).
+template <int W, int NK>
+__device__ __forceinline__ void big_tiles(const i32x4 *Al, const uint8_t *const (&cp)[NK],
+                                          const uint8_t *const (&sp)[NK], int cb16, int sb16, int lane,
+                                          const float (&nu)[NK], const float (&ga)[NK], float alpha,
+                                          const HeadConsts &hc, float (&out)[NK]) {
+  const int grp = lane >> 4;
+  i32x4 accP[NK], accQ[NK];
+#pragma unroll
+  for (int s = 0; s < NK; ++s) accP[s] = accQ[s] = i32x4{0, 0, 0, 0};
+  const int nmc = 2 * cb16, nmp = 2 * parity_words(cb16, W);
+  uint32_t cur[NK], pw[NK];
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    cur[s] = *reinterpret_cast<const uint32_t *>(cp[s]);
+    pw[s] = 0u;
+  }
+  for (int p = 0; p < cb16; ++p) {
+    // the word after this one: the next lane group's first word after the
+    // last (3-bit codes cross words), none for the last lane group
+    const bool has_next = p + 1 < cb16 || (W == 3 && grp < 3);
+    uint32_t nxt[NK];
+#pragma unroll
+    for (int s = 0; s < NK; ++s) nxt[s] = has_next ? *reinterpret_cast<const uint32_t *>(cp[s] + 4 * (p + 1)) : 0u;
+    const i32x4 a0 = Al[(2 * p) * 64 + lane], a1 = Al[(2 * p + 1) * 64 + lane];
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      accP[s] = mfma8(a0, planes(cur[s], 0), accP[s]);
+      accP[s] = mfma8(a1, planes(cur[s], 1), accP[s]);
+    }
+    if constexpr (W == 3) {
+      const uint32_t mask = 0x49249249u << ((grp * cb16 + p) % 3);
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        const uint32_t par = cur[s] ^ __builtin_amdgcn_alignbit(nxt[s], cur[s], 1) ^
+                             __builtin_amdgcn_alignbit(nxt[s], cur[s], 2);
+        pw[s] |= par & mask;
+      }
+      if (p % 3 == 2 || p == cb16 - 1) {
+        const int f = p / 3;
+        const i32x4 a2 = Al[(nmc + 2 * f) * 64 + lane], a3 = Al[(nmc + 2 * f + 1) * 64 + lane];
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+          accP[s] = mfma8(a2, planes(pw[s], 0), accP[s]);
+          accP[s] = mfma8(a3, planes(pw[s], 1), accP[s]);
+          pw[s] = 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NK; ++s) cur[s] = nxt[s];
+  }
+  for (int p = 0; p < sb16; ++p) {
+    const i32x4 a0 = Al[(nmc + nmp + 2 * p) * 64 + lane], a1 = Al[(nmc + nmp + 2 * p + 1) * 64 + lane];
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const uint32_t wd = *reinterpret_cast<const uint32_t *>(sp[s] + 4 * p);
+      accQ[s] = mfma8(a0, planes(wd, 0), accQ[s]);
+      accQ[s] = mfma8(a1, planes(wd, 1), accQ[s]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    const float Ph = fmaf((float)accP[s][0], 128.f, (float)accP[s][1]);
+    const float Pl = fmaf((float)accP[s][2], 128.f, (float)accP[s][3]);
+    const float Qh = fmaf((float)accQ[s][0], 128.f, (float)accQ[s][1]);
+    const float Ql = fmaf((float)accQ[s][2], 128.f, (float)accQ[s][3]);
+    const float P = fmaf(fmaf(Pl, 0x1.0p-14f, Ph), hc.invSP, -hc.KP);
+    const float Q = fmaf(fmaf(Ql, 0x1.0p-14f, Qh), hc.invSQ, -hc.KQ);
+    out[s] = nu[s] * fmaf(alpha * ga[s], Q, P);
+  }
+}
+
+// Copies one query group's A fragments (nm x 64 lanes x 16 B, at prep) into
+// LDS with all threads of a block of nthreads.
+__device__ __forceinline__ void stage_frags(i32x4 *Al, const uint8_t *prep, int nm, int tid, int nthreads) {
+  const i32x4 *src = reinterpret_cast<const i32x4 *>(prep);
+  for (int i = tid; i < nm * 64; i += nthreads) Al[i] = src[i];
+}
+
 // Expands a dispatch over the record geometries d <= 256 can produce:
 // (code words per lane group, sign words per lane group, code bits).
 #define TQ_FOR_EACH_GEOMETRY(X)                                              \

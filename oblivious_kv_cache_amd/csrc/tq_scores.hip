@@ -272,10 +272,107 @@ int dispatch(const ScoreArgs &a, dim3 grid, int cb16, int sb16, int w, int nq, h
   return TQ_ENOTSUP;
 }
 
+// Records of vectors longer than 256 coordinates: one block per (key group,
+// head group) and run of 64-key tiles; the group's A fragments (up to 80 KB at
+// d = 1024) are staged in LDS and shared by the block's four waves, and the
+// record words are walked in a runtime loop (big_tiles).
+struct BigScoreArgs {
+  const uint8_t *codes, *signs;
+  const float *norms, *rnorms;
+  float *logits;
+  const uint8_t *ws;
+  int64_t T, ldk;
+  int qpg, hg, tiles_per_wave, cb16, sb16, nm;
+  float alpha;
+};
+
+template <int W>
+__global__ void __launch_bounds__(256) scores_big_kernel(BigScoreArgs a) {
+  extern __shared__ __align__(16) i32x4 Al[];
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4, wv = tid >> 6;
+  const int64_t gy = blockIdx.y;                 // key group * hg + head group
+  const int64_t kg = gy / a.hg;
+  const int hgi = (int)(gy - kg * a.hg);
+  const uint8_t *prep = a.ws + gy * prep_stride(a.nm);
+  stage_frags(Al, prep, a.nm, tid, 256);
+  const HeadConsts hc = HeadConsts::load(reinterpret_cast<const float *>(prep + (int64_t)a.nm * 1024) + grp * 4);
+  __syncthreads();
+  const int head = hgi * 4 + grp;
+  const bool ok = head < a.qpg;
+  float *lrow = a.logits + (kg * a.qpg + (ok ? head : 0)) * a.T;
+  const int64_t cbytes = 16 * a.cb16, sbytes = 16 * a.sb16;
+  const uint8_t *cbase = a.codes + kg * a.ldk * cbytes + grp * a.cb16 * 4;
+  const uint8_t *sbase = a.signs + kg * a.ldk * sbytes + grp * a.sb16 * 4;
+  const float *nbase = a.norms + kg * a.ldk, *rbase = a.rnorms + kg * a.ldk;
+  const int64_t T = a.T;
+  const int64_t tile0 = ((int64_t)blockIdx.x * 4 + wv) * a.tiles_per_wave;
+  for (int i = 0; i < a.tiles_per_wave; ++i) {
+    const int64_t t0 = (tile0 + i) * 64;
+    if (t0 >= T) break;
+    const uint8_t *cp[4];
+    const uint8_t *sp[4];
+    float nu[4], ga[4], l[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t t = min(t0 + 16 * s + col, T - 1);
+      cp[s] = cbase + t * cbytes;
+      sp[s] = sbase + t * sbytes;
+      nu[s] = nbase[t];
+      ga[s] = rbase[t];
+    }
+    big_tiles<W, 4>(Al, cp, sp, a.cb16, a.sb16, lane, nu, ga, a.alpha, hc, l);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t t = t0 + 16 * s + col;
+      if (ok && t < T) lrow[t] = l[s];
+    }
+  }
+}
+
+int launch_scores_big(const tq_ctx *ctx, const void *ws, int64_t G, int qpg, int64_t T, int64_t ldk,
+                      const uint8_t *codes, const uint8_t *signs, const float *norms, const float *rnorms,
+                      float *logits, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  BigScoreArgs a{};
+  a.codes = codes;
+  a.signs = signs;
+  a.norms = norms;
+  a.rnorms = rnorms;
+  a.logits = logits;
+  a.ws = reinterpret_cast<const uint8_t *>(ws);
+  a.T = T;
+  a.ldk = ldk;
+  a.qpg = qpg;
+  a.hg = (qpg + 3) / 4;
+  a.cb16 = ctx->code_bytes / 16;
+  a.sb16 = ctx->sign_bytes / 16;
+  a.nm = mfma_count(a.cb16, a.sb16, ctx->hp.w);
+  a.alpha = ctx->alpha;
+  const int64_t groups = G * a.hg;
+  const int64_t tiles = (T + 63) / 64;
+  int64_t tpw = (tiles * groups + TQ_SCORES_WAVES - 1) / TQ_SCORES_WAVES;
+  if (tpw > (tiles + 3) / 4) tpw = (tiles + 3) / 4;
+  if (tpw < 1) tpw = 1;
+  const int64_t chunks = (tiles + 4 * tpw - 1) / (4 * tpw);
+  if (chunks > 0x7fffffff) return TQ_ENOTSUP;
+  a.tiles_per_wave = (int)tpw;
+  const size_t lds = (size_t)a.nm * 1024;
+  const dim3 grid((unsigned)chunks, (unsigned)groups);
+  auto go = [&](auto kern) {
+    if (allow_lds(reinterpret_cast<const void *>(kern), lds) != TQ_OK) return TQ_EHIP;
+    if (e0 || e1)
+      hipExtLaunchKernelGGL(kern, grid, dim3(256), lds, stream, e0, e1, 0, a);
+    else
+      hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, a);
+    return hip_status();
+  };
+  return ctx->hp.w == 3 ? go(scores_big_kernel<3>) : go(scores_big_kernel<1>);
+}
+
 }  // namespace
 
 int launch_prep(const tq_ctx *ctx, const float *q, int64_t groups, int qpg, int hg, int64_t nq_total,
                 uint8_t *ws, hipStream_t stream) {
+  if (ctx->hp.d > 256) return launch_prep_big(ctx, q, groups, qpg, hg, nq_total, ws, stream);
   const PrepArgs pa = make_prep_args(ctx, q, qpg, hg, nq_total, ws);
   if (groups > 0x7fffffff) return TQ_ENOTSUP;
   const dim3 grid((unsigned)groups);
@@ -320,6 +417,9 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   if (G == 0 || T == 0) return TQ_OK;
   int st = check_scores_shape(ctx, G, qpg, T, ldk);
   if (st != TQ_OK) return st;
+  if (ctx->hp.d > 256)
+    return launch_scores_big(ctx, ws, G, qpg, T, ldk, codes, signs, norms, rnorms, logits, stream, ev_start,
+                             ev_stop);
   const int hg = (qpg + 3) / 4;
   const int cb16 = ctx->code_bytes / 16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
   // NQ head groups per wave (2 where it fits); blocks along y: key group x NQ-group block

@@ -255,6 +255,167 @@ __global__ void __launch_bounds__(256) topk_merge_kernel(const float *cand_s, co
   }
 }
 
+// ---------------------------------------------------------------- large k
+// k up to TQ_MAX_TOPK, or records of vectors longer than 256 coordinates:
+// one 256-thread block per (query group of 4, database chunk).  The block
+// keeps, per query, a sorted list of the best LIST entries seen (in LDS, with
+// the group's A fragments) and a candidate buffer.  The four waves score 256
+// database vectors per round (big_tiles); a score enters the buffer only if it
+// beats the list's k-th entry (vectors of later rounds have larger ids, so a
+// tie never enters).  When a buffer may overflow in the next round, the block
+// sorts it and merges it into the list.  The chunk's list goes to the
+// candidate array that topk_merge_kernel reduces over chunks.
+constexpr int LIST = 1024;        // list capacity (>= k)
+constexpr int CBUF = 1024;        // candidate buffer per query
+constexpr int BLK_ROUND = 256;    // vectors scored per round (4 waves x 64)
+
+struct BlkArgs {
+  const uint8_t *codes, *signs;
+  const float *norms, *rnorms;
+  const uint8_t *prep;
+  float *cand_s;
+  int *cand_i;
+  int64_t n, nq, chunk;
+  int nchunk, cb16, sb16, nm, k;
+  float alpha;
+};
+
+template <int W>
+__global__ void __launch_bounds__(256) topk_block_kernel(BlkArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  i32x4 *Al = reinterpret_cast<i32x4 *>(smem);
+  float *bs = reinterpret_cast<float *>(Al + a.nm * 64);     // [4][LIST + CBUF]
+  int *bi = reinterpret_cast<int *>(bs + 4 * (LIST + CBUF));
+  __shared__ int cnt[4];
+  __shared__ float thr[4];
+  constexpr int ROW = LIST + CBUF;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4, wv = tid >> 6;
+  const int64_t qg = blockIdx.y;
+  const int c = blockIdx.x;
+  const uint8_t *prep = a.prep + qg * prep_stride(a.nm);
+  stage_frags(Al, prep, a.nm, tid, 256);
+  for (int i = tid; i < 4 * ROW; i += 256) {
+    bs[i] = -FLT_MAX;
+    bi[i] = INT_MAX;
+  }
+  if (tid < 4) {
+    cnt[tid] = 0;
+    thr[tid] = -FLT_MAX;
+  }
+  const HeadConsts hc = HeadConsts::load(reinterpret_cast<const float *>(prep + (int64_t)a.nm * 1024) + grp * 4);
+  __syncthreads();
+
+  // candidates of every query sorted worst first, then merged into the lists:
+  // [list best first | candidates worst first] is bitonic; the better half of
+  // each compare-exchange at distance LIST is the best LIST of both, and a
+  // bitonic merge sorts it
+  auto merge = [&]() {
+    for (int size = 2; size <= CBUF; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < 4 * (CBUF / 2); i += 256) {
+          const int qq = i / (CBUF / 2), ii = i - qq * (CBUF / 2);
+          const int lo = 2 * ii - (ii & (stride - 1)), hi = lo + stride;
+          float *rs = bs + qq * ROW + LIST;
+          int *ri = bi + qq * ROW + LIST;
+          const bool worst_first = (lo & size) == 0;
+          const float s0 = rs[lo], s1 = rs[hi];
+          const int i0 = ri[lo], i1 = ri[hi];
+          const bool swap = worst_first ? better(s0, i0, s1, i1) : better(s1, i1, s0, i0);
+          if (swap) {
+            rs[lo] = s1; rs[hi] = s0;
+            ri[lo] = i1; ri[hi] = i0;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < 4 * LIST; i += 256) {
+      const int qq = i / LIST, ii = i - qq * LIST;
+      float *rs = bs + qq * ROW;
+      int *ri = bi + qq * ROW;
+      const float s0 = rs[ii], s1 = rs[ii + LIST];
+      const int i0 = ri[ii], i1 = ri[ii + LIST];
+      if (better(s1, i1, s0, i0)) {
+        rs[ii] = s1;
+        ri[ii] = i1;
+      }
+      rs[ii + LIST] = -FLT_MAX;          // the buffer is emptied
+      ri[ii + LIST] = INT_MAX;
+    }
+    __syncthreads();
+    for (int stride = LIST / 2; stride > 0; stride >>= 1) {
+      for (int i = tid; i < 4 * (LIST / 2); i += 256) {
+        const int qq = i / (LIST / 2), ii = i - qq * (LIST / 2);
+        const int lo = 2 * ii - (ii & (stride - 1)), hi = lo + stride;
+        float *rs = bs + qq * ROW;
+        int *ri = bi + qq * ROW;
+        const float s0 = rs[lo], s1 = rs[hi];
+        const int i0 = ri[lo], i1 = ri[hi];
+        if (better(s1, i1, s0, i0)) {
+          rs[lo] = s1; rs[hi] = s0;
+          ri[lo] = i1; ri[hi] = i0;
+        }
+      }
+      __syncthreads();
+    }
+    if (tid < 4) {
+      cnt[tid] = 0;
+      // the k-th entry bounds what can still enter (none while the list is short)
+      thr[tid] = bi[tid * ROW + a.k - 1] == INT_MAX ? -FLT_MAX : bs[tid * ROW + a.k - 1];
+    }
+    __syncthreads();
+  };
+
+  const int64_t begin = (int64_t)c * a.chunk;
+  const int64_t end = min(begin + a.chunk, a.n);
+  const int64_t cbytes = 16 * a.cb16, sbytes = 16 * a.sb16;
+  const uint8_t *cbase = a.codes + grp * a.cb16 * 4;
+  const uint8_t *sbase = a.signs + grp * a.sb16 * 4;
+  for (int64_t r0 = begin; r0 < end; r0 += BLK_ROUND) {
+    const int64_t t0 = r0 + wv * 64;
+    if (t0 < end) {
+      const uint8_t *cp[4];
+      const uint8_t *sp[4];
+      float nu[4], ga[4], l[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int64_t t = min(t0 + 16 * s + col, end - 1);
+        cp[s] = cbase + t * cbytes;
+        sp[s] = sbase + t * sbytes;
+        nu[s] = a.norms[t];
+        ga[s] = a.rnorms[t];
+      }
+      big_tiles<W, 4>(Al, cp, sp, a.cb16, a.sb16, lane, nu, ga, a.alpha, hc, l);
+      const float th = thr[grp];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int64_t t = t0 + 16 * s + col;
+        if (t < end && l[s] > th) {
+          const int pos = atomicAdd(&cnt[grp], 1);
+          bs[grp * ROW + LIST + pos] = l[s];
+          bi[grp * ROW + LIST + pos] = (int)t;
+        }
+      }
+    }
+    __syncthreads();
+    const bool last = r0 + BLK_ROUND >= end;
+    const int most = max(max(cnt[0], cnt[1]), max(cnt[2], cnt[3]));
+    // every thread has read the counters before the next round adds to them,
+    // so the decision is the same in all threads
+    __syncthreads();
+    if (most > CBUF - BLK_ROUND || (last && most > 0)) merge();
+  }
+  for (int i = tid; i < 4 * a.k; i += 256) {
+    const int qq = i / a.k, j = i - qq * a.k;
+    const int64_t q = qg * 4 + qq;
+    if (q < a.nq) {
+      const int64_t o = (q * a.nchunk + c) * a.k + j;
+      a.cand_s[o] = bs[qq * ROW + j];
+      a.cand_i[o] = bi[qq * ROW + j];
+    }
+  }
+}
+
 int dispatch_scan(const ScanArgs &a, dim3 grid, int cb16, int sb16, int w, int kp, hipStream_t s) {
 #define TQ_CASE(C, S, W_)                                                              \
   if (cb16 == C && sb16 == S && w == W_) {                                             \
@@ -271,11 +432,33 @@ int dispatch_scan(const ScanArgs &a, dim3 grid, int cb16, int sb16, int w, int k
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// The block path (k > 64, or d > 256): chunks so that about two blocks per CU
+// run, at most 8, and at most 8192 candidates per query for the final sort.
+bool topk_block_path(const tq_ctx *ctx, int k) { return k > 64 || ctx->hp.d > 256; }
+
+TopkGeom topk_block_geom(const tq_ctx *ctx, int64_t nq, int64_t n, int k) {
+  TopkGeom g{};
+  g.groups = (nq + 3) / 4;
+  g.qblocks = g.groups;
+  int64_t want = (2 * (int64_t)ctx->cus + g.groups - 1) / g.groups;
+  const int64_t rounds = (n + BLK_ROUND - 1) / BLK_ROUND;
+  if (want > rounds) want = rounds;
+  if (want > MAX_CHUNKS) want = MAX_CHUNKS;
+  if (want * k > 8192) want = 8192 / k;
+  if (want < 1) want = 1;
+  g.nchunk = (int)want;
+  g.chunk = (rounds + want - 1) / want * BLK_ROUND;
+  g.nchunk = (int)((n + g.chunk - 1) / g.chunk);
+  g.kp = 0;
+  g.ncand = (int64_t)g.nchunk * k;
+  return g;
+}
+
 }  // namespace
 
 size_t topk_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int k) {
   const int nm = mfma_count(ctx->code_bytes / 16, ctx->sign_bytes / 16, ctx->hp.w);
-  const TopkGeom g = topk_geom(nq, n, k, nm);
+  const TopkGeom g = topk_block_path(ctx, k) ? topk_block_geom(ctx, nq, n, k) : topk_geom(nq, n, k, nm);
   return (size_t)(align256(g.groups * prep_stride(nm)) + 2 * align256(nq * g.ncand * 4));
 }
 
@@ -284,7 +467,8 @@ int launch_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const 
                 int64_t *ids, float *scores, void *ws, hipStream_t stream) {
   const int cb16 = ctx->code_bytes / 16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
   const int nm = mfma_count(cb16, sb16, w);
-  const TopkGeom g = topk_geom(nq, n, k, nm);
+  const bool blk = topk_block_path(ctx, k);
+  const TopkGeom g = blk ? topk_block_geom(ctx, nq, n, k) : topk_geom(nq, n, k, nm);
   uint8_t *base = reinterpret_cast<uint8_t *>(ws);
   uint8_t *prep = base;
   float *cand_s = reinterpret_cast<float *>(base + align256(g.groups * prep_stride(nm)));
@@ -295,6 +479,35 @@ int launch_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const 
     return TQ_ENOTSUP;
   int st = launch_prep(ctx, q, g.groups, 4, 1, nq, prep, stream);
   if (st != TQ_OK) return st;
+  if (blk) {
+    BlkArgs b{};
+    b.codes = codes;
+    b.signs = signs;
+    b.norms = norms;
+    b.rnorms = rnorms;
+    b.prep = prep;
+    b.cand_s = cand_s;
+    b.cand_i = cand_i;
+    b.n = n;
+    b.nq = nq;
+    b.chunk = g.chunk;
+    b.nchunk = g.nchunk;
+    b.cb16 = cb16;
+    b.sb16 = sb16;
+    b.nm = nm;
+    b.k = k;
+    b.alpha = ctx->alpha;
+    const size_t lds = (size_t)nm * 1024 + 4 * (size_t)(LIST + CBUF) * 8;
+    const void *fn = w == 3 ? reinterpret_cast<const void *>(&topk_block_kernel<3>)
+                            : reinterpret_cast<const void *>(&topk_block_kernel<1>);
+    if ((st = allow_lds(fn, lds)) != TQ_OK) return st;
+    const dim3 grid((unsigned)g.nchunk, (unsigned)g.groups);
+    if (w == 3)
+      topk_block_kernel<3><<<grid, 256, lds, stream>>>(b);
+    else
+      topk_block_kernel<1><<<grid, 256, lds, stream>>>(b);
+    if ((st = hip_status()) != TQ_OK) return st;
+  } else {
   ScanArgs a{};
   a.codes = codes;
   a.signs = signs;
@@ -314,6 +527,7 @@ int launch_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const 
   a.k = k;
   st = dispatch_scan(a, dim3((unsigned)g.nchunk, (unsigned)g.qblocks), cb16, sb16, w, g.kp, stream);
   if (st != TQ_OK) return st;
+  }
   int npow2 = 1;
   while (npow2 < g.ncand) npow2 <<= 1;
   const size_t lds = (size_t)npow2 * 8;

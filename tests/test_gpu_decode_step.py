@@ -48,7 +48,9 @@ def _clear_rows(p, G, d, seed, bf16):
 @pytest.mark.parametrize("d,kb,vb,G,qpg,ldk,pos,bf16", [
     (128, 3, 3, 3, 4, 700, 600, False), (128, 3, 3, 2, 4, 1100, 1024, True), (128, 3, 3, 2, 3, 64, 0, False),
     (128, 3, 3, 1, 8, 520, 511, True), (128, 4, 4, 2, 4, 300, 299, True), (128, 2, 2, 3, 4, 90, 50, False),
-    (64, 3, 3, 2, 4, 600, 555, False), (128, 3, 2, 2, 4, 400, 123, True)])
+    (64, 3, 3, 2, 4, 600, 555, False), (128, 3, 2, 2, 4, 400, 123, True),
+    # longer vectors: logits, value sum and combine in three steps
+    (256, 3, 3, 2, 4, 300, 257, True), (512, 4, 2, 1, 5, 200, 130, False)])
 def test_decode_step_matches_oracle(tq, d, kb, vb, G, qpg, ldk, pos, bf16):
     pk, pv = O.make_params(d, kb, 0), O.make_params(d, vb, 1, "mse")
     kctx, vctx = tq.Context(d, kb, 0), tq.Context(d, vb, 1, tq.TQ_MODE_MSE)

@@ -111,7 +111,7 @@ def test_topk_errors(tq):
     with pytest.raises(tq.TQError):
         tq.tq_topk(ctx, q, rec, 11)          # k > n
     with pytest.raises(tq.TQError):
-        tq.tq_topk(ctx, q, rec, 65)          # k > TQ_MAX_TOPK
+        tq.tq_topk(ctx, q, rec, 1025)        # k > TQ_MAX_TOPK
 
 
 @pytest.mark.parametrize("k", [10, 64])

@@ -38,6 +38,7 @@ def test_library_exports_every_declared_symbol():
 @pytest.mark.parametrize("d,bits,mode,seed", [
     (128, 3, "prod", 0), (128, 2, "prod", 1), (128, 4, "prod", 7), (200, 2, "prod", 0),
     (200, 4, "prod", 0), (64, 3, "mse", 1), (8, 1, "mse", 3), (256, 4, "mse", 5), (96, 3, "prod", 11),
+    (520, 3, "prod", 2), (1024, 4, "prod", 4), (1024, 2, "mse", 6),
 ])
 def test_host_params_match_oracle(d, bits, mode, seed):
     from oblivious_kv_cache_amd import binding as tq
@@ -51,7 +52,7 @@ def test_host_params_match_oracle(d, bits, mode, seed):
 
 def test_host_params_validation():
     from oblivious_kv_cache_amd import binding as tq
-    for d, bits, mode in [(7, 3, 0), (0, 3, 0), (264, 3, 0), (128, 1, 0), (128, 5, 0), (128, 0, 1),
+    for d, bits, mode in [(7, 3, 0), (0, 3, 0), (1032, 3, 0), (1020, 3, 0), (128, 1, 0), (128, 5, 0), (128, 0, 1),
                           (128, 5, 1), (128, 3, 2)]:
         with pytest.raises(tq.TQError) as e:
             tq.tq_host_params(d, bits, 0, mode)
