@@ -73,6 +73,8 @@ extern "C" {
 #define TQ_MODE_PROD 0     /* (bits-1)-bit codes + 1-bit QJL sketch, m = d */
 #define TQ_MODE_MSE  1     /* bits-bit codes only (no sketch)              */
 #define TQ_MODE_POLAR 2    /* bits-bit codes of the recursive polar angles  */
+#define TQ_MODE_FRAC  3    /* b = bits/2 (2.5, 3.5): codes of ceil(b)-1 and
+                              floor(b)-1 bits on the two halves + 1-bit QJL */
 
 /* ops for tq_workspace_size */
 #define TQ_OP_SCORES  1
@@ -93,12 +95,15 @@ typedef struct tq_ctx tq_ctx;
 typedef struct {
   int d;           /* vector dimension                                  */
   int m;           /* JL rows (= d in prod mode, 0 in mse mode)         */
-  int bits;        /* total bits per coordinate requested at init       */
-  int code_bits;   /* w: bits per scalar code (bits-1 prod, bits mse)   */
+  int bits;        /* total bits per coordinate requested at init
+                      (TQ_MODE_FRAC: twice the bits per coordinate)     */
+  int code_bits;   /* w: bits per scalar code (bits-1 prod, bits mse;
+                      TQ_MODE_FRAC: of the first half; the second
+                      half's codes have w - 1 bits)                     */
   int levels;      /* 2^w codebook entries                              */
   int code_bytes;  /* bytes per code record                             */
   int sign_bytes;  /* bytes per sign record (0 in mse mode)             */
-  int mode;        /* TQ_MODE_PROD or TQ_MODE_MSE                       */
+  int mode;        /* TQ_MODE_PROD, _MSE, _POLAR or _FRAC               */
 } tq_layout_t;
 
 /* Build a prod-mode context: Pi = Haar(d) as Q diag(sign R_ii) of the QR
@@ -129,6 +134,24 @@ int tq_init_mse(int d, int bits, uint64_t seed, tq_ctx **out);
  * calls (tq_scores, tq_attend, tq_topk, decode steps) return TQ_EINVAL. */
 int tq_init_polar(int d, int bits, uint64_t seed, tq_ctx **out);
 
+/* Fractional-width context, b = half_bits / 2 bits per coordinate with
+ * half_bits in {5, 7} (2.5 and 3.5 bits: suzuke blog, 實際跑出來的數據;
+ * xujun.org note 189244, 跑分全面碾压; the pages give no mechanism, and this
+ * is the library's reading).  Pi and S as tq_init with the same seed; the
+ * rotated coordinates 0 .. d/2-1 take codes of w_hi = ceil(b) - 1 bits, the
+ * rest w_lo = floor(b) - 1 bits, each half with the Lloyd-Max codebook for
+ * N(0, 1/d) at its width; one QJL sign bit per JL row (m = d) of the stage-1
+ * residual over all coordinates, so the estimator keeps its form.  Records:
+ * code_bytes = d (w_hi + w_lo) / 16 (no padding), laid out by coordinate
+ * quarter: quarter g (coordinates [g d/4, (g+1) d/4)) holds w_g bit planes of
+ * d/4 bits, plane p = bit p of the quarter's codes in order (w_g = w_hi for
+ * g < 2, else w_lo); sign records, norms and residual norms as tq_init.
+ * d in {128, 256}.  Such a context takes tq_quantize, tq_dequant and the
+ * scoring calls (tq_scores, tq_prep_queries, tq_scores_prepared(_timed),
+ * tq_scores_static); tq_attend, tq_topk and the decode steps return
+ * TQ_EINVAL. */
+int tq_init_frac(int d, int half_bits, uint64_t seed, tq_ctx **out);
+
 /* Host-only: the float64 angle codebooks a PolarQuant context holds, per level
  * l = 1..log2(d): c [log2 d][2^bits] centroids, t [log2 d][2^bits - 1]
  * thresholds (radians).  Either pointer may be NULL. */
@@ -143,14 +166,17 @@ int tq_layout(const tq_ctx *ctx, tq_layout_t *out);
 /* Host-only: compute the float64 parameters a context would hold, without a
  * GPU.  Pi [d*d] row-major, S [m*d] row-major (prod mode), c [2^w] ascending
  * centroids, t [2^w - 1] ascending thresholds (already scaled by 1/sqrt(d)).
- * Any output pointer may be NULL.  mode = TQ_MODE_PROD or TQ_MODE_MSE (else
- * TQ_EINVAL; see tq_polar_codebook for PolarQuant). */
+ * Any output pointer may be NULL.  mode = TQ_MODE_PROD, TQ_MODE_MSE or
+ * TQ_MODE_FRAC (bits = half_bits; c and t then hold the first half's codebook
+ * followed by the second's: 2^w_hi + 2^w_lo centroids, 2^w_hi + 2^w_lo - 2
+ * thresholds); else TQ_EINVAL (see tq_polar_codebook for PolarQuant). */
 int tq_host_params(int d, int bits, uint64_t seed, int mode,
                    double *Pi, double *S, double *c, double *t);
 
 /* Host copies of a context's float64 parameters (any pointer may be NULL);
  * for a PolarQuant context c and t are the per-level angle codebooks of
- * tq_polar_codebook (log2(d) x 2^bits and log2(d) x (2^bits - 1) doubles). */
+ * tq_polar_codebook (log2(d) x 2^bits and log2(d) x (2^bits - 1) doubles);
+ * for a fractional-width context both halves' codebooks, as tq_host_params. */
 int tq_get_params(const tq_ctx *ctx, double *Pi, double *S, double *c, double *t);
 
 /* Quantize n vectors (online append: any n >= 0).
@@ -184,7 +210,8 @@ int tq_workspace_size(const tq_ctx *ctx, int op, int64_t a, int64_t b, int64_t c
  *   logits [device] float [G][qpg][T]: raw inner-product estimates (no
  *          1/sqrt(d) scaling);
  *   ws     [device] >= tq_workspace_size(TQ_OP_SCORES, G, qpg) bytes.
- * Requires a prod-mode context; T >= 0, ldk >= T, 1 <= qpg <= TQ_MAX_QPG_SCORES
+ * Requires a prod-mode or fractional-width context; T >= 0, ldk >= T,
+ * 1 <= qpg <= TQ_MAX_QPG_SCORES
  * (TQ_EINVAL), G * ceil(qpg / 4) <= 65535 (TQ_ENOTSUP).  Queries are scored in
  * blocks of 4 against every key, so a large qpg (all positions of a prefill
  * against the same keys) is one call. */

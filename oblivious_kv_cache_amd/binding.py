@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(_HERE, "lib", "libtq.so"
 TQ_OK, TQ_EINVAL, TQ_ENOTSUP, TQ_ENOMEM, TQ_EHIP, TQ_ESCRATCH = 0, -1, -2, -3, -4, -5
 TQ_SCRATCH_BYTES = 16 << 20
 TQ_F32, TQ_BF16 = 0, 1
-TQ_MODE_PROD, TQ_MODE_MSE, TQ_MODE_POLAR = 0, 1, 2
+TQ_MODE_PROD, TQ_MODE_MSE, TQ_MODE_POLAR, TQ_MODE_FRAC = 0, 1, 2, 3
 TQ_OP_SCORES, TQ_OP_ATTEND, TQ_OP_TOPK = 1, 2, 3
 TQ_MAX_D, TQ_MAX_TOPK = 1024, 1024
 
@@ -26,7 +26,7 @@ EXPORTS = [
     "tq_quantize", "tq_workspace_size", "tq_scores", "tq_prep_queries", "tq_scores_prepared",
     "tq_scores_prepared_timed",
     "tq_softmax", "tq_attend", "tq_decode_prep", "tq_decode_step", "tq_dequant", "tq_topk",
-    "tq_scores_static", "tq_init_polar", "tq_polar_codebook", "tq_strerror",
+    "tq_scores_static", "tq_init_polar", "tq_polar_codebook", "tq_init_frac", "tq_strerror",
 ]
 
 
@@ -63,6 +63,7 @@ def _load():
         "tq_init": (I, [I, I, U64, ctypes.POINTER(P)]),
         "tq_init_mse": (I, [I, I, U64, ctypes.POINTER(P)]),
         "tq_init_polar": (I, [I, I, U64, ctypes.POINTER(P)]),
+        "tq_init_frac": (I, [I, I, U64, ctypes.POINTER(P)]),
         "tq_polar_codebook": (I, [I, I, D, D]),
         "tq_free": (None, [P]),
         "tq_layout": (I, [P, ctypes.POINTER(tq_layout_t)]),
@@ -134,7 +135,7 @@ def _check_records(ctx, rec, nrec, what, device=None):
     if nrec <= 0:
         return
     parts = [("codes", torch.uint8, ctx.code_bytes), ("norms", torch.float32, 1)]
-    if ctx.mode == TQ_MODE_PROD:
+    if ctx.sketch:
         parts += [("signs", torch.uint8, ctx.sign_bytes), ("rnorms", torch.float32, 1)]
     for key, dt, per in parts:
         _check_tensor(f"{what} {key}", rec.get(key), dt, nrec * per, check_device=False)
@@ -181,14 +182,19 @@ def _dp(a):
 def tq_host_params(d, bits, seed, mode=TQ_MODE_PROD):
     """Host-only float64 parameters (Pi, S, c, t) a context would hold; needs no GPU."""
     import numpy as np
-    w = bits - 1 if mode == TQ_MODE_PROD else bits
-    m = d if mode == TQ_MODE_PROD else 0
+    if mode == TQ_MODE_FRAC:          # bits = twice the bits per coordinate: both halves' codebooks
+        n = 2 ** ((bits + 1) // 2 - 1) + 2 ** (bits // 2 - 1) if bits in (5, 7) else 1
+        m = d
+    else:
+        w = bits - 1 if mode == TQ_MODE_PROD else bits
+        n = 2 ** w if 1 <= w <= 4 else 1
+        m = d if mode == TQ_MODE_PROD else 0
     Pi = np.zeros((d, d))
     S = np.zeros((max(m, 1), d))
-    c = np.zeros(2 ** w) if 1 <= w <= 4 else np.zeros(1)
-    t = np.zeros(max(2 ** w - 1, 1))
+    c = np.zeros(n)
+    t = np.zeros(max(n - 1, 1))
     _check(LIB.tq_host_params(d, bits, seed, mode, _dp(Pi), _dp(S), _dp(c), _dp(t)), "tq_host_params")
-    return Pi, S[:m], c, t
+    return Pi, S[:m], c, t[:n - 2] if mode == TQ_MODE_FRAC else t
 
 
 def tq_polar_codebook(d, bits):
@@ -207,7 +213,8 @@ class Context:
 
     def __init__(self, d, bits, seed=0, mode=TQ_MODE_PROD):
         h = ctypes.c_void_p()
-        fn = {TQ_MODE_PROD: LIB.tq_init, TQ_MODE_MSE: LIB.tq_init_mse, TQ_MODE_POLAR: LIB.tq_init_polar}[mode]
+        fn = {TQ_MODE_PROD: LIB.tq_init, TQ_MODE_MSE: LIB.tq_init_mse, TQ_MODE_POLAR: LIB.tq_init_polar,
+              TQ_MODE_FRAC: LIB.tq_init_frac}[mode]
         _check(fn(int(d), int(bits), int(seed), ctypes.byref(h)), "tq_init")
         self.handle = h
         lay = tq_layout_t()
@@ -216,6 +223,8 @@ class Context:
         self.d, self.m, self.bits, self.w = lay.d, lay.m, lay.bits, lay.code_bits
         self.code_bytes, self.sign_bytes, self.mode = lay.code_bytes, lay.sign_bytes, lay.mode
         self.seed = seed
+        # records with a QJL sketch (signs and residual norms)
+        self.sketch = self.mode in (TQ_MODE_PROD, TQ_MODE_FRAC)
 
     def close(self):
         if getattr(self, "handle", None):
@@ -231,6 +240,12 @@ class Context:
     def params(self):
         import numpy as np
         d, m, L = self.d, self.m, 2 ** self.w
+        if self.mode == TQ_MODE_FRAC:     # both halves' codebooks, first then second
+            Pi, S = np.zeros((d, d)), np.zeros((m, d))
+            n = L + L // 2
+            c, t = np.zeros(n), np.zeros(n - 2)
+            _check(LIB.tq_get_params(self.handle, _dp(Pi), _dp(S), _dp(c), _dp(t)), "tq_get_params")
+            return Pi, S, (c[:L], c[L:]), (t[:L - 1], t[L - 1:])
         nl = d.bit_length() - 1 if self.mode == TQ_MODE_POLAR else 1   # polar: a codebook per level
         Pi, S = np.zeros((d, d)), np.zeros((max(m, 1), d))
         c, t = np.zeros(nl * L), np.zeros(max(nl * (L - 1), 1))
@@ -247,7 +262,7 @@ class Context:
 
     def empty_records(self, n, device="cuda"):
         """Allocate packed-record buffers for n vectors."""
-        prod = self.mode == TQ_MODE_PROD
+        prod = self.sketch
         return {
             "codes": torch.zeros((n, self.code_bytes), dtype=torch.uint8, device=device),
             "signs": torch.zeros((n, self.sign_bytes), dtype=torch.uint8, device=device) if prod else None,

@@ -33,6 +33,11 @@ void split_bf16(double x, uint16_t &hi, uint16_t &lo) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// contexts whose records carry a QJL sketch (the estimator's inputs)
+bool scoring_mode(const tq_ctx *ctx) {
+  return ctx->hp.mode == TQ_MODE_PROD || ctx->hp.mode == TQ_MODE_FRAC;
+}
+
 int current_device_matches(const tq_ctx *ctx) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return TQ_EHIP;
@@ -46,12 +51,12 @@ int current_device_matches(const tq_ctx *ctx) {
 // with the row permutation sigma(u, r) = (r / 4) * P + 4 u + (r % 4), which
 // hands lane group g the coordinates [g P, (g+1) P).
 //
-// For d > 256 (the kernel that stages vectors in LDS) there is no
-// permutation: row = 16 u + r and column 32 k + 8 g + e for both GEMMs.
+// For the kernel that stages vectors in LDS (d > 256, and the fractional
+// widths) there is no permutation: row = 16 u + r and column 32 k + 8 g + e
+// for both GEMMs.
 void build_frags(const tq::HostParams &hp, int dpad, const double *M, int rows, int cols,
-                 bool gemm2, Frag *hi, Frag *lo) {
+                 bool gemm2, bool plain, Frag *hi, Frag *lo) {
   const int NT = dpad / 16, NK = dpad / 32, P = dpad / 4;
-  const bool plain = dpad > 256;
   for (int u = 0; u < NT; ++u)
     for (int k = 0; k < NK; ++k)
       for (int l = 0; l < 64; ++l) {
@@ -87,31 +92,42 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
   }
   const tq::HostParams &hp = ctx->hp;
   const int m = hp.m, w = hp.w, L = hp.levels;
+  const bool frac = mode == TQ_MODE_FRAC;
+  ctx->frac = frac ? 1 : 0;
   ctx->dpad = d <= 32 ? 32 : d <= 64 ? 64 : d <= 128 ? 128 : d <= 256 ? 256 : (d + 31) / 32 * 32;
-  ctx->code_bytes = ((d * w + 7) / 8 + 15) / 16 * 16;
+  // fractional mode: planar quarters, no padding (d in {128, 256})
+  ctx->code_bytes = frac ? d * (w + hp.w2) / 16 : ((d * w + 7) / 8 + 15) / 16 * 16;
   ctx->sign_bytes = m ? ((m + 7) / 8 + 15) / 16 * 16 : 0;
+  ctx->cw16 = frac ? w * d / 128 : ctx->code_bytes / 16;
   ctx->alpha = m ? (float)(std::sqrt(M_PI / 2.0) / m) : 0.f;
-  for (int k = 0; k < L; ++k) ctx->cf[k] = (float)hp.c[k];
-  for (int j = 0; j < L / 2; ++j) ctx->cpos[j] = (float)hp.c[L / 2 + j];
-  for (int j = 0; j + 1 < L / 2; ++j) ctx->tpos[j] = (float)hp.t[L / 2 + j];
-  // odd multilinear coefficients of the antisymmetric codebook in the sign
+  // centroids (all, and the positive half), positive thresholds, and the odd
+  // multilinear coefficients of the antisymmetric codebook in the sign
   // variables s_p = 2 bit_p - 1 (p = 0..w-1) and, for w = 3, s0 s1 s2
-  for (int p = 0; p < 4; ++p) {
-    double acc = 0.0;
-    for (int idx = 0; idx < L; ++idx) {
-      double s;
-      if (p < w && p < 3) {
-        s = ((idx >> p) & 1) ? 1.0 : -1.0;
-      } else if (p == 3 && w == 3) {
-        s = 1.0;
-        for (int b = 0; b < 3; ++b) s *= ((idx >> b) & 1) ? 1.0 : -1.0;
-      } else {
-        s = 0.0;
+  auto codebook = [](const std::vector<double> &c, const std::vector<double> &t, int cw, float *cf,
+                     float *cpos, float *tpos, float *basis) {
+    const int n = 1 << cw;
+    for (int k = 0; k < n; ++k) cf[k] = (float)c[k];
+    for (int j = 0; j < n / 2; ++j) cpos[j] = (float)c[n / 2 + j];
+    for (int j = 0; j + 1 < n / 2; ++j) tpos[j] = (float)t[n / 2 + j];
+    for (int p = 0; p < 4; ++p) {
+      double acc = 0.0;
+      for (int idx = 0; idx < n; ++idx) {
+        double s;
+        if (p < cw && p < 3) {
+          s = ((idx >> p) & 1) ? 1.0 : -1.0;
+        } else if (p == 3 && cw == 3) {
+          s = 1.0;
+          for (int b = 0; b < 3; ++b) s *= ((idx >> b) & 1) ? 1.0 : -1.0;
+        } else {
+          s = 0.0;
+        }
+        acc += c[idx] * s;
       }
-      acc += hp.c[idx] * s;
+      basis[p] = (float)(acc / n);
     }
-    ctx->basis[p] = (float)(acc / L);
-  }
+  };
+  if (mode != TQ_MODE_POLAR) codebook(hp.c, hp.t, w, ctx->cf, ctx->cpos, ctx->tpos, ctx->basis);
+  if (frac) codebook(hp.c2, hp.t2, hp.w2, ctx->cf2, ctx->cpos2, ctx->tpos2, ctx->basis2);
   // the same expansion with every odd monomial of up to 4 code bits: the w
   // single bits, then the products of three bits (w = 3: {012}; w = 4:
   // {012, 013, 023, 123}); used by the value sum of the attention kernel
@@ -169,7 +185,8 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
       ST32[(size_t)j * m + i] = (float)hp.S[(size_t)i * d + j];
     }
   Frag *fr = reinterpret_cast<Frag *>(host.data() + (bytes_f32 + 255) / 256 * 256);
-  build_frags(hp, dpad, hp.Pi.data(), d, d, false, fr, fr + nfr);
+  const bool plain = dpad > 256 || frac;      // the LDS-staged quantize kernel
+  build_frags(hp, dpad, hp.Pi.data(), d, d, false, plain, fr, fr + nfr);
   if (m) {
     std::vector<double> Sp((size_t)m * d, 0.0);   // S' = S Pi^T
     for (int i = 0; i < m; ++i)
@@ -178,7 +195,7 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
         for (int j = 0; j < d; ++j) acc += hp.S[(size_t)i * d + j] * hp.Pi[(size_t)k * d + j];
         Sp[(size_t)i * d + k] = acc;
       }
-    build_frags(hp, dpad, Sp.data(), m, d, true, fr + 2 * nfr, fr + 3 * nfr);
+    build_frags(hp, dpad, Sp.data(), m, d, true, plain, fr + 2 * nfr, fr + 3 * nfr);
   }
   float *pol = reinterpret_cast<float *>(host.data() + (bytes_f32 + 255) / 256 * 256 + bytes_fr);
   if (polar) {
@@ -233,7 +250,7 @@ namespace tq {
 int check_scores_call(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, int64_t ldk,
                       const uint8_t *codes, const uint8_t *signs, const float *norms,
                       const float *rnorms, const float *logits) {
-  if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
+  if (!ctx || !scoring_mode(ctx)) return TQ_EINVAL;
   if (G < 0 || T < 0 || ldk < T || qpg < 1 || qpg > TQ_MAX_QPG_SCORES) return TQ_EINVAL;
   if (G == 0 || T == 0) return TQ_OK;
   if (!q || !codes || !signs || !norms || !rnorms || !logits) return TQ_EINVAL;
@@ -257,6 +274,10 @@ int tq_init_mse(int d, int bits, uint64_t seed, tq_ctx **out) {
 
 int tq_init_polar(int d, int bits, uint64_t seed, tq_ctx **out) {
   return make_ctx(d, bits, seed, TQ_MODE_POLAR, out);
+}
+
+int tq_init_frac(int d, int half_bits, uint64_t seed, tq_ctx **out) {
+  return make_ctx(d, half_bits, seed, TQ_MODE_FRAC, out);
 }
 
 int tq_polar_codebook(int d, int bits, double *c, double *t) {
@@ -292,8 +313,14 @@ int tq_get_params(const tq_ctx *ctx, double *Pi, double *S, double *c, double *t
   const tq::HostParams &hp = ctx->hp;
   if (Pi) std::memcpy(Pi, hp.Pi.data(), hp.Pi.size() * sizeof(double));
   if (S && hp.m) std::memcpy(S, hp.S.data(), hp.S.size() * sizeof(double));
-  if (c) std::memcpy(c, hp.c.data(), hp.c.size() * sizeof(double));
-  if (t) std::memcpy(t, hp.t.data(), hp.t.size() * sizeof(double));
+  if (c) {
+    std::memcpy(c, hp.c.data(), hp.c.size() * sizeof(double));
+    if (!hp.c2.empty()) std::memcpy(c + hp.c.size(), hp.c2.data(), hp.c2.size() * sizeof(double));
+  }
+  if (t) {
+    std::memcpy(t, hp.t.data(), hp.t.size() * sizeof(double));
+    if (!hp.t2.empty()) std::memcpy(t + hp.t.size(), hp.t2.data(), hp.t2.size() * sizeof(double));
+  }
   return TQ_OK;
 }
 
@@ -302,7 +329,7 @@ int tq_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t 
                 hipStream_t stream) {
   if (!ctx || n < 0 || ldr < 1) return TQ_EINVAL;
   if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EINVAL;
-  const bool prod = ctx->hp.mode == TQ_MODE_PROD;
+  const bool prod = ctx->hp.mode == TQ_MODE_PROD || ctx->hp.mode == TQ_MODE_FRAC;
   if (n == 0) return TQ_OK;
   if (!x || !codes || !norms) return TQ_EINVAL;
   if (prod ? (!signs || !rnorms) : (signs || rnorms)) return TQ_EINVAL;
@@ -322,7 +349,7 @@ int tq_workspace_size(const tq_ctx *ctx, int op, int64_t a, int64_t b, int64_t c
   if (!ctx || !bytes || a < 0 || b < 0 || c < 0) return TQ_EINVAL;
   switch (op) {
     case TQ_OP_SCORES:
-      if (ctx->hp.mode != TQ_MODE_PROD || b < 1 || b > TQ_MAX_QPG_SCORES) return TQ_EINVAL;
+      if (!scoring_mode(ctx) || b < 1 || b > TQ_MAX_QPG_SCORES) return TQ_EINVAL;
       *bytes = tq::scores_ws_bytes(ctx, a, (int)b);
       return TQ_OK;
     case TQ_OP_ATTEND:
@@ -351,7 +378,7 @@ int tq_scores(const tq_ctx *ctx, const float *q, int64_t G, int qpg, int64_t T, 
 
 int tq_prep_queries(const tq_ctx *ctx, const float *q, int64_t G, int qpg, void *ws,
                     size_t ws_bytes, hipStream_t stream) {
-  if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
+  if (!ctx || !scoring_mode(ctx)) return TQ_EINVAL;
   if (G < 0 || qpg < 1 || qpg > TQ_MAX_QPG_SCORES) return TQ_EINVAL;
   if (G == 0) return TQ_OK;
   if (!q || !ws || !aligned(q, 4) || !aligned(ws, 16)) return TQ_EINVAL;
@@ -373,7 +400,7 @@ int tq_scores_prepared_timed(const tq_ctx *ctx, const void *ws, size_t ws_bytes,
                              int64_t T, int64_t ldk, const uint8_t *codes, const uint8_t *signs,
                              const float *norms, const float *rnorms, float *logits,
                              hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  if (!ctx || ctx->hp.mode != TQ_MODE_PROD) return TQ_EINVAL;
+  if (!ctx || !scoring_mode(ctx)) return TQ_EINVAL;
   if (G < 0 || T < 0 || ldk < T || qpg < 1 || qpg > TQ_MAX_QPG_SCORES) return TQ_EINVAL;
   if (G == 0 || T == 0) return TQ_OK;
   if (!ws || !codes || !signs || !norms || !rnorms || !logits) return TQ_EINVAL;
@@ -514,7 +541,7 @@ int tq_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs, co
                const float *rnorms, int64_t n, float *out, hipStream_t stream) {
   if (!ctx || n < 0) return TQ_EINVAL;
   if (n == 0) return TQ_OK;
-  const bool prod = ctx->hp.mode == TQ_MODE_PROD;
+  const bool prod = scoring_mode(ctx);
   if (!codes || !norms || !out || (prod && (!signs || !rnorms))) return TQ_EINVAL;
   if (!aligned(codes, 16) || (prod && !aligned(signs, 16)) || !aligned(norms, 4) || !aligned(out, 4))
     return TQ_EINVAL;

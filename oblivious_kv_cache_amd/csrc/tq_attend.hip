@@ -682,7 +682,7 @@ __global__ void __launch_bounds__(256) attend_vsum_kernel(VsumArgs a) {
 
 size_t attend_ws_bytes(const tq_ctx *k, int64_t G, int qpg, int64_t T) {
   const int hg = (qpg + 3) / 4;
-  const int nm = mfma_count(k->code_bytes / 16, k->sign_bytes / 16, k->hp.w);
+  const int nm = mfma_count(k->cw16, k->sign_bytes / 16, k->hp.w);
   const int64_t nchunk = (T + CH - 1) / CH;
   const int d = k->hp.d;
   // d > 128: the logits of the three-step path as well
@@ -715,7 +715,7 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   int st = check_attend(kc, vc, G, qpg, T, ldk, probs != nullptr);
   if (st != TQ_OK) return st;
   const int hg = (qpg + 3) / 4;
-  const int cb16 = kc->code_bytes / 16, sb16 = kc->sign_bytes / 16, w = kc->hp.w;
+  const int cb16 = kc->cw16, sb16 = kc->sign_bytes / 16, w = kc->hp.w;
   const int nm = mfma_count(cb16, sb16, w);
   const int64_t nchunk = (T + CH - 1) / CH;
   const int64_t groups = G * hg;

@@ -30,6 +30,10 @@ struct QBigArgs {
   const Frag *PiH, *PiL, *SH, *SL;
   int d, m, dpad, w, code_bytes, sign_bytes;
   float tpos[8], cpos[8];
+  // fractional widths: coordinates d/2 .. d-1 take w2-bit codes (tpos2,
+  // cpos2), and the codes are stored as bit planes per coordinate quarter
+  int frac, w2;
+  float tpos2[8], cpos2[8];
 };
 
 template <bool BF16IN>
@@ -48,7 +52,7 @@ __global__ void __launch_bounds__(256) quantize_big_kernel(QBigArgs a) {
   float *rsw = vnu + 16;                                         // [4 waves][16] sum of r^2
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, col = lane & 15, grp = lane >> 4;
-  const int half = (1 << a.w) / 2;
+  const int qd = a.d / 4, wpp = a.d / 128;       // fractional layout: quarter size, words per plane
 
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     // ---- 1: the 16 vectors' lengths (fp64), then their operand fragments;
@@ -114,6 +118,11 @@ __global__ void __launch_bounds__(256) quantize_big_kernel(QBigArgs a) {
     const float inv = vinv[col];
     float rs = 0.f;
     for (int u = wv; u < NT; u += 4) {
+      // the tile's 16 coordinates lie in one half (d/2 is a multiple of 16)
+      const bool second = a.frac && 16 * u >= a.d / 2;
+      const int cw = second ? a.w2 : a.w;
+      const int half = (1 << cw) / 2;
+      const float *tp = second ? a.tpos2 : a.tpos, *cp = second ? a.cpos2 : a.cpos;
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int k = 0; k < NK; ++k) {
         const bf16x8 ah = as_bf(a.PiH[(u * NK + k) * 64 + lane]);
@@ -129,11 +138,11 @@ __global__ void __launch_bounds__(256) quantize_big_kernel(QBigArgs a) {
         const float y = acc[jj] * inv;
         const uint32_t yb = __float_as_uint(y), ab = yb & 0x7fffffffu;
         uint32_t mm = 0;
-        float cm = a.cpos[0];
+        float cm = cp[0];
         for (int j = 0; j < half - 1; ++j) {
-          const bool gt = __uint_as_float(ab) > a.tpos[j];
+          const bool gt = __uint_as_float(ab) > tp[j];
           mm += gt ? 1u : 0u;
-          cm = gt ? a.cpos[j + 1] : cm;
+          cm = gt ? cp[j + 1] : cm;
         }
         // idx = half + mm for y >= +0, its mirror for y <= -0; r = y - c[idx]
         const uint32_t neg = (uint32_t)((int32_t)yb >> 31);
@@ -144,10 +153,18 @@ __global__ void __launch_bounds__(256) quantize_big_kernel(QBigArgs a) {
           r = 0.f;
         }
         rs += r * r;
-        const int bit = i * a.w;
-        if (idx) {
-          atomicOr(&cwl[col * cwn + (bit >> 5)], idx << (bit & 31));
-          if ((bit & 31) + a.w > 32) atomicOr(&cwl[col * cwn + (bit >> 5) + 1], idx >> (32 - (bit & 31)));
+        if (a.frac) {
+          // quarter g holds its w_g bit planes of qd bits each, quarters in order
+          const int g = i / qd, jq = i - g * qd;
+          const int base = g < 2 ? g * a.w * wpp : 2 * a.w * wpp + (g - 2) * a.w2 * wpp;
+          for (int pl = 0; pl < cw; ++pl)
+            if ((idx >> pl) & 1u) atomicOr(&cwl[col * cwn + base + pl * wpp + (jq >> 5)], 1u << (jq & 31));
+        } else {
+          const int bit = i * a.w;
+          if (idx) {
+            atomicOr(&cwl[col * cwn + (bit >> 5)], idx << (bit & 31));
+            if ((bit & 31) + a.w > 32) atomicOr(&cwl[col * cwn + (bit >> 5) + 1], idx >> (32 - (bit & 31)));
+          }
         }
         if (a.m > 0) {
           const __bf16 h = (__bf16)r, l = (__bf16)(r - (float)h);
@@ -229,6 +246,9 @@ struct PrepBigArgs {
   int64_t nq_total;
   int d, m, w, qpg, hg, cb, sb, nm;
   float basis[4];
+  int cw16;            // code words per lane group
+  int frac, w2;        // fractional widths: the second half's code bits and codebook
+  float basis2[4];
 };
 
 __global__ void __launch_bounds__(256) proj_big_kernel(PrepBigArgs a) {
@@ -298,21 +318,41 @@ __global__ void __launch_bounds__(256) frag_big_kernel(PrepBigArgs a) {
   // |coefficient| 2^-(bit & 7) of each chain
   float sP[4] = {0.f, 0.f, 0.f, 0.f}, sQ[4] = {0.f, 0.f, 0.f, 0.f};
   float mP[4] = {0.f, 0.f, 0.f, 0.f}, mQ[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int i = tid; i < d; i += 256)
+  const float bsum1 = a.basis[0] + (w >= 2 ? a.basis[1] : 0.f) + (w >= 3 ? a.basis[2] + a.basis[3] : 0.f);
+  const float bsum2 = a.basis2[0] + (a.w2 >= 2 ? a.basis2[1] : 0.f);
+  const int qd = d / 4, wpp = d / 128;
+  // fractional widths: sum_i (sum of coordinate i's basis) q_rot[i] directly
+  for (int i = tid; i < d; i += 256) {
+    const float wt = a.frac ? (i < d / 2 ? bsum1 : bsum2) : 1.f;
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) sP[hh] += qr(hh, i);
+    for (int hh = 0; hh < 4; ++hh) sP[hh] = fmaf(wt, qr(hh, i), sP[hh]);
+  }
   for (int j = tid; j < m; j += 256)
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
       sQ[hh] += qs(hh, j);
       mQ[hh] = fmaxf(mQ[hh], ldexpf(fabsf(2.f * qs(hh, j)), -(j & 7)));
     }
-  for (int pos = tid; pos < d * w; pos += 256) {
-    const int i = pos / w, p = pos - i * w;
+  if (a.frac) {
+    // bit (plane pl, coordinate i) sits at bit (i mod qd) & 7 of its byte
+    for (int i = tid; i < d; i += 256) {
+      const bool second = i >= d / 2;
+      const int cw = second ? a.w2 : w, e = (i % qd) & 7;
+      const float *bs = second ? a.basis2 : a.basis;
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(2.f * a.basis[p] * qr(hh, i)), -(pos & 7)));
-      if (w == 3 && p == 0) mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(2.f * a.basis[3] * qr(hh, i)), -(pos & 7)));
+      for (int hh = 0; hh < 4; ++hh) {
+        for (int pl = 0; pl < cw; ++pl) mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(2.f * bs[pl] * qr(hh, i)), -e));
+        if (cw == 3) mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(2.f * bs[3] * qr(hh, i)), -e));
+      }
+    }
+  } else {
+    for (int pos = tid; pos < d * w; pos += 256) {
+      const int i = pos / w, p = pos - i * w;
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(2.f * a.basis[p] * qr(hh, i)), -(pos & 7)));
+        if (w == 3 && p == 0) mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(2.f * a.basis[3] * qr(hh, i)), -(pos & 7)));
+      }
     }
   }
 #pragma unroll
@@ -338,7 +378,7 @@ __global__ void __launch_bounds__(256) frag_big_kernel(PrepBigArgs a) {
     mx1 = fmaxf(mx1, redall[i][hh][3]);
   }
   const float sc0 = mx0 > 0.f ? 127.f / mx0 : 1.f, sc1 = mx1 > 0.f ? 127.f / mx1 : 1.f;
-  const int cwpl = a.cb / 16, swpl = a.sb / 16;
+  const int cwpl = a.cw16, swpl = a.sb / 16;
   const int nmc = 2 * cwpl, nmp = 2 * parity_words(cwpl, w);
   for (int mu = 0; mu < a.nm; ++mu) {
     int mloc, wpl, kind;          // kind 0: code bits, 1: merged parity bits, 2: sign bits
@@ -358,10 +398,20 @@ __global__ void __launch_bounds__(256) frag_big_kernel(PrepBigArgs a) {
       const int q = 8 * b + j;
       // merged parity word `pair`: bit q belongs to the code starting at bit
       // q of record word g*wpl + p, p = 3 pair + ((q - g*wpl) mod 3), if any
-      const int p = kind == 1 ? 3 * pair + ((q - g * wpl) % 3 + 3) % 3 : pair;
+      const int p = kind == 1 && !a.frac ? 3 * pair + ((q - g * wpl) % 3 + 3) % 3 : pair;
       const int bitpos = 32 * (g * wpl + p) + q;
       float vcoef = 0.f;
-      if (p < wpl) {
+      if (a.frac && kind != 2) {
+        // word slot p of lane group g: plane p / wpp of the quarter's
+        // coordinates 32 (p mod wpp) .. +31; the parity words (3-bit codes,
+        // first half only) are the planes' XOR, one per plane word
+        const int cw = g < 2 ? w : a.w2;
+        const float *bs = g < 2 ? a.basis : a.basis2;
+        const int pl = kind == 0 ? p / wpp : 0, jw = kind == 0 ? p % wpp : p;
+        const int i = g * qd + 32 * jw + q;
+        if (kind == 0 && pl < cw) vcoef = 2.f * bs[pl] * qr(hh, i);
+        if (kind == 1 && cw == 3 && p < wpp) vcoef = 2.f * bs[3] * qr(hh, i);
+      } else if (p < wpl) {
         if (kind == 0) {
           const int i = bitpos / w, pl = bitpos - i * w;
           if (i < d) vcoef = 2.f * a.basis[pl] * qr(hh, i);
@@ -396,11 +446,10 @@ __global__ void __launch_bounds__(256) frag_big_kernel(PrepBigArgs a) {
       x0 = fmaxf(x0, redall[i][h4][2]);
       x1 = fmaxf(x1, redall[i][h4][3]);
     }
-    const float bsum = a.basis[0] + (w >= 2 ? a.basis[1] : 0.f) + (w >= 3 ? a.basis[2] + a.basis[3] : 0.f);
     float *cst = reinterpret_cast<float *>(out + (int64_t)a.nm * 1024);
     cst[h4 * 4 + 0] = x0 > 0.f ? 1.f / (127.f / x0) : 1.f;
     cst[h4 * 4 + 1] = x1 > 0.f ? 1.f / (127.f / x1) : 1.f;
-    cst[h4 * 4 + 2] = bsum * s0;
+    cst[h4 * 4 + 2] = a.frac ? s0 : bsum1 * s0;
     cst[h4 * 4 + 3] = s1;
   }
 }
@@ -433,7 +482,11 @@ int launch_quantize_big(const tq_ctx *ctx, const void *x, int dtype, int64_t n, 
   for (int j = 0; j < 8; ++j) {
     a.tpos[j] = ctx->tpos[j];
     a.cpos[j] = ctx->cpos[j];
+    a.tpos2[j] = ctx->tpos2[j];
+    a.cpos2[j] = ctx->cpos2[j];
   }
+  a.frac = ctx->frac;
+  a.w2 = ctx->hp.w2;
   const bool bf16 = dtype == TQ_BF16;
   const int NK = a.dpad / 32;
   const size_t frag_bytes = sizeof(Frag) * 64 * (size_t)NK * ((bf16 ? 1 : 2) + 2);
@@ -465,8 +518,14 @@ int launch_prep_big(const tq_ctx *ctx, const float *q, int64_t groups, int qpg, 
   a.hg = hg;
   a.cb = ctx->code_bytes;
   a.sb = ctx->sign_bytes;
-  a.nm = mfma_count(ctx->code_bytes / 16, ctx->sign_bytes / 16, ctx->hp.w);
-  for (int i = 0; i < 4; ++i) a.basis[i] = ctx->basis[i];
+  a.nm = mfma_count(ctx->cw16, ctx->sign_bytes / 16, ctx->hp.w);
+  for (int i = 0; i < 4; ++i) {
+    a.basis[i] = ctx->basis[i];
+    a.basis2[i] = ctx->basis2[i];
+  }
+  a.cw16 = ctx->cw16;
+  a.frac = ctx->frac;
+  a.w2 = ctx->hp.w2;
   if (groups == 0) return TQ_OK;
   if (groups > 0x7fffffff) return TQ_ENOTSUP;
   const unsigned cblocks = (unsigned)((a.d + a.m + 63) / 64);

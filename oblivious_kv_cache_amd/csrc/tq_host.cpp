@@ -222,6 +222,13 @@ int build_host_params(int d, int bits, uint64_t seed, int mode, HostParams &hp) 
     if (bits < 1 || bits > 4) return TQ_EINVAL;
     hp.w = bits;
     hp.m = 0;
+  } else if (mode == TQ_MODE_FRAC) {
+    // bits = twice the bits per coordinate; quarters of d/4 coordinates are
+    // whole 32-bit plane words
+    if ((bits != 5 && bits != 7) || (d != 128 && d != 256)) return TQ_EINVAL;
+    hp.w = (bits + 1) / 2 - 1;
+    hp.w2 = bits / 2 - 1;
+    hp.m = d;
   } else {
     return TQ_EINVAL;
   }
@@ -265,6 +272,13 @@ int build_host_params(int d, int bits, uint64_t seed, int mode, HostParams &hp) 
   hp.t.resize(t.size());
   for (size_t k = 0; k < c.size(); ++k) hp.c[k] = c[k] * s;
   for (size_t k = 0; k < t.size(); ++k) hp.t[k] = t[k] * s;
+  if (mode == TQ_MODE_FRAC) {
+    lloyd_max_unit_gaussian(1 << hp.w2, c, t);
+    hp.c2.resize(c.size());
+    hp.t2.resize(t.size());
+    for (size_t k = 0; k < c.size(); ++k) hp.c2[k] = c[k] * s;
+    for (size_t k = 0; k < t.size(); ++k) hp.t2[k] = t[k] * s;
+  }
   return TQ_OK;
 }
 
@@ -274,13 +288,19 @@ extern "C" int tq_host_params(int d, int bits, uint64_t seed, int mode, double *
                               double *c, double *t) {
   // prod and MSE-only contexts (a PolarQuant context's codebooks come from
   // tq_polar_codebook: their size differs)
-  if (mode != TQ_MODE_PROD && mode != TQ_MODE_MSE) return TQ_EINVAL;
+  if (mode != TQ_MODE_PROD && mode != TQ_MODE_MSE && mode != TQ_MODE_FRAC) return TQ_EINVAL;
   tq::HostParams hp;
   const int st = tq::build_host_params(d, bits, seed, mode, hp);
   if (st != TQ_OK) return st;
   if (Pi) std::memcpy(Pi, hp.Pi.data(), hp.Pi.size() * sizeof(double));
   if (S && hp.m) std::memcpy(S, hp.S.data(), hp.S.size() * sizeof(double));
-  if (c) std::memcpy(c, hp.c.data(), hp.c.size() * sizeof(double));
-  if (t) std::memcpy(t, hp.t.data(), hp.t.size() * sizeof(double));
+  if (c) {
+    std::memcpy(c, hp.c.data(), hp.c.size() * sizeof(double));
+    if (!hp.c2.empty()) std::memcpy(c + hp.c.size(), hp.c2.data(), hp.c2.size() * sizeof(double));
+  }
+  if (t) {
+    std::memcpy(t, hp.t.data(), hp.t.size() * sizeof(double));
+    if (!hp.t2.empty()) std::memcpy(t + hp.t.size(), hp.t2.data(), hp.t2.size() * sizeof(double));
+  }
   return TQ_OK;
 }

@@ -12,12 +12,14 @@ namespace tq {
 
 struct HostParams {
   int d = 0, m = 0, bits = 0, w = 0, levels = 0, mode = 0;
+  int w2 = 0;              // fractional mode: code bits of the second half (w: the first)
   uint64_t seed = 0;
   std::vector<double> Pi;  // [d][d] row-major
   std::vector<double> S;   // [m][d] row-major
   std::vector<double> c;   // [levels] ascending, for N(0, 1/d); polar mode:
                            // [log2 d][levels], the angle codebook of every level
   std::vector<double> t;   // [levels-1] ascending; polar mode: [log2 d][levels-1]
+  std::vector<double> c2, t2;   // fractional mode: the second half's codebook
 };
 
 int build_host_params(int d, int bits, uint64_t seed, int mode, HostParams &hp);
@@ -45,6 +47,12 @@ struct tq_ctx {
   float cf[16] = {};   // all centroids, fp32
   float basis[4] = {}; // odd-basis coefficients of the codebook (see tq_scores.hip)
   float vbasis[8] = {}; // all odd monomials of up to 4 code bits: w singles, then triples
+  // fractional mode (TQ_MODE_FRAC): the second half's codebook
+  int frac = 0;
+  float cpos2[8] = {}, tpos2[8] = {}, cf2[16] = {}, basis2[4] = {};
+  // record words per lane group of the scoring kernels (code_bytes / 16, or
+  // the first half's w d/128 planar words in fractional mode)
+  int cw16 = 0;
   // device constants (one allocation owned by the context)
   void *dmem = nullptr;
   float *Pi32 = nullptr;    // [d][d] row-major

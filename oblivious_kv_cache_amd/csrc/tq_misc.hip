@@ -2,6 +2,7 @@
 //
 //   prod: x_hat = nu (Pi^T c[idx] + alpha gamma S^T (2 bits - 1))
 //   mse:  x_hat = nu Pi^T c[idx]
+//   fractional widths: as prod, with each half's centroids
 //   polar: x_hat = nu Pi^T y_hat, y_hat the unit vector whose recursive polar
 //          angles are the codes' centroid angles: coordinate i is the product,
 //          over the levels l = 1..L of its path to the root, of the cosine
@@ -27,6 +28,8 @@ struct DqArgs {
   float c[16];
   const float *pcs;   // polar mode: (cos, sin) of the angle centroids [L][2^w][2]; else null
   int nlev;           // polar mode: L = log2 d
+  int frac, w2;       // fractional widths: second-half code bits and centroids
+  float c2[16];
 };
 
 // Record slot of the angle of node j at level l (polar layout: slots
@@ -61,6 +64,17 @@ __global__ void __launch_bounds__(256) dequant_kernel(DqArgs a) {
           yv *= a.pcs[(((level - 1) << a.w) + (int)code) * 2 + ((j >> (level - 1)) & 1)];
         }
         cv[j] = yv;
+      } else if (a.frac) {
+        // planar quarters: quarter g holds w_g bit planes of d/4 bits
+        const int qd = a.d >> 2, g = j / qd, jq = j - g * qd;
+        const int cw = g < 2 ? a.w : a.w2;
+        const int base = 4 * (g < 2 ? g * a.w : 2 * a.w + (g - 2) * a.w2) * (qd >> 5);
+        uint32_t code = 0;
+        for (int pl = 0; pl < cw; ++pl) {
+          const int bit = 8 * base + pl * qd + jq;
+          code |= (uint32_t)((rec[bit >> 3] >> (bit & 7)) & 1) << pl;
+        }
+        cv[j] = g < 2 ? a.c[code] : a.c2[code];
       } else {
         cv[j] = a.c[code_at(j)];
       }
@@ -106,7 +120,12 @@ int launch_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs
   a.cb = ctx->code_bytes;
   a.sb = ctx->sign_bytes;
   a.alpha = ctx->alpha;
-  for (int k = 0; k < 16; ++k) a.c[k] = ctx->cf[k];
+  for (int k = 0; k < 16; ++k) {
+    a.c[k] = ctx->cf[k];
+    a.c2[k] = ctx->cf2[k];
+  }
+  a.frac = ctx->frac;
+  a.w2 = ctx->hp.w2;
   a.pcs = ctx->hp.mode == TQ_MODE_POLAR ? ctx->polar_cs : nullptr;
   a.nlev = 0;
   while ((1 << a.nlev) < a.d) ++a.nlev;

@@ -289,7 +289,7 @@ inline PrepArgs make_prep_args(const tq_ctx *ctx, const float *q, int qpg, int h
   pa.hg = hg;
   pa.cb = ctx->code_bytes;
   pa.sb = ctx->sign_bytes;
-  pa.nm = mfma_count(ctx->code_bytes / 16, ctx->sign_bytes / 16, ctx->hp.w);
+  pa.nm = mfma_count(ctx->cw16, ctx->sign_bytes / 16, ctx->hp.w);
   for (int i = 0; i < 4; ++i) pa.basis[i] = ctx->basis[i];
   return pa;
 }

@@ -53,6 +53,7 @@ int launch_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int6
                     int64_t ldr, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
                     hipStream_t stream) {
   if (n == 0) return TQ_OK;
+  if (ctx->frac) return launch_quantize_big(ctx, x, dtype, n, ldx, ldr, codes, signs, norms, rnorms, stream);
   QArgs a = make_qargs(ctx, x, n, ldx, ldr, codes, signs, norms, rnorms);
   const bool bf16 = dtype == TQ_BF16;
   const int w = ctx->hp.w;

@@ -135,7 +135,11 @@ __device__ __forceinline__ ParityMasks<CB16, W> parity_masks(int grp) {
 // (lane % 16) of the tile:  nu * (P + alpha * gamma * Q), P and Q recombined
 // from four int32 digit rows.  Each bit-plane operand is built once and used
 // by the NQ groups' MFMAs.
-template <int CB16, int SB16, int W, int NQ>
+//
+// FRAC: fractional-width records (planar quarters): lane group g holds the
+// bit planes of its quarter's codes, CB16 = 3 WPP words for 3-bit codes, and
+// a code's parity is the XOR of its three plane words (no merging).
+template <int CB16, int SB16, int W, int NQ, bool FRAC = false>
 __device__ __forceinline__ void tile_logits(const i32x4 (*A)[ScoreShape<CB16, SB16, W>::NM],
                                             const KeyWords<CB16, SB16, W> &k, float nu, float gamma,
                                             float alpha, const HeadConsts *hc,
@@ -154,7 +158,16 @@ __device__ __forceinline__ void tile_logits(const i32x4 (*A)[ScoreShape<CB16, SB
     mf(accP, 2 * p, k.cw[p], 0);
     mf(accP, 2 * p + 1, k.cw[p], 1);
   }
-  if constexpr (W == 3) {
+  if constexpr (W == 3 && FRAC) {
+    constexpr int WPP = CB16 / 3;
+    static_assert(Sh::NPW == WPP, "one parity word per plane word");
+#pragma unroll
+    for (int f = 0; f < WPP; ++f) {
+      const uint32_t pw = k.cw[f] ^ k.cw[WPP + f] ^ k.cw[2 * WPP + f];
+      mf(accP, Sh::NMC + 2 * f, pw, 0);
+      mf(accP, Sh::NMC + 2 * f + 1, pw, 1);
+    }
+  } else if constexpr (W == 3) {
     // bit q of par = parity of record bits q, q+1, q+2
     uint32_t pw[Sh::NPW];
 #pragma unroll

@@ -55,6 +55,7 @@ struct ScoreArgs {
   int qpg, hg, hq, tiles_per_wave, cb, sb;   // hq: blocks of NQ head groups per key group
   int wide;                 // T and the logits base allow one 4*spb-byte store per lane
   float alpha;
+  int frac_lo;              // fractional widths: plane words of a second-half quarter
 };
 
 // 16-key subtiles per wave iteration: a 64-key tile fills one LDS slot of the
@@ -64,7 +65,12 @@ constexpr int kScoresSPB = 4;
 // NQ groups of 4 queries (head groups) per wave: each key tile's bit-plane
 // operands are built once for all of them (many queries per key group, e.g.
 // every position of a prefill, are bound by that VALU work, not by bytes).
-template <int CB16, int SB16, int W, int NQ>
+//
+// FRAC (fractional-width records, a.cb bytes each, not a multiple of 16):
+// every lane loads its quarter's plane words itself (CB16 slots, of which a
+// second-half quarter fills a.frac_lo; the other slots repeat a real word and
+// meet zero A coefficients), one tile ahead of the one it scores.
+template <int CB16, int SB16, int W, int NQ, bool FRAC = false>
 __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
   constexpr int SPB = kScoresSPB, KT = 16 * SPB;
@@ -93,6 +99,60 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   }
   const ParityMasks<CB16, W> pm = parity_masks<CB16, W>(grp);
 
+  const int T = (int)a.T;                  // T < 2^31 is checked on the host
+  const int tile0 = (blockIdx.x * 4 + wv) * a.tiles_per_wave;
+  if constexpr (FRAC) {
+    constexpr int KT = 16 * kScoresSPB;
+    int ntile = a.tiles_per_wave;
+    const int last = (T + KT - 1) / KT;
+    if (tile0 + ntile > last) ntile = last - tile0;
+    if (ntile <= 0) return;
+    const uint8_t *cgrp = a.codes + (int64_t)kg * a.ldk * a.cb;
+    const uint8_t *sgrp = a.signs + (int64_t)kg * a.ldk * (SB16 * 16) + grp * (SB16 * 4);
+    const float *nbase = a.norms + (int64_t)kg * a.ldk;
+    const float *rbase = a.rnorms + (int64_t)kg * a.ldk;
+    const int nreal = grp < 2 ? CB16 : a.frac_lo;
+    const int woff = grp < 2 ? grp * CB16 : 2 * CB16 + (grp - 2) * a.frac_lo;
+    struct Tile {
+      KeyWords<CB16, SB16, W> kw[kScoresSPB];
+      float nu[kScoresSPB], ga[kScoresSPB];
+    };
+    auto load = [&](Tile &tl, int t0) {
+#pragma unroll
+      for (int s = 0; s < kScoresSPB; ++s) {
+        const uint32_t t = (uint32_t)min(t0 + 16 * s + col, T - 1);
+        const uint32_t *cw = reinterpret_cast<const uint32_t *>(cgrp + t * (uint32_t)a.cb) + woff;
+#pragma unroll
+        for (int i = 0; i < CB16; ++i) tl.kw[s].cw[i] = key_word<true>(cw + min(i, nreal - 1));
+        if constexpr (W == 3) tl.kw[s].cw[CB16] = 0u;
+#pragma unroll
+        for (int i = 0; i < SB16; ++i)
+          tl.kw[s].sw[i] = key_word<true>(reinterpret_cast<const uint32_t *>(sgrp + t * (uint32_t)(SB16 * 16)) + i);
+        tl.nu[s] = load_f32(nbase, t);
+        tl.ga[s] = load_f32(rbase, t);
+      }
+    };
+    Tile cur, nxt;
+    load(cur, tile0 * KT);
+    for (int i = 0; i < ntile; ++i) {
+      const int t0 = (tile0 + i) * KT;
+      if (i + 1 < ntile) load(nxt, t0 + KT);
+      float l[kScoresSPB][NQ];
+#pragma unroll
+      for (int s = 0; s < kScoresSPB; ++s)
+        tile_logits<CB16, SB16, W, NQ, true>(A, cur.kw[s], cur.nu[s], cur.ga[s], a.alpha, hc, pm, l[s]);
+#pragma unroll
+      for (int g = 0; g < NQ; ++g)
+#pragma unroll
+        for (int s = 0; s < kScoresSPB; ++s) {
+          const int t = t0 + 16 * s + col;
+          if (head_ok[g] && t < T) lrow[g][t] = l[s][g];
+        }
+      cur = nxt;
+    }
+    return;
+  }
+
   // Record strides are compile-time (code_bytes = 16 CB16, sign_bytes = 16 SB16)
   // and per-token offsets are 32-bit from per-group base pointers, which keeps
   // address arithmetic to a few shifts per load.
@@ -100,9 +160,7 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   const uint8_t *sbase = a.signs + (int64_t)kg * a.ldk * (SB16 * 16);
   const float *nbase = a.norms + (int64_t)kg * a.ldk;
   const float *rbase = a.rnorms + (int64_t)kg * a.ldk;
-  const int T = (int)a.T;                  // T < 2^31 is checked on the host
 
-  const int tile0 = (blockIdx.x * 4 + wv) * a.tiles_per_wave;
   int ntile = a.tiles_per_wave;
   const int last = (T + KT - 1) / KT;
   if (tile0 + ntile > last) ntile = last - tile0;
@@ -246,21 +304,32 @@ constexpr int kScoresNQ2MaxNM = 12;
 
 // With events, the dispatch itself records them (hipExtLaunchKernel): they
 // bracket exactly this kernel's execution.
-template <int C, int S, int W_, int NQ>
+template <int C, int S, int W_, int NQ, bool FRAC>
 int launch_one(const ScoreArgs &a, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (e0 || e1)
-    hipExtLaunchKernelGGL(scores_kernel<C, S, W_, NQ>, grid, dim3(256), 0, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL(scores_kernel<C, S, W_, NQ, FRAC>, grid, dim3(256), 0, s, e0, e1, 0, a);
   else
-    scores_kernel<C, S, W_, NQ><<<grid, 256, 0, s>>>(a);
+    scores_kernel<C, S, W_, NQ, FRAC><<<grid, 256, 0, s>>>(a);
   return hip_status();
 }
 
-template <int C, int S, int W_>
+template <int C, int S, int W_, bool FRAC = false>
 int launch_geometry(const ScoreArgs &a, dim3 grid, int nq, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if constexpr (ScoreShape<C, S, W_>::NM <= kScoresNQ2MaxNM) {
-    if (nq == 2) return launch_one<C, S, W_, 2>(a, grid, s, e0, e1);
+    if (nq == 2) return launch_one<C, S, W_, 2, FRAC>(a, grid, s, e0, e1);
   }
-  return launch_one<C, S, W_, 1>(a, grid, s, e0, e1);
+  return launch_one<C, S, W_, 1, FRAC>(a, grid, s, e0, e1);
+}
+
+// fractional-width geometries (d = 128, 256 at 2.5 and 3.5 bits):
+// (first-half plane words per lane group, sign words, first-half code bits)
+int dispatch_frac(const ScoreArgs &a, dim3 grid, int cb16, int sb16, int w, int nq, hipStream_t s,
+                  hipEvent_t e0, hipEvent_t e1) {
+  if (cb16 == 2 && sb16 == 1 && w == 2) return launch_geometry<2, 1, 2, true>(a, grid, nq, s, e0, e1);
+  if (cb16 == 3 && sb16 == 1 && w == 3) return launch_geometry<3, 1, 3, true>(a, grid, nq, s, e0, e1);
+  if (cb16 == 4 && sb16 == 2 && w == 2) return launch_geometry<4, 2, 2, true>(a, grid, nq, s, e0, e1);
+  if (cb16 == 6 && sb16 == 2 && w == 3) return launch_geometry<6, 2, 3, true>(a, grid, nq, s, e0, e1);
+  return TQ_ENOTSUP;
 }
 
 int dispatch(const ScoreArgs &a, dim3 grid, int cb16, int sb16, int w, int nq, hipStream_t s, hipEvent_t e0,
@@ -343,7 +412,7 @@ int launch_scores_big(const tq_ctx *ctx, const void *ws, int64_t G, int qpg, int
   a.ldk = ldk;
   a.qpg = qpg;
   a.hg = (qpg + 3) / 4;
-  a.cb16 = ctx->code_bytes / 16;
+  a.cb16 = ctx->cw16;
   a.sb16 = ctx->sign_bytes / 16;
   a.nm = mfma_count(a.cb16, a.sb16, ctx->hp.w);
   a.alpha = ctx->alpha;
@@ -372,7 +441,7 @@ int launch_scores_big(const tq_ctx *ctx, const void *ws, int64_t G, int qpg, int
 
 int launch_prep(const tq_ctx *ctx, const float *q, int64_t groups, int qpg, int hg, int64_t nq_total,
                 uint8_t *ws, hipStream_t stream) {
-  if (ctx->hp.d > 256) return launch_prep_big(ctx, q, groups, qpg, hg, nq_total, ws, stream);
+  if (ctx->hp.d > 256 || ctx->frac) return launch_prep_big(ctx, q, groups, qpg, hg, nq_total, ws, stream);
   const PrepArgs pa = make_prep_args(ctx, q, qpg, hg, nq_total, ws);
   if (groups > 0x7fffffff) return TQ_ENOTSUP;
   const dim3 grid((unsigned)groups);
@@ -389,7 +458,7 @@ int launch_prep(const tq_ctx *ctx, const float *q, int64_t groups, int qpg, int 
 
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t G, int qpg) {
   const int hg = (qpg + 3) / 4;
-  const int nm = mfma_count(ctx->code_bytes / 16, ctx->sign_bytes / 16, ctx->hp.w);
+  const int nm = mfma_count(ctx->cw16, ctx->sign_bytes / 16, ctx->hp.w);
   return (size_t)(G * hg * prep_stride(nm));
 }
 
@@ -421,7 +490,7 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
     return launch_scores_big(ctx, ws, G, qpg, T, ldk, codes, signs, norms, rnorms, logits, stream, ev_start,
                              ev_stop);
   const int hg = (qpg + 3) / 4;
-  const int cb16 = ctx->code_bytes / 16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
+  const int cb16 = ctx->cw16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
   // NQ head groups per wave (2 where it fits); blocks along y: key group x NQ-group block
   const int nq = hg >= 2 && mfma_count(cb16, sb16, w) <= kScoresNQ2MaxNM ? 2 : 1;
   const int hq = (hg + nq - 1) / nq;
@@ -441,6 +510,7 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   sa.cb = ctx->code_bytes;
   sa.sb = ctx->sign_bytes;
   sa.alpha = ctx->alpha;
+  sa.frac_lo = ctx->frac ? ctx->hp.w2 * ctx->hp.d / 128 : 0;
   const int spb = kScoresSPB;
   sa.wide = T % spb == 0 && reinterpret_cast<uintptr_t>(logits) % (4 * spb) == 0;
   // key tiles of 16 * spb per wave iteration; aim for ~TQ_SCORES_WAVES waves overall
@@ -454,6 +524,9 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   if (tpw > 256) tpw = 256;
   const int64_t chunks = (tiles + 4 * tpw - 1) / (4 * tpw);
   sa.tiles_per_wave = (int)tpw;
+  if (ctx->frac)
+    return dispatch_frac(sa, dim3((unsigned)chunks, (unsigned)groups), cb16, sb16, w, nq, stream, ev_start,
+                         ev_stop);
   return dispatch(sa, dim3((unsigned)chunks, (unsigned)groups), cb16, sb16, w, nq, stream, ev_start, ev_stop);
 }
 

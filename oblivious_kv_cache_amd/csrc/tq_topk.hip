@@ -457,7 +457,7 @@ TopkGeom topk_block_geom(const tq_ctx *ctx, int64_t nq, int64_t n, int k) {
 }  // namespace
 
 size_t topk_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int k) {
-  const int nm = mfma_count(ctx->code_bytes / 16, ctx->sign_bytes / 16, ctx->hp.w);
+  const int nm = mfma_count(ctx->cw16, ctx->sign_bytes / 16, ctx->hp.w);
   const TopkGeom g = topk_block_path(ctx, k) ? topk_block_geom(ctx, nq, n, k) : topk_geom(nq, n, k, nm);
   return (size_t)(align256(g.groups * prep_stride(nm)) + 2 * align256(nq * g.ncand * 4));
 }
@@ -465,7 +465,7 @@ size_t topk_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int k) {
 int launch_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const uint8_t *codes,
                 const uint8_t *signs, const float *norms, const float *rnorms, int k,
                 int64_t *ids, float *scores, void *ws, hipStream_t stream) {
-  const int cb16 = ctx->code_bytes / 16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
+  const int cb16 = ctx->cw16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
   const int nm = mfma_count(cb16, sb16, w);
   const bool blk = topk_block_path(ctx, k);
   const TopkGeom g = blk ? topk_block_geom(ctx, nq, n, k) : topk_geom(nq, n, k, nm);

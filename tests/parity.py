@@ -134,3 +134,41 @@ def check_polar(p, gpu, X, allow_frac=MAX_FRAC):
     zero = ref["norms"] == 0
     assert not gpu["codes"][zero].any()
     return int(diff.sum())
+
+
+def check_quantized_frac(p, gpu, ref, X, allow_frac=MAX_FRAC):
+    """Fractional-width records (oracle/frac.py) against the oracle's: the rules
+    of check_quantized, with each coordinate's thresholds those of its half."""
+    import oracle.frac as F
+    g_idx, r_idx = F.unpack(p, gpu["codes"]), ref["idx"]
+    assert gpu["codes"].shape == ref["codes"].shape
+    gn, rn = gpu["norms"].astype(np.float32), ref["norms"].astype(np.float32)
+    assert (np.abs(gn.astype(np.float64) - rn) <= np.spacing(np.maximum(np.abs(rn), 1e-30))).all()
+    diff = g_idx != r_idx
+    h = p.d // 2
+    for v, i in zip(*np.nonzero(diff)):
+        t = p.t_hi if i < h else p.t_lo
+        dist = np.min(np.abs(ref["y"][v, i] - t))
+        assert dist < BAND, f"vector {v} coordinate {i}: code mismatch outside the band ({dist:.3e})"
+        assert abs(int(g_idx[v, i]) - int(r_idx[v, i])) == 1
+    assert diff.sum() <= allow_frac * diff.size, f"{diff.sum()} code mismatches of {diff.size}"
+    g_s = O.unpack_bits(gpu["signs"], 1, p.m)
+    z_ref, s_ref = ref["z"].copy(), ref["sbits"].copy()
+    g_ref = ref["rnorms"].astype(np.float64).copy()
+    for v in np.nonzero(diff.any(axis=1))[0]:
+        alt = r_idx[v].copy()
+        alt[diff[v]] = g_idx[v][diff[v]]
+        g_ref[v], z_ref[v], s_ref[v] = F.stage2_from_codes(p, X[v], alt)
+    sdiff = g_s != s_ref
+    if sdiff.any():
+        z = np.abs(z_ref[sdiff])
+        assert (z < BAND).all(), f"sign mismatch outside the band: |z| {z.max():.3e}"
+    assert sdiff.sum() <= allow_frac * sdiff.size, f"{sdiff.sum()} sign mismatches"
+    assert not np.unpackbits(gpu["signs"], axis=1, bitorder="little")[:, p.m:].any(), "nonzero sign padding"
+    gg = gpu["rnorms"].astype(np.float64)
+    assert (np.abs(gg - g_ref) <= 2e-5 + 1e-5 * g_ref).all(), np.abs(gg - g_ref).max()
+    zero = ref["norms"] == 0
+    if zero.any():
+        assert not gpu["codes"][zero].any() and not gpu["signs"][zero].any()
+        assert (gpu["rnorms"][zero] == 0).all()
+    return {"code_mismatch": int(diff.sum()), "sign_mismatch": int(sdiff.sum())}

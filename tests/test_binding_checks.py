@@ -28,7 +28,7 @@ def tq():
 
 def _ctx(tq, d=128, code_bytes=32, sign_bytes=16, prod=True):
     return SimpleNamespace(d=d, code_bytes=code_bytes, sign_bytes=sign_bytes,
-                           mode=tq.TQ_MODE_PROD if prod else tq.TQ_MODE_MSE, handle=None)
+                           mode=tq.TQ_MODE_PROD if prod else tq.TQ_MODE_MSE, sketch=prod, handle=None)
 
 
 def _rec(n, cb=32, sb=16):

@@ -104,3 +104,19 @@ def test_polar_codebooks_match_oracle(d, bits):
         assert np.abs(c[level] - bc).max() < 1e-12 and np.abs(t[level] - bt).max() < 1e-12
     with pytest.raises(tq.TQError):
         tq.tq_polar_codebook(96, bits)          # not a power of two
+
+
+@pytest.mark.parametrize("d,hb,seed", [(128, 5, 0), (256, 7, 3), (128, 7, 9)])
+def test_host_params_fractional_widths_match_oracle(d, hb, seed):
+    import oracle.frac as F
+    from oblivious_kv_cache_amd import binding as tq
+    Pi, S, c, t = tq.tq_host_params(d, hb, seed, tq.TQ_MODE_FRAC)
+    p = F.FracParams(d, hb, seed)
+    assert np.abs(Pi - p.Pi).max() < 1e-12 and np.abs(S - p.S).max() < 1e-12
+    nh = p.c_hi.size
+    assert c.size == nh + p.c_lo.size and t.size == c.size - 2
+    assert np.abs(c[:nh] - p.c_hi).max() < 1e-13 and np.abs(c[nh:] - p.c_lo).max() < 1e-13
+    assert np.abs(t[:nh - 1] - p.t_hi).max() < 1e-13 and np.abs(t[nh - 1:] - p.t_lo).max() < 1e-13
+    for d_bad, hb_bad in [(128, 6), (128, 3), (192, 5), (64, 7), (512, 5)]:
+        with pytest.raises(tq.TQError):
+            tq.tq_host_params(d_bad, hb_bad, 0, tq.TQ_MODE_FRAC)
