@@ -221,14 +221,18 @@ def bench_attend(tq, wl, dev):
     return r
 
 
-def bench_decode_bits(tq, wl, dev, bits, steps=50):
+def bench_decode_bits(tq, wl, dev, bits, steps=50, frac=False):
     """The default decode step (32 x 8 KV heads x 32768 tokens, d=128, GQA 4)
-    at another bit width: step time and the scores kernel's duration."""
+    at another bit width: step time and the scores kernel's duration.  With
+    frac, bits is twice the fractional width (5: 2.5 bits, 7: 3.5 bits); the
+    new key is then appended by tq_quantize and the queries prepared by
+    tq_prep_queries (two launches instead of the fused one)."""
     import torch
     B, Hkv, T, d, Hq = 32, 8, 32768, 128, 32
     qpg, G = Hq // Hkv, B * Hkv
-    log(f"decode 32K at b={bits}: setup")
-    ctx = tq.Context(d, bits, seed=0)
+    name = f"{bits / 2:g}" if frac else f"{bits}"
+    log(f"decode 32K at b={name}: setup")
+    ctx = tq.Context(d, bits, 0, tq.TQ_MODE_FRAC) if frac else tq.Context(d, bits, seed=0)
     K, _ = wl.outlier_keys_torch(B, Hkv, T, d, seed=2, device=dev)
     cache = ctx.empty_records(G * T, dev)
     tq.tq_quantize(ctx, K.view(G * T, d), out=cache)
@@ -242,8 +246,14 @@ def bench_decode_bits(tq, wl, dev, bits, steps=50):
     scale = 1.0 / math.sqrt(d)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
 
+    slot = {k: v[T - 1:] for k, v in cache.items()}       # record T-1 of group g at (T-1) + g T
+
     def step(e=None):
-        tq.tq_decode_prep(ctx, q, new_k, cache, T - 1, ldk=T, ws=ws)
+        if frac:
+            tq.tq_quantize(ctx, new_k, out=slot, ldr=T)
+            tq.tq_prep_queries(ctx, q, ws=ws)
+        else:
+            tq.tq_decode_prep(ctx, q, new_k, cache, T - 1, ldk=T, ws=ws)
         tq.tq_scores_prepared(ctx, ws, G, qpg, cache, T=T, ldk=T, logits=logits, events=e)
         tq.tq_softmax(logits, scale, probs=probs)
 
@@ -261,9 +271,10 @@ def bench_decode_bits(tq, wl, dev, bits, steps=50):
     sms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     sbytes = G * T * (ctx.code_bytes + ctx.sign_bytes + 8) + G * qpg * T * 4 + ws.numel()
     r = {"ms_per_step": ms, "logits_per_s": G * qpg * T / (ms / 1e3), "scores_ms": sms,
+         "key_bytes_per_token": ctx.code_bytes + ctx.sign_bytes + 8,
          "scores_bytes": sbytes, "scores_gbs": sbytes / (sms / 1e3) / 1e9,
          "scores_hbm_frac": sbytes / (sms / 1e3) / 1e9 / HBM_PEAK_GBS}
-    log(f"  b={bits}: step {ms:.3f} ms, scores kernel {sms * 1e3:.1f} us = {r['scores_gbs']:.0f} GB/s")
+    log(f"  b={name}: step {ms:.3f} ms, scores kernel {sms * 1e3:.1f} us = {r['scores_gbs']:.0f} GB/s")
     ctx.close()
     return r
 
@@ -581,6 +592,8 @@ def main():
         for b in (2, 4):
             if b != bits:
                 extra[f"decode_32k_b{b}"] = bench_decode_bits(tq, wl, dev, b)
+        for hb in (5, 7):               # fractional widths 2.5 and 3.5 bits
+            extra[f"decode_32k_b{hb / 2:g}"] = bench_decode_bits(tq, wl, dev, hb, frac=True)
         log("quantize throughput: 2^20 x 128 bf16, power-law spectrum (two input sets, alternated)")
         Xs = [wl.power_law_torch(1 << 20, d, seed=3 + i, device=dev) for i in range(2)]
         qz = {}

@@ -146,7 +146,8 @@ int tq_init_polar(int d, int bits, uint64_t seed, tq_ctx **out);
  * quarter: quarter g (coordinates [g d/4, (g+1) d/4)) holds w_g bit planes of
  * d/4 bits, plane p = bit p of the quarter's codes in order (w_g = w_hi for
  * g < 2, else w_lo); sign records, norms and residual norms as tq_init.
- * d in {128, 256}.  Such a context takes tq_quantize, tq_dequant and the
+ * d in {128, 256}; tq_quantize takes a codes pointer aligned to 4 bytes
+ * (a record slot inside a cache).  Such a context takes tq_quantize, tq_dequant and the
  * scoring calls (tq_scores, tq_prep_queries, tq_scores_prepared(_timed),
  * tq_scores_static); tq_attend, tq_topk and the decode steps return
  * TQ_EINVAL. */

@@ -336,7 +336,9 @@ int tq_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t 
   const bool polar = ctx->hp.mode == TQ_MODE_POLAR;
   if (ldx < ctx->hp.d) return TQ_EINVAL;
   if (dtype == TQ_BF16 ? (ldx % 8) : (ldx % 4)) return TQ_EINVAL;
-  if (!aligned(x, 16) || !aligned(codes, 16) || (signs && !aligned(signs, 16)) ||
+  // fractional-width records are a multiple of 8 bytes, written as 32-bit
+  // words: a record slot of a cache is aligned to 8 bytes only
+  if (!aligned(x, 16) || !aligned(codes, ctx->frac ? 4 : 16) || (signs && !aligned(signs, 16)) ||
       !aligned(norms, 4) || (rnorms && !aligned(rnorms, 4)))
     return TQ_EINVAL;
   const int st = current_device_matches(ctx);

@@ -27,6 +27,8 @@
 // per (KV group, head group) into the caller's workspace.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "tq_prep_body.h"
 
 namespace tq {
@@ -55,7 +57,6 @@ struct ScoreArgs {
   int qpg, hg, hq, tiles_per_wave, cb, sb;   // hq: blocks of NQ head groups per key group
   int wide;                 // T and the logits base allow one 4*spb-byte store per lane
   float alpha;
-  int frac_lo;              // fractional widths: plane words of a second-half quarter
 };
 
 // 16-key subtiles per wave iteration: a 64-key tile fills one LDS slot of the
@@ -66,10 +67,9 @@ constexpr int kScoresSPB = 4;
 // operands are built once for all of them (many queries per key group, e.g.
 // every position of a prefill, are bound by that VALU work, not by bytes).
 //
-// FRAC (fractional-width records, a.cb bytes each, not a multiple of 16):
-// every lane loads its quarter's plane words itself (CB16 slots, of which a
-// second-half quarter fills a.frac_lo; the other slots repeat a real word and
-// meet zero A coefficients), one tile ahead of the one it scores.
+// FRAC: fractional-width records (24 to 80 code bytes, the two halves' bit
+// planes by quarter); the tile copies into LDS end with a partial 1 KB
+// instruction where the tile's bytes are not a multiple of 1 KB.
 template <int CB16, int SB16, int W, int NQ, bool FRAC = false>
 __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
@@ -101,65 +101,21 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
 
   const int T = (int)a.T;                  // T < 2^31 is checked on the host
   const int tile0 = (blockIdx.x * 4 + wv) * a.tiles_per_wave;
-  if constexpr (FRAC) {
-    constexpr int KT = 16 * kScoresSPB;
-    int ntile = a.tiles_per_wave;
-    const int last = (T + KT - 1) / KT;
-    if (tile0 + ntile > last) ntile = last - tile0;
-    if (ntile <= 0) return;
-    const uint8_t *cgrp = a.codes + (int64_t)kg * a.ldk * a.cb;
-    const uint8_t *sgrp = a.signs + (int64_t)kg * a.ldk * (SB16 * 16) + grp * (SB16 * 4);
-    const float *nbase = a.norms + (int64_t)kg * a.ldk;
-    const float *rbase = a.rnorms + (int64_t)kg * a.ldk;
-    const int nreal = grp < 2 ? CB16 : a.frac_lo;
-    const int woff = grp < 2 ? grp * CB16 : 2 * CB16 + (grp - 2) * a.frac_lo;
-    struct Tile {
-      KeyWords<CB16, SB16, W> kw[kScoresSPB];
-      float nu[kScoresSPB], ga[kScoresSPB];
-    };
-    auto load = [&](Tile &tl, int t0) {
-#pragma unroll
-      for (int s = 0; s < kScoresSPB; ++s) {
-        const uint32_t t = (uint32_t)min(t0 + 16 * s + col, T - 1);
-        const uint32_t *cw = reinterpret_cast<const uint32_t *>(cgrp + t * (uint32_t)a.cb) + woff;
-#pragma unroll
-        for (int i = 0; i < CB16; ++i) tl.kw[s].cw[i] = key_word<true>(cw + min(i, nreal - 1));
-        if constexpr (W == 3) tl.kw[s].cw[CB16] = 0u;
-#pragma unroll
-        for (int i = 0; i < SB16; ++i)
-          tl.kw[s].sw[i] = key_word<true>(reinterpret_cast<const uint32_t *>(sgrp + t * (uint32_t)(SB16 * 16)) + i);
-        tl.nu[s] = load_f32(nbase, t);
-        tl.ga[s] = load_f32(rbase, t);
-      }
-    };
-    Tile cur, nxt;
-    load(cur, tile0 * KT);
-    for (int i = 0; i < ntile; ++i) {
-      const int t0 = (tile0 + i) * KT;
-      if (i + 1 < ntile) load(nxt, t0 + KT);
-      float l[kScoresSPB][NQ];
-#pragma unroll
-      for (int s = 0; s < kScoresSPB; ++s)
-        tile_logits<CB16, SB16, W, NQ, true>(A, cur.kw[s], cur.nu[s], cur.ga[s], a.alpha, hc, pm, l[s]);
-#pragma unroll
-      for (int g = 0; g < NQ; ++g)
-#pragma unroll
-        for (int s = 0; s < kScoresSPB; ++s) {
-          const int t = t0 + 16 * s + col;
-          if (head_ok[g] && t < T) lrow[g][t] = l[s][g];
-        }
-      cur = nxt;
-    }
-    return;
-  }
-
-  // Record strides are compile-time (code_bytes = 16 CB16, sign_bytes = 16 SB16)
-  // and per-token offsets are 32-bit from per-group base pointers, which keeps
-  // address arithmetic to a few shifts per load.
-  const uint8_t *cbase = a.codes + (int64_t)kg * a.ldk * (CB16 * 16);
-  const uint8_t *sbase = a.signs + (int64_t)kg * a.ldk * (SB16 * 16);
+  // Record strides are compile-time (code_bytes = 16 CB16, sign_bytes = 16 SB16;
+  // fractional widths: 8 (CB16 / W) (2 W - 1) code bytes, the two halves'
+  // planes) and per-token offsets are 32-bit from per-group base pointers,
+  // which keeps address arithmetic to a few shifts per load.
+  constexpr int CBY = FRAC ? 8 * (CB16 / W) * (2 * W - 1) : CB16 * 16, SBY = SB16 * 16;
+  const uint8_t *cbase = a.codes + (int64_t)kg * a.ldk * CBY;
+  const uint8_t *sbase = a.signs + (int64_t)kg * a.ldk * SBY;
   const float *nbase = a.norms + (int64_t)kg * a.ldk;
   const float *rbase = a.rnorms + (int64_t)kg * a.ldk;
+  // fractional widths: lane group g's plane words start at word woff of the
+  // record; a second-half quarter has fewer (nreal), and its remaining slots
+  // repeat a real word (their A coefficients are zero)
+  constexpr int WPP = FRAC ? CB16 / W : 1, NLO = FRAC ? (W - 1) * WPP : CB16;
+  const int nreal = grp < 2 ? CB16 : NLO;
+  const int woff = grp < 2 ? grp * CB16 : 2 * CB16 + (grp - 2) * NLO;
 
   int ntile = a.tiles_per_wave;
   const int last = (T + KT - 1) / KT;
@@ -168,7 +124,17 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
 #pragma unroll
     for (int s = 0; s < SPB; ++s) {
       const uint32_t t = (uint32_t)min(t0 + 16 * s + col, T - 1);
-      load_key_words<true>(kw[s], cbase, sbase, t, grp);
+      if constexpr (FRAC) {
+        const uint32_t *cw = reinterpret_cast<const uint32_t *>(cbase + t * (uint32_t)CBY) + woff;
+#pragma unroll
+        for (int i = 0; i < CB16; ++i) kw[s].cw[i] = key_word<true>(cw + min(i, nreal - 1));
+        if constexpr (W == 3) kw[s].cw[CB16] = 0u;
+        const uint32_t *sw = reinterpret_cast<const uint32_t *>(sbase + t * (uint32_t)SBY + grp * (SB16 * 4));
+#pragma unroll
+        for (int i = 0; i < SB16; ++i) kw[s].sw[i] = key_word<true>(sw + i);
+      } else {
+        load_key_words<true>(kw[s], cbase, sbase, t, grp);
+      }
       nu[s] = load_f32(nbase, t);
       ga[s] = load_f32(rbase, t);
     }
@@ -180,7 +146,7 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
     float l[SPB][NQ];
 #pragma unroll
     for (int s = 0; s < SPB; ++s) {
-      tile_logits<CB16, SB16, W, NQ>(A, kw[s], nu[s], ga[s], a.alpha, hc, pm, l[s]);
+      tile_logits<CB16, SB16, W, NQ, FRAC>(A, kw[s], nu[s], ga[s], a.alpha, hc, pm, l[s]);
 #pragma unroll
       for (int g = 0; g < NQ; ++g) __asm__ volatile("" : "+v"(l[s][g]));
     }
@@ -208,19 +174,28 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   // (the texture address unit was the busiest part), and this form needs
   // the fewest: CB16 + SB16 + 2 per 64 keys, against 16 or more with one
   // load of each record word per lane.
-  constexpr int CBY = CB16 * 16, SBY = SB16 * 16, TB = KT * (CBY + SBY);
+  constexpr int TB = KT * (CBY + SBY);
   __shared__ __align__(16) uint8_t kbA[4][TB];
   __shared__ __align__(16) uint8_t kbB[4][TB];
-  auto dma = [&](uint8_t *dst, const uint8_t *src, int kb) {
+  // NB bytes (a multiple of 16) from src to dst, 1 KB per instruction; a
+  // remainder takes one more instruction on the lanes it needs
+  auto dma = [&](uint8_t *dst, const uint8_t *src, auto nb) {
+    constexpr int NB = decltype(nb)::value, FULL = NB / 1024, REM = NB % 1024;
 #pragma unroll
-    for (int i = 0; i < kb; ++i)
+    for (int i = 0; i < FULL; ++i)
       __builtin_amdgcn_global_load_lds(src + i * 1024 + lane * 16,
                                        (__attribute__((address_space(3))) void *)(dst + i * 1024), 16, 0,
                                        2 /* nt */);
+    if constexpr (REM > 0) {
+      if (lane * 16 < REM)
+        __builtin_amdgcn_global_load_lds(src + FULL * 1024 + lane * 16,
+                                         (__attribute__((address_space(3))) void *)(dst + FULL * 1024), 16, 0,
+                                         2 /* nt */);
+    }
   };
   auto load_dma = [&](uint8_t (&kb)[4][TB], float &nu, float &ga, int t0) {
-    dma(kb[wv], cbase + (uint32_t)t0 * CBY, KT * CBY / 1024);
-    dma(kb[wv] + KT * CBY, sbase + (uint32_t)t0 * SBY, KT * SBY / 1024);
+    dma(kb[wv], cbase + (uint32_t)t0 * CBY, std::integral_constant<int, KT * CBY>{});
+    dma(kb[wv] + KT * CBY, sbase + (uint32_t)t0 * SBY, std::integral_constant<int, KT * SBY>{});
     const uint32_t tl = (uint32_t)(t0 + (lane % KT));
     nu = load_f32(nbase, tl);
     ga = load_f32(rbase, tl);
@@ -231,13 +206,20 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
 #pragma unroll
     for (int s = 0; s < SPB; ++s) {
       const int k = 16 * s + col;
-      const uint8_t *rc = kb[wv] + k * CBY + grp * (CB16 * 4);
       const uint8_t *rsg = kb[wv] + KT * CBY + k * SBY + grp * (SB16 * 4);
+      if constexpr (FRAC) {
+        const uint8_t *rc = kb[wv] + k * CBY + woff * 4;
 #pragma unroll
-      for (int i = 0; i < CB16; ++i) kw[s].cw[i] = *reinterpret_cast<const uint32_t *>(rc + 4 * i);
-      if constexpr (W == 3) {   // first code word of the next lane group (in LDS after ours), none for the last
-        const uint32_t nxt = *reinterpret_cast<const uint32_t *>(rc + 4 * CB16);
-        kw[s].cw[CB16] = grp < 3 ? nxt : 0u;
+        for (int i = 0; i < CB16; ++i) kw[s].cw[i] = *reinterpret_cast<const uint32_t *>(rc + 4 * min(i, nreal - 1));
+        if constexpr (W == 3) kw[s].cw[CB16] = 0u;
+      } else {
+        const uint8_t *rc = kb[wv] + k * CBY + grp * (CB16 * 4);
+#pragma unroll
+        for (int i = 0; i < CB16; ++i) kw[s].cw[i] = *reinterpret_cast<const uint32_t *>(rc + 4 * i);
+        if constexpr (W == 3) {   // first code word of the next lane group (in LDS after ours), none for the last
+          const uint32_t nxt = *reinterpret_cast<const uint32_t *>(rc + 4 * CB16);
+          kw[s].cw[CB16] = grp < 3 ? nxt : 0u;
+        }
       }
 #pragma unroll
       for (int i = 0; i < SB16; ++i) kw[s].sw[i] = *reinterpret_cast<const uint32_t *>(rsg + 4 * i);
@@ -248,7 +230,7 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
     for (int s = 0; s < SPB; ++s) {
       const float nu = __shfl(nub, 16 * s + col), ga = __shfl(gab, 16 * s + col);
       float l[NQ];
-      tile_logits<CB16, SB16, W, NQ>(A, kw[s], nu, ga, a.alpha, hc, pm, l);
+      tile_logits<CB16, SB16, W, NQ, FRAC>(A, kw[s], nu, ga, a.alpha, hc, pm, l);
 #pragma unroll
       for (int g = 0; g < NQ; ++g) lt[wv][g][grp][16 * s + col] = l[g];
     }
@@ -269,7 +251,10 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   if (ntile <= 0) return;
   // first key of this wave's i-th tile
   auto key0 = [&](int i) { return (tile0 + i) * KT; };
-  const int nfull = key0(ntile - 1) + KT > T ? ntile - 1 : ntile;
+  // (fractional widths: a key group whose records do not start on 16 bytes,
+  // ldk * code bytes odd in 8-byte units, is read lane by lane throughout)
+  const bool dma_ok = !FRAC || ((a.ldk * CBY) & 15) == 0;
+  const int nfull = !dma_ok ? 0 : key0(ntile - 1) + KT > T ? ntile - 1 : ntile;
   // two slots, two tiles in flight: a slot is read into registers, refilled
   // with the tile after next, and only then is its tile scored
   float nA, gA, nB, gB;
@@ -290,11 +275,11 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
     if (it + 3 < nfull) load_dma(kbB, nB, gB, key0(it + 3));
     score_dma(kw, nu, ga, key0(it + 1));
   }
-  if (nfull < ntile) {          // the group's last tile, keys clamped and stores guarded
+  for (int i = nfull; i < ntile; ++i) {   // the group's last tile (keys clamped, stores guarded)
     KeyWords<CB16, SB16, W> k0[SPB];
     float n0[SPB], g0[SPB];
-    load_tile(k0, n0, g0, key0(nfull));
-    score_tile(k0, n0, g0, key0(nfull));
+    load_tile(k0, n0, g0, key0(i));
+    score_tile(k0, n0, g0, key0(i));
   }
 }
 
@@ -510,7 +495,6 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   sa.cb = ctx->code_bytes;
   sa.sb = ctx->sign_bytes;
   sa.alpha = ctx->alpha;
-  sa.frac_lo = ctx->frac ? ctx->hp.w2 * ctx->hp.d / 128 : 0;
   const int spb = kScoresSPB;
   sa.wide = T % spb == 0 && reinterpret_cast<uintptr_t>(logits) % (4 * spb) == 0;
   // key tiles of 16 * spb per wave iteration; aim for ~TQ_SCORES_WAVES waves overall

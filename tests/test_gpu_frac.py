@@ -62,6 +62,23 @@ def test_quantize_frac(tq, d, hb, n, bf16):
     print(check_quantized_frac(p, g, F.quantize(p, xin, return_unpacked=True), xin))
 
 
+def test_quantize_frac_append_into_cache_slot(tq):
+    # one new key per group into slot pos of a [G][ldk] cache: the slot's
+    # record is 8-byte aligned (24-byte records)
+    d, hb, G, ldk, pos = 128, 5, 6, 40, 17
+    p = F.FracParams(d, hb, 0)
+    ctx = tq.Context(d, hb, 0, tq.TQ_MODE_FRAC)
+    cache = ctx.empty_records(G * ldk)
+    X = wl.gaussian((G, d), 12)
+    tq.tq_quantize(ctx, torch.from_numpy(X).cuda(), out={k: v[pos:] for k, v in cache.items()}, ldr=ldk)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in cache.items()}
+    rows = np.arange(G) * ldk + pos
+    check_quantized_frac(p, {k: v[rows] for k, v in g.items()}, F.quantize(p, X, return_unpacked=True), X)
+    others = np.setdiff1d(np.arange(G * ldk), rows)
+    assert not g["codes"][others].any() and not g["norms"][others].any()
+
+
 def test_quantize_frac_strided_records(tq):
     d, hb, n = 128, 5, 70
     X = wl.gaussian((n, d), 3)
@@ -84,6 +101,8 @@ def _oracle_grouped(p, Q, rec, G, T, ldk):
 @pytest.mark.parametrize("d,hb,G,qpg,T,ldk,records", [
     (128, 5, 3, 4, 1000, 1000, "oracle"), (128, 7, 2, 8, 513, 520, "oracle"), (128, 7, 1, 5, 300, 300, "random"),
     (256, 5, 2, 4, 257, 257, "random"), (256, 7, 1, 9, 700, 700, "oracle"), (128, 5, 2, 1, 1, 3, "random"),
+    # group bases off 16 bytes (ldk * 24 and ldk * 40 odd multiples of 8): read lane by lane
+    (128, 5, 3, 4, 400, 401, "random"), (128, 7, 2, 4, 333, 335, "oracle"),
 ])
 def test_scores_frac(tq, d, hb, G, qpg, T, ldk, records):
     p = F.FracParams(d, hb, 0)
