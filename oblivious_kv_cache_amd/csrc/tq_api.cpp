@@ -168,7 +168,12 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
   const int nlev = polar ? (int)std::lround(std::log2((double)d)) : 0;
   const size_t n_thr = polar ? (size_t)nlev * (L - 1) : 0, n_cs = polar ? (size_t)nlev * L * 2 : 0;
   const size_t bytes_pol = sizeof(float) * (n_thr + n_cs);
-  const size_t total = (bytes_f32 + 255) / 256 * 256 + bytes_fr + bytes_pol;
+  // query-prep GEMM operand [Pi; S] (prod mode, d <= 256): (d + m) / 16 row
+  // tiles x dpad / 32 column blocks of 64 lane fragments, hi and lo
+  const bool pq = mode == TQ_MODE_PROD && d <= 256;
+  const size_t pq_tiles = pq ? (size_t)(d + m + 15) / 16 : 0, npq = pq_tiles * (dpad / 32) * 64;
+  const size_t off_pq = (bytes_f32 + 255) / 256 * 256 + bytes_fr + (bytes_pol + 255) / 256 * 256;
+  const size_t total = off_pq + sizeof(Frag) * 3 * npq;
   std::vector<uint8_t> host(total, 0);
   float *Pi32 = reinterpret_cast<float *>(host.data());
   float *PiT32 = Pi32 + (size_t)d * d;
@@ -205,6 +210,36 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
       pol[n_thr + 2 * i + 1] = (float)std::sin(hp.c[i]);
     }
   }
+  if (pq) {
+    Frag *ph = reinterpret_cast<Frag *>(host.data() + off_pq), *pm = ph + npq, *pl = ph + 2 * npq;
+    const int NK = dpad / 32;
+    for (size_t u = 0; u < pq_tiles; ++u)
+      for (int k = 0; k < NK; ++k)
+        for (int l = 0; l < 64; ++l) {
+          const int row = 16 * (int)u + l % 16, g = l / 16;
+          uint16_t h8[8], m8[8], l8[8];
+          for (int e = 0; e < 8; ++e) {
+            const int c = 32 * k + 8 * g + e;
+            double v = 0.0;
+            if (c < d && row < d) v = hp.Pi[(size_t)row * d + c];
+            else if (c < d && row < d + m) v = hp.S[(size_t)(row - d) * d + c];
+            // three parts: hi = bf16(v), mid = bf16(v - hi), lo = bf16(v - hi - mid)
+            h8[e] = bf16_rne((float)v);
+            const double r1 = v - (double)bf16_to_f(h8[e]);
+            m8[e] = bf16_rne((float)r1);
+            l8[e] = bf16_rne((float)(r1 - (double)bf16_to_f(m8[e])));
+          }
+          Frag fh, fm, fl;
+          for (int i = 0; i < 4; ++i) {
+            fh.v[i] = (uint32_t)h8[2 * i] | ((uint32_t)h8[2 * i + 1] << 16);
+            fm.v[i] = (uint32_t)m8[2 * i] | ((uint32_t)m8[2 * i + 1] << 16);
+            fl.v[i] = (uint32_t)l8[2 * i] | ((uint32_t)l8[2 * i + 1] << 16);
+          }
+          ph[(u * NK + k) * 64 + l] = fh;
+          pm[(u * NK + k) * 64 + l] = fm;
+          pl[(u * NK + k) * 64 + l] = fl;
+        }
+  }
   if (hipMalloc(&ctx->dmem, total) != hipSuccess) {
     (void)hipGetLastError();
     delete ctx;
@@ -230,6 +265,10 @@ int make_ctx(int d, int bits, uint64_t seed, int mode, tq_ctx **out) {
   if (polar) {
     ctx->polar_thr = reinterpret_cast<float *>(base + (bytes_f32 + 255) / 256 * 256 + bytes_fr);
     ctx->polar_cs = ctx->polar_thr + n_thr;
+  }
+  if (pq) {
+    ctx->PqH = reinterpret_cast<Frag *>(base + off_pq);
+    ctx->npq = npq;
   }
   // the static scratch buffer of this device is located once, at init
   if (tq::scratch_attach(ctx->device) == nullptr) {

@@ -61,6 +61,11 @@ struct tq_ctx {
   float *ST32 = nullptr;    // [d][m] = S^T
   tq::Frag *PiA_hi = nullptr, *PiA_lo = nullptr;   // quantize GEMM-1 operand fragments
   tq::Frag *S2A_hi = nullptr, *S2A_lo = nullptr;   // quantize GEMM-2 operand fragments
+  // query-prep GEMM operand: [Pi; S] (rows 16 u + r, columns 32 k + 8 g + e)
+  // in three bf16 parts (hi, mid, lo: npq fragments each, consecutive), prod
+  // mode with d <= 256
+  tq::Frag *PqH = nullptr;
+  size_t npq = 0;
   float *polar_thr = nullptr;   // polar mode: angle thresholds [log2 d][levels - 1]
   float *polar_cs = nullptr;    // polar mode: (cos, sin) of angle centroids [log2 d][levels][2]
 };
@@ -77,6 +82,10 @@ int launch_quantize_big(const tq_ctx *ctx, const void *x, int dtype, int64_t n, 
                         hipStream_t stream);
 int launch_prep_big(const tq_ctx *ctx, const float *q, int64_t groups, int qpg, int hg,
                     int64_t nq_total, uint8_t *ws, hipStream_t stream);
+// query prep of many groups as one MFMA GEMM (tq_prep_gemm.hip)
+bool prep_gemm_applies(const tq_ctx *ctx, int64_t groups);
+int launch_prep_gemm(const tq_ctx *ctx, const float *q, int64_t groups, int qpg, int hg,
+                     int64_t nq_total, uint8_t *ws, hipStream_t stream);
 int launch_polar_quantize(const tq_ctx *ctx, const void *x, int dtype, int64_t n, int64_t ldx,
                           int64_t ldr, uint8_t *codes, float *norms, hipStream_t stream);
 size_t scores_ws_bytes(const tq_ctx *ctx, int64_t G, int qpg);

@@ -87,6 +87,8 @@ def test_scores_random_records(tq, d, bits, G, qpg, T, ldk):
     # b = 2, 3, 4, d = 64 and 128, with a partial last head group
     (128, 3, 2, 2048, 100, 100), (64, 2, 4, 1024, 70, 70), (128, 4, 1, 4096, 40, 40),
     (128, 3, 1, 4099, 33, 33),
+    # d + m > 256: the prep GEMM takes 32 queries per block
+    (200, 2, 1, 4100, 50, 50), (256, 4, 2, 2048, 40, 40), (96, 3, 3, 1366, 30, 31),
 ])
 def test_scores_many_queries_per_group(tq, d, bits, G, qpg, T, ldk):
     ctx = tq.Context(d, bits, 0)
