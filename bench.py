@@ -47,7 +47,7 @@ def log(*a):
 # FETCH_SIZE / WRITE_SIZE counters scaled by a plain copy's counters.  The
 # record holds the SHA-256 of the sources of the counted kernels; once those
 # change the figure is stale and reported as null.
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "scores_decode32k_b3_hbm_traffic.txt")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "scores_decode32k_b{}_hbm_traffic.txt")
 TRAFFIC_SOURCES = ("tq_scores.hip", "tq_score_core.h")
 
 
@@ -61,10 +61,11 @@ def scores_sources_sha256():
 
 
 def recorded_traffic(bits, alg_bytes):
-    if bits != 3 or not os.path.exists(TRAFFIC_RECORD):
+    path = TRAFFIC_RECORD.format(bits)
+    if not os.path.exists(path):
         return None
     rec = {}
-    with open(TRAFFIC_RECORD) as fh:
+    with open(path) as fh:
         for line in fh:
             k, sep, v = line.partition(":")
             if sep and k.strip() in ("sources_sha256", "hbm_bytes_per_call"):
@@ -272,6 +273,7 @@ def bench_decode_bits(tq, wl, dev, bits, steps=50, frac=False):
     sbytes = G * T * (ctx.code_bytes + ctx.sign_bytes + 8) + G * qpg * T * 4 + ws.numel()
     r = {"ms_per_step": ms, "logits_per_s": G * qpg * T / (ms / 1e3), "scores_ms": sms,
          "key_bytes_per_token": ctx.code_bytes + ctx.sign_bytes + 8,
+         "scores_traffic": None if frac else recorded_traffic(bits, sbytes),
          "scores_bytes": sbytes, "scores_gbs": sbytes / (sms / 1e3) / 1e9,
          "scores_hbm_frac": sbytes / (sms / 1e3) / 1e9 / HBM_PEAK_GBS}
     log(f"  b={name}: step {ms:.3f} ms, scores kernel {sms * 1e3:.1f} us = {r['scores_gbs']:.0f} GB/s")
