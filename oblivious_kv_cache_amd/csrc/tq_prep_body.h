@@ -17,6 +17,10 @@ struct PrepArgs {
   int64_t nq_total;    // queries beyond this flat index are zero
   int d, m, w, qpg, hg, cb, sb, nm;
   float basis[4];
+  // fractional widths (planar quarters): code words per lane group, the
+  // second half's code bits and odd-basis coefficients
+  int frac, cw16, w2;
+  float basis2[4];
 };
 
 // Shared memory of one query-prep group (about 48 KB at d <= 128)
@@ -55,9 +59,13 @@ __device__ __forceinline__ void prep_body(const PrepArgs &a, PrepSmem<SPLIT> &sm
   const int grp = gidx / a.hg, hgi = gidx - grp * a.hg;
   const int lane = tid & 63, wv = tid >> 6;
   const int d = a.d, m = a.m, w = a.w;
-  const int ncb = a.cb * 8, nsb = a.sb * 8;
-  const int npar = w == 3 ? ncb : 0;
-  const int cwpl = a.cb / 16, swpl = a.sb / 16;
+  // coefficient slots: record bit order, or for fractional widths the bits
+  // of each lane group's word slots (32 (g cw16 + p) + q) then one parity
+  // word per plane word of the first-half quarters
+  const int cwpl = a.frac ? a.cw16 : a.cb / 16, swpl = a.sb / 16;
+  const int wpp = d / 128;
+  const int ncb = a.frac ? 4 * cwpl * 32 : a.cb * 8, nsb = a.sb * 8;
+  const int npar = w == 3 ? (a.frac ? 4 * wpp * 32 : ncb) : 0;
 
   // d <= 128: thread (matrix, column quad, row group) loads RPG rows x 4
   // columns of Pi^T or S^T with 16-byte loads, issued before the queries
@@ -152,7 +160,30 @@ __device__ __forceinline__ void prep_body(const PrepArgs &a, PrepSmem<SPLIT> &sm
         }
       }
     }
-    if (col < cols) {
+    if (col < cols && mat == 0 && a.frac) {
+      // quarter g of coordinate col: plane pl of word slot pl wpp + jq / 32
+      const int qd = d / 4, g4 = col / qd, jq = col - g4 * qd;
+      const bool second = g4 >= 2;
+      const int cw = second ? a.w2 : w;
+      const float *bs = second ? a.basis2 : a.basis;
+      const float bsum = bs[0] + (cw >= 2 ? bs[1] : 0.f) + (cw >= 3 ? bs[2] + bs[3] : 0.f);
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        sP[hh] = bsum * acc[hh];
+        for (int pl = 0; pl < cw; ++pl) {
+          const int pos = 32 * (g4 * cwpl + pl * wpp + (jq >> 5)) + (jq & 31);
+          const float v = 2.f * bs[pl] * acc[hh];
+          vP[hh][pos] = v;
+          mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(v), -(jq & 7)));
+        }
+        if (cw == 3) {
+          const int pos = 32 * (g4 * wpp + (jq >> 5)) + (jq & 31);
+          const float v = 2.f * bs[3] * acc[hh];
+          vP[hh][ncb + pos] = v;
+          mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(v), -(jq & 7)));
+        }
+      }
+    } else if (col < cols) {
       if (mat == 0) {
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh) {
@@ -236,9 +267,11 @@ __device__ __forceinline__ void prep_body(const PrepArgs &a, PrepSmem<SPLIT> &sm
       const int q = 8 * b + j;
       // merged parity word `pair`: bit q belongs to the code starting at bit
       // q of record word g*wpl + p, p = 3 pair + ((q - g*wpl) mod 3), if any
-      const int p = par ? 3 * pair + ((q - g * wpl) % 3 + 3) % 3 : pair;
-      const int bitpos = 32 * (g * wpl + p) + q;
-      float u = p < wpl ? ldexpf(vv[bitpos] * S, -j) : 0.f;
+      // (fractional widths: parity word `pair` is plane word `pair`, unmerged)
+      const int p = par && !a.frac ? 3 * pair + ((q - g * wpl) % 3 + 3) % 3 : pair;
+      const int pw = par && a.frac ? wpp : wpl;
+      const int bitpos = 32 * (g * pw + p) + q;
+      float u = p < pw ? ldexpf(vv[bitpos] * S, -j) : 0.f;
       if (j == 7) u = -u;                 // B byte value is -128 for bit 7
       // base-128 digits, all four computed and one selected (no per-lane loop)
       const float r0 = rintf(u);
@@ -268,7 +301,7 @@ __device__ __forceinline__ void prep_body(const PrepArgs &a, PrepSmem<SPLIT> &sm
     float *cst = reinterpret_cast<float *>(out + (int64_t)a.nm * 1024);
     cst[h4 * 4 + 0] = x0 > 0.f ? 1.f / (127.f / x0) : 1.f;
     cst[h4 * 4 + 1] = x1 > 0.f ? 1.f / (127.f / x1) : 1.f;
-    cst[h4 * 4 + 2] = bsum * s0;
+    cst[h4 * 4 + 2] = a.frac ? s0 : bsum * s0;      // fractional widths: s0 is already weighted
     cst[h4 * 4 + 3] = s1;
   }
 }
@@ -290,7 +323,13 @@ inline PrepArgs make_prep_args(const tq_ctx *ctx, const float *q, int qpg, int h
   pa.cb = ctx->code_bytes;
   pa.sb = ctx->sign_bytes;
   pa.nm = mfma_count(ctx->cw16, ctx->sign_bytes / 16, ctx->hp.w);
-  for (int i = 0; i < 4; ++i) pa.basis[i] = ctx->basis[i];
+  for (int i = 0; i < 4; ++i) {
+    pa.basis[i] = ctx->basis[i];
+    pa.basis2[i] = ctx->basis2[i];
+  }
+  pa.frac = ctx->frac;
+  pa.cw16 = ctx->cw16;
+  pa.w2 = ctx->hp.w2;
   return pa;
 }
 

@@ -426,7 +426,7 @@ int launch_scores_big(const tq_ctx *ctx, const void *ws, int64_t G, int qpg, int
 
 int launch_prep(const tq_ctx *ctx, const float *q, int64_t groups, int qpg, int hg, int64_t nq_total,
                 uint8_t *ws, hipStream_t stream) {
-  if (ctx->hp.d > 256 || ctx->frac) return launch_prep_big(ctx, q, groups, qpg, hg, nq_total, ws, stream);
+  if (ctx->hp.d > 256) return launch_prep_big(ctx, q, groups, qpg, hg, nq_total, ws, stream);
   if (prep_gemm_applies(ctx, groups)) return launch_prep_gemm(ctx, q, groups, qpg, hg, nq_total, ws, stream);
   const PrepArgs pa = make_prep_args(ctx, q, qpg, hg, nq_total, ws);
   if (groups > 0x7fffffff) return TQ_ENOTSUP;
