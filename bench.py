@@ -625,8 +625,25 @@ def main():
                 f"MFMA {hw_tflops:.0f} TF/s, io {io_gbs:.0f} GB/s")
             c2.close()
             del out
+        # the other encoders on the same 2^20 vectors: PolarQuant (NEXT-4, MSE stage,
+        # b bits per angle) and the fractional widths (NEXT-3, 2.5 / 3.5 bits)
+        other = {}
+        for name, mode, b in (("polar_b2", tq.TQ_MODE_POLAR, 2), ("polar_b4", tq.TQ_MODE_POLAR, 4),
+                              ("frac_2.5", tq.TQ_MODE_FRAC, 5), ("frac_3.5", tq.TQ_MODE_FRAC, 7)):
+            c2 = tq.Context(d, b, 0, mode)
+            out = c2.empty_records(1 << 20, dev)
+            ms = _time(torch, lambda: tq.tq_quantize(c2, Xs[0], out=out), 5)
+            vps = (1 << 20) / (ms / 1000.0)
+            rec_b = c2.code_bytes + c2.sign_bytes + (8 if c2.sign_bytes else 4)
+            io_gbs = (1 << 20) * (2 * d + rec_b) / (ms / 1000.0) / 1e9
+            other[name] = {"ms": ms, "vec_per_s": vps, "record_bytes": rec_b, "io_gbs": io_gbs,
+                           "io_hbm_frac": io_gbs / HBM_PEAK_GBS}
+            log(f"  {name}: {ms:.3f} ms, {vps:.3e} vec/s, {rec_b} B records")
+            c2.close()
+            del out
         del Xs
         extra["quantize_2p20"] = qz
+        extra["quantize_2p20_other_modes"] = other
         extra["attend_128k"] = bench_attend(tq, wl, dev)
         extra["topk_1e6"] = bench_topk(tq, wl, dev)
         extra["many_queries_2k"] = bench_many_queries(tq, wl, dev)
