@@ -34,9 +34,12 @@
  *     tq_workspace_size().
  *
  * Packed record layout (structure-of-arrays, one record per vector):
- *   codes [n][code_bytes]  code i of a vector sits in bits [i*w, (i+1)*w) of its
- *                          record, little-endian, LSB first; code k selects the
- *                          k-th smallest centroid;
+ *   codes [n][code_bytes]  prod mode: code i of a vector sits in bits
+ *                          [i*w, (i+1)*w) of its record, little-endian, LSB
+ *                          first; MSE-only mode: w bit planes of d bits, plane
+ *                          p in bytes [p*d/8, (p+1)*d/8) holding bit p of code
+ *                          i at bit i of the plane (LSB first); code k selects
+ *                          the k-th smallest centroid;
  *   signs [n][sign_bytes]  sign bit j is bit (j & 7) of byte (j >> 3); 1 = +1
  *                          (prod mode only);
  *   norms [n]   float32    nu = |x|_2;

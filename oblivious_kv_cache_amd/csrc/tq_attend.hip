@@ -10,11 +10,11 @@
 // Split over token chunks like flash-decoding on one GPU:
 //   partial kernel (block = one query group x a run of chunks, online softmax):
 //     A. int8-MFMA logits of the chunk into LDS (and to the optional logits
-//        output); the chunk's value records staged in LDS;
+//        output); the chunk's value records are already on their way into
+//        LDS (copied by the memory system, issued one chunk ahead);
 //     B. chunk max, running max M, rescale factor f = exp(M_old - M_new);
 //        weights w_t = exp(z_t - M) nu_t turned into int8 fixed-point digits
-//        (the A operand of the value sum); the staged value records
-//        transposed into bit-plane words (32 tokens per word);
+//        (the A operand of the value sum);
 //     C. the value sum on int8 MFMA over bit planes (below);
 //     D. per-block partials (M, sum of exp, rotated accumulator).
 //   combine kernel: merges the partials with the usual max rescaling,
@@ -31,12 +31,17 @@
 // with beta_P the bit (or bit parity) P of token t's code i.  V is an int8
 // matrix product over tokens: the A operand holds the weights of 64 tokens as
 // four base-128 digits per head (16 rows = 4 heads x 4 digits, scaled per
-// chunk), the B operand the bits of 64 tokens of 16 coordinates, built from
-// one 32-token plane word per lane as (word & 0x01010101 << j) -- bit j of
-// each byte -- exactly as the key estimator builds its B from record words.
-// The plane words come from the staged value records by 32 x 32 bit
-// transposes.  W is the same product against an all-ones B, so 2 V - W is
-// exact in int32 before the digits are recombined in fp32.
+// chunk), the B operand one byte per token whose bit j is that token's plane
+// bit of coordinate 8 n + j (n = the operand column).  Value records store
+// their codes as bit planes (one byte = 8 coordinates of one plane), so the
+// B operand of a 16-lane group is a byte transpose of 16 records, which the
+// LDS does in hardware (ds_read_b64_tr_b8: lane 2r + h names row r, bytes
+// 8h .. 8h+7, of an 8 x 16 byte tile; lane i receives column i of the 8 rows,
+// row r in byte r).  Masking the bytes with 0x01010101 << j selects
+// coordinate 8 n + j (byte value 2^j, -128 for j = 7, undone after the
+// product); the parity planes are XORs of plane bytes.  W is the same product
+// against all-ones bytes, so 2 V - W is exact in int32 before the digits are
+// recombined in fp32.
 #include <algorithm>
 #include <cfloat>
 
@@ -47,13 +52,16 @@ namespace {
 
 constexpr int CH = 512;            // tokens per chunk
 constexpr int NT = 256;            // threads per partial block
-constexpr int NB32 = CH / 32;      // 32-token plane words per bit row and chunk
 #ifndef TQ_ATT_BLOCKS
 #define TQ_ATT_BLOCKS 512          // partial blocks per call (2 per CU are resident)
 #endif
 
 // odd monomials of the code bits of a w-bit value code: w singles + triples
 __host__ __device__ constexpr int value_planes(int vw) { return vw + (vw == 3 ? 1 : vw == 4 ? 4 : 0); }
+
+// the fused kernel: d = 64 or 128 (a value plane is one or two 8-byte rows
+// of the LDS transpose read)
+bool attend_fused(int d) { return d == 64 || d == 128; }
 
 struct AttArgs {
   const uint8_t *kcodes, *ksigns;
@@ -69,76 +77,54 @@ struct AttArgs {
   float vbasis[8];                 // value codebook: odd-monomial coefficients
 };
 
-// 32 x 32 bit transpose in registers: afterwards bit i of x[q] is what bit q
-// of x[i] was.  Five rounds swap the off-diagonal blocks of size J.
-template <int J>
-__device__ __forceinline__ void transpose_round(uint32_t (&x)[32]) {
-  constexpr uint32_t M = J == 4 ? 0x0f0f0f0fu : J == 2 ? 0x33333333u : 0x55555555u;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    if ((k & J) == 0) {
-      const uint32_t lo = x[k], hi = x[k + J];
-      if constexpr (J == 16) {          // whole 16-bit halves: byte permutes
-        x[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-        x[k + J] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
-      } else if constexpr (J == 8) {    // whole bytes: byte permutes
-        x[k] = __builtin_amdgcn_perm(hi, lo, 0x06020400u);
-        x[k + J] = __builtin_amdgcn_perm(hi, lo, 0x07030501u);
-      } else {                          // bit fields: two bitfield selects
-        x[k] = (lo & M) | ((hi << J) & ~M);
-        x[k + J] = ((lo >> J) & M) | (hi & ~M);
-      }
-    }
-  }
-}
-__device__ __forceinline__ void transpose32(uint32_t (&x)[32]) {
-  transpose_round<16>(x);
-  transpose_round<8>(x);
-  transpose_round<4>(x);
-  transpose_round<2>(x);
-  transpose_round<1>(x);
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+// LDS transpose read of 8-bit elements (see the header comment)
+__device__ __forceinline__ i32x2 lds_tr8(const uint8_t *p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2 *)(p));
 }
 
 // One block = one query group x one split (a run of `cps` chunks of CH
 // tokens).  Wave wv owns the 64-token blocks wv and wv + 4 of every chunk and
-// everything computed from them: their logits, staged value records, plane
-// words, fixed-point weights and value sums, with an online softmax of its
-// own (running max M and sum of exp per head; the value accumulators are
-// rescaled by exp(M_old - M_new) whenever its tokens raise the max).  The
-// waves therefore never wait for each other inside the chunk loop; their
-// four partial softmax states are merged once at the end.  The key words,
-// value records and value norms of the wave's next tokens are loaded into
-// registers while the current ones are processed.
+// everything computed from them: their logits, staged value records,
+// fixed-point weights and value sums, with an online softmax of its own
+// (running max M and sum of exp per head; the value sums are rescaled by
+// exp(M_old - M_new) whenever its tokens raise the max).  The waves therefore
+// never wait for each other inside the chunk loop; their four partial softmax
+// states are merged once at the end.  The key words and norms of the wave's
+// next tokens are loaded into registers while the current ones are scored,
+// and the next value records are copied into the wave's LDS slot by the
+// memory system (global_load_lds, 16 bytes per lane) during the next logits.
 #ifndef TQ_ATT_WAVES_PER_EU
 #define TQ_ATT_WAVES_PER_EU 2
 #endif
-template <int CB16, int SB16, int W, int VW>
+template <int D, int CB16, int SB16, int W, int VW>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(TQ_ATT_WAVES_PER_EU)))
 attend_partial_kernel(AttArgs a) {
   constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
   using KW = KeyWords<CB16, SB16, W>;
   constexpr int NPL = value_planes(VW);
-  constexpr int VBMAX = 16 * VW;                  // value record bytes (d <= 128)
-  constexpr int VR = VBMAX / 8;                   // 16-byte value units per lane per chunk, at most
-  constexpr int NPMAX = VBMAX * 8;                // bit rows of a value record
+  constexpr int PB = D / 8;                       // bytes per value bit plane
+  constexpr int VCB = (VW * PB + 15) / 16 * 16;   // value record bytes
+  constexpr int NU16 = VCB / 16;                  // 1 KB copies per 64-token block
   constexpr int WT = 128;                         // tokens of a wave per chunk
-  // plane-word rows: bit row P of a 32-token block at plane_index(P), a skew
-  // of 4 words per coordinate tile (16 VW rows) and a block stride of TSTR
-  // words (4 mod 32) spread the LDS banks of both the transposing lanes and
-  // the MFMA operand readers; the rows of the next coordinate tile are then
-  // 16 VW + 4 words on
-  auto plane_index = [](int P) { return P + 4 * (P / (16 * VW)); };
-  constexpr int TSTR = NPMAX + NPMAX / (4 * VW) + 4;
-  // fixed-point weights U = w S 2^(21 - j), [head][token] with a skew of 4
-  // words per 32 tokens
+  // fixed-point weights U = w S 2^21, [head][token] with a skew of 4 words
+  // per 32 tokens
   constexpr int UST = WT + WT / 8 + 4;
   auto uidx = [](int t) { return t + 4 * (t >> 5); };
+  // value record slots: token-major (+ the 8 bytes a d = 64 row read
+  // passes); two per wave where two blocks of 4 waves still fit a CU's LDS
+  // (the next chunk's records are then copied while this chunk is scored),
+  // else one (refilled after the value sum)
+  constexpr int SLOT = WT * VCB + 16;
+  constexpr bool DB = 2 * (4 * (2048 + 2 * SLOT + 16 * UST) + 128) <= 160 * 1024;
+  constexpr int NSLOT = DB ? 2 : 1;
   struct WaveLds {
     float zt[WT][4];                              // scaled logits [token][head]
-    uint32_t vrec[WT * VBMAX / 4];                // staged value records, token-major
-    uint32_t tpl[WT / 32 * TSTR];                 // plane words [32-token block][bit row]
     uint32_t ufix[4 * UST];                       // fixed-point weights
-    float vacc[4][128 + 16];                      // value sums [head][rotated coordinate]
+    union __align__(16) {
+      uint8_t vrec[NSLOT][SLOT];                  // value records
+      float vacc[4][128 + 16];                    // at the end: value sums [head][rotated coordinate]
+    };
   };
   __shared__ __align__(16) WaveLds wl[NT / 64];
   __shared__ float fin[NT / 64][4][2];            // per wave and head: running max, sum of exp
@@ -149,10 +135,8 @@ attend_partial_kernel(AttArgs a) {
   const int hgi = (int)(gidx - kg * a.hg);
   const int c_begin = blockIdx.x * a.cps;
   const int c_end = min(c_begin + a.cps, a.nchunk);
-  const int d = a.d;
+  constexpr int d = D;
   const int64_t T = a.T;
-  const int vcb = a.vcb, nd = vcb / 4;                 // value record dwords
-  const int nct = (d + 15) / 16;                       // 16-coordinate tiles
 
   const uint8_t *prep = a.prep + gidx * prep_stride(NM);
   i32x4 A[NM];
@@ -165,18 +149,15 @@ attend_partial_kernel(AttArgs a) {
   const uint8_t *kcb = a.kcodes + kg * a.ldk * a.kcb;
   const uint8_t *ksb = a.ksigns + kg * a.ldk * a.ksb;
   const float *knb = a.knorms + kg * a.ldk, *krb = a.krnorms + kg * a.ldk;
-  const uint8_t *vcbp = a.vcodes + kg * a.ldk * a.vcb;
+  const uint8_t *vcbp = a.vcodes + kg * a.ldk * VCB;
   const float *vnb = a.vnorms + kg * a.ldk;
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
   // registers of the wave's tokens in flight: key words per 16-key subtile,
-  // key norms one per lane (handed out by cross-lane reads), the value
-  // records of the wave's two 64-token blocks (VR 16-byte units per lane)
-  // and the value norms of tokens lane and lane + 64
+  // key norms one per lane (handed out by cross-lane reads) and the value
+  // norms of tokens lane and lane + 64
   KW kw[2][4];
   float knu[2], kga[2], vn[2];
-  u32x4 vr[VR];
-  const int vunits = 4 * vcb;                        // 16-byte units of a 64-token block
   auto issue = [&](int c) {
     // 32-bit offsets from the group's base pointers (the host checks that a
     // group's records span less than 4 GB) keep the address math short
@@ -198,22 +179,29 @@ attend_partial_kernel(AttArgs a) {
       knu[tt] = load_f32(knb, tl);
       kga[tt] = load_f32(krb, tl);
       vn[tt] = vnb[tl];
-      // value records: clamped 16-byte units (units past the cache end
-      // repeat the last real one; their tokens get zero weight)
-      const int tbc = min(tb, tlast);              // a block past the cache end reads its last token
-      const uint32_t lim = (uint32_t)(min(64, (int)T - tbc) * (vcb / 16)) - 1u;
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(vcbp + (uint32_t)tbc * vcb);
+    }
+  };
+  // the value records of the wave's two 64-token blocks of chunk c into its
+  // LDS slot: each block is one contiguous run of 64 VCB bytes, moved as
+  // 16-byte units (units past the cache end repeat the last real one; their
+  // tokens get zero weight)
+  auto stage_values = [&](int c, int slot) {
+    const int tlast = (int)T - 1;
 #pragma unroll
-      for (int b = 0; b < VR / 2; ++b)
-        if (b * 64 < vunits) vr[tt * (VR / 2) + b] = __builtin_nontemporal_load(src + min((uint32_t)(b * 64 + lane), lim));
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tb = c * CH + (wv + 4 * tt) * 64;
+      const int tbc = min(tb, tlast);              // a block past the cache end reads its last token
+      const uint32_t lim = (uint32_t)(min(64, (int)T - tbc) * NU16) - 1u;
+      const uint8_t *src = vcbp + (uint32_t)tbc * VCB;
+      uint8_t *dst = L.vrec[slot] + tt * 64 * VCB;
+#pragma unroll
+      for (int i = 0; i < NU16; ++i)
+        __builtin_amdgcn_global_load_lds(src + 16 * min((uint32_t)(i * 64 + lane), lim),
+                                         (__attribute__((address_space(3))) void *)(dst + i * 1024), 16, 0,
+                                         2 /* nt */);
     }
   };
 
-  // B operand masks of the value sum: lane group g takes bits 4 (g & 1) + e
-  // of each byte of its plane word (dword e of the operand)
-  const int vhalf = grp & 1;
-  const uint32_t bm0 = 0x01010101u << (4 * vhalf), bm1 = bm0 << 1, bm2 = bm0 << 2, bm3 = bm0 << 3;
-  auto vplanes = [&](uint32_t w) { return i32x4{(int)(w & bm0), (int)(w & bm1), (int)(w & bm2), (int)(w & bm3)}; };
   // within-wave ordering of LDS accesses between lanes (the waves never wait
   // for each other)
   // (the LDS executes a wave's instructions in order, so the compiler only
@@ -227,21 +215,27 @@ attend_partial_kernel(AttArgs a) {
 
   float M[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};
-  float *vac = &L.vacc[grp][col];                  // coordinate 16 ct + col of head grp: vac[16 ct]
+  // value sums of head grp, coordinates 8 col + j (rotated domain)
+  float vac[8];
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) vac[16 * ct] = 0.f;
-  int pr0[VW];
-#pragma unroll
-  for (int p = 0; p < VW; ++p) pr0[p] = plane_index(col * VW + p);
+  for (int j = 0; j < 8; ++j) vac[j] = 0.f;
   // A operand of the value sum: lane (row m = 4 h + digit, group g) holds, at
-  // dword e and byte b, digit (m & 3) of head (m >> 2) for the wave's token
-  // 64 tt + 32 (g >> 1) + 8 b + 4 (g & 1) + e, negated for bit 7 (B byte -128)
+  // dword e and byte b, digit (m & 3) of head (m >> 2) for token
+  // 16 g + 4 e + b of a 64-token block
   const int ah = col >> 2, ash = 21 - 7 * (col & 3);
+  // B operand rows: lane 2r + h of each 16-lane group names bytes 8h .. 8h+7
+  // of token 16 grp + r (and 16 grp + 8 + r) in a plane
+  const int brow = (16 * grp + (col >> 1)) * VCB + 8 * (col & 1);
+  float K = 0.f;
+#pragma unroll
+  for (int pl = 0; pl < NPL; ++pl) K += a.vbasis[pl];
 
   issue(c_begin);
+  stage_values(c_begin, 0);
   for (int c = c_begin; c < c_end; ++c) {
     const int64_t tbeg = (int64_t)c * CH;
-    // ---- A: logits of the wave's tokens into LDS; value records staged
+    const int slot = DB ? (c - c_begin) & 1 : 0;
+    // ---- A: logits of the wave's tokens into LDS
     float lg[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -266,19 +260,16 @@ attend_partial_kernel(AttArgs a) {
         mz = fmaxf(mz, z);
         if (a.logits && head < a.qpg && t < T) a.logits[(kg * a.qpg + head) * T + t] = lg[tt][s];
       }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int b = 0; b < VR / 2; ++b)
-        if (b * 64 + lane < vunits) reinterpret_cast<u32x4 *>(L.vrec)[tt * vunits + b * 64 + lane] = vr[tt * (VR / 2) + b];
     const float vnl0 = vn[0], vnl1 = vn[1];
     const bool v0 = tbeg + wv * 64 + lane < T, v1 = tbeg + (wv + 4) * 64 + lane < T;
-    if (c + 1 < c_end) issue(c + 1);
+    if (c + 1 < c_end) {
+      issue(c + 1);
+      if constexpr (DB) stage_values(c + 1, slot ^ 1);
+    }
     wave_sync();
 
     // ---- B: the wave's running max per head (row grp of every lane holds
-    // head grp), rescale factors; plane words of the staged value records;
-    // fixed-point weights
+    // head grp), rescale factors; fixed-point weights
     mz = row_max(mz);
     float f[4];
 #pragma unroll
@@ -290,38 +281,16 @@ attend_partial_kernel(AttArgs a) {
       lsum[h] *= f[h];
     }
     // weights w = exp(z - M) nu <= numax, in units of numax / 127: u = w S,
-    // S = 127 / numax, so u <= 127.  The A operand carries u 2^-j (the B byte
-    // of bit j of a plane word is 2^j) as four base-128 digits: the bits of
-    // U = u 2^(21 - j), an integer below 2^28.
+    // S = 127 / numax, so u <= 127; the A operand carries the four base-128
+    // digits of U = u 2^21, an integer below 2^28
     const float numax = wave_max(fmaxf(v0 ? vnl0 : 0.f, v1 ? vnl1 : 0.f));
     const float S = numax > 0.f ? 127.f / numax : 1.f;
-    {
-      // lane (record dword k, 32-token block beta) transposes dword k of 32
-      // tokens.  Word i is read from token (i + 3 beta) mod 32 (so that the
-      // lanes spread over the LDS banks) and the transposed words are rotated
-      // back.
-      const int ntr = nd * (WT / 32);
-      if (lane < ntr) {
-        const int k = lane % nd, beta = lane / nd, rot = (3 * beta) & 31;
-        uint32_t x[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) x[i] = L.vrec[(32 * beta + ((i + rot) & 31)) * nd + k];
-        transpose32(x);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          u32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_alignbit(x[4 * i + e], x[4 * i + e], (32 - rot) & 31);
-          *reinterpret_cast<u32x4 *>(&L.tpl[beta * TSTR + plane_index(32 * k + 4 * i)]) = v;
-        }
-      }
-    }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t = tt * 64 + lane;
       const float4 z4 = *reinterpret_cast<const float4 *>(&L.zt[t][0]);
       const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
-      const float sc = (tt ? vnl1 : vnl0) * S * __builtin_amdgcn_ldexpf(1.f, 21 - (lane & 7));
+      const float sc = (tt ? vnl1 : vnl0) * S * 0x1.0p21f;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         // 0 for masked tokens (z = -inf; M is -inf too while none of the
@@ -340,74 +309,100 @@ attend_partial_kernel(AttArgs a) {
       i32x4 Aw[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const int tb = tt * 64 + 32 * (grp >> 1) + 4 * (grp & 1);
-        uint32_t dw[4] = {0u, 0u, 0u, 0u};
+        const int tb = tt * 64 + 16 * grp;
+        uint32_t dw[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const u32x4 u = *reinterpret_cast<const u32x4 *>(&L.ufix[ah * UST + uidx(tb + 8 * b)]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dw[e] |= __builtin_amdgcn_ubfe(u[e], ash, 7) << (8 * b);
+        for (int e = 0; e < 4; ++e) {
+          const u32x4 u = *reinterpret_cast<const u32x4 *>(&L.ufix[ah * UST + uidx(tb + 4 * e)]);
+          dw[e] = __builtin_amdgcn_ubfe(u[0], ash, 7) | (__builtin_amdgcn_ubfe(u[1], ash, 7) << 8) |
+                  (__builtin_amdgcn_ubfe(u[2], ash, 7) << 16) | (__builtin_amdgcn_ubfe(u[3], ash, 7) << 24);
         }
-        // bytes of bit 7 (dword 3 of the odd lane groups) negated bytewise
-        if (grp & 1) dw[3] = (0x80808080u - dw[3]) ^ 0x80808080u;
         Aw[tt] = i32x4{(int)dw[0], (int)dw[1], (int)dw[2], (int)dw[3]};
       }
-      // W = sum of the weights (all-ones B), the offset of every plane, as
-      // digit pairs; K = sum of the plane coefficients
-      const i32x4 ones = vplanes(0xffffffffu);
+      // W = sum of the weights (all-ones B) as digit pairs
+      const i32x4 ones = i32x4{0x01010101, 0x01010101, 0x01010101, 0x01010101};
       i32x4 accW = mfma8(Aw[0], ones, i32x4{0, 0, 0, 0});
       accW = mfma8(Aw[1], ones, accW);
-      float K = 0.f;
-#pragma unroll
-      for (int pl = 0; pl < NPL; ++pl) K += a.vbasis[pl];
       const float KWh = K * (float)(accW[0] * 128 + accW[1]), KWl = K * (float)(accW[2] * 128 + accW[3]);
-      const uint32_t *tw0 = &L.tpl[(grp >> 1) * TSTR];
-      const uint32_t *tw1 = &L.tpl[(2 + (grp >> 1)) * TSTR];
-      // fixed trip count (the tiles past d are skipped) so that the MFMAs of
-      // one tile overlap the recombination of the previous one
+      // plane bytes of the lane's octet for its 16 tokens of each block: the
+      // single planes by transpose reads, the triples by XOR
+      u32x4 pb4[2][NPL];
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        if (ct >= nct) break;
-        // bit rows of coordinate 16 ct + col.  Rows past the record hold no
-        // bit of a real coordinate: they only reach coordinates >= d, whose
-        // sums are never used, and lie inside the row (16 nct VW <= NPMAX)
-        int pr[VW];
+      for (int tt = 0; tt < 2; ++tt) {
+        const uint8_t *r0 = L.vrec[slot] + tt * 64 * VCB + brow;
 #pragma unroll
-        for (int p = 0; p < VW; ++p) pr[p] = pr0[p] + (16 * VW + 4) * ct;
-        i32x4 pacc[NPL];
-#pragma unroll
-        for (int pl = 0; pl < NPL; ++pl) pacc[pl] = i32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const uint32_t *tw = tt ? tw1 : tw0;
-          uint32_t pw[VW];
-#pragma unroll
-          for (int p = 0; p < VW; ++p) pw[p] = tw[pr[p]];
-#pragma unroll
-          for (int p = 0; p < VW; ++p) pacc[p] = mfma8(Aw[tt], vplanes(pw[p]), pacc[p]);
-          if constexpr (VW == 3) {
-            pacc[3] = mfma8(Aw[tt], vplanes(pw[0] ^ pw[1] ^ pw[2]), pacc[3]);
-          } else if constexpr (VW == 4) {
-            pacc[4] = mfma8(Aw[tt], vplanes(pw[0] ^ pw[1] ^ pw[2]), pacc[4]);
-            pacc[5] = mfma8(Aw[tt], vplanes(pw[0] ^ pw[1] ^ pw[3]), pacc[5]);
-            pacc[6] = mfma8(Aw[tt], vplanes(pw[0] ^ pw[2] ^ pw[3]), pacc[6]);
-            pacc[7] = mfma8(Aw[tt], vplanes(pw[1] ^ pw[2] ^ pw[3]), pacc[7]);
-          }
+        for (int p = 0; p < VW; ++p) {
+          const i32x2 lo = lds_tr8(r0 + p * PB), hi = lds_tr8(r0 + p * PB + 8 * VCB);
+          pb4[tt][p] = u32x4{(unsigned)lo[0], (unsigned)lo[1], (unsigned)hi[0], (unsigned)hi[1]};
         }
-        // sum_P A_P (2 V_P - W): digit pairs (d0 * 128 + d1, d2 * 128 + d3) of
-        // every plane are exact in int32 and in fp32 (below 2^23)
+        if constexpr (VW == 3) {
+          pb4[tt][3] = pb4[tt][0] ^ pb4[tt][1] ^ pb4[tt][2];
+        } else if constexpr (VW == 4) {
+          pb4[tt][4] = pb4[tt][0] ^ pb4[tt][1] ^ pb4[tt][2];
+          pb4[tt][5] = pb4[tt][0] ^ pb4[tt][1] ^ pb4[tt][3];
+          pb4[tt][6] = pb4[tt][0] ^ pb4[tt][2] ^ pb4[tt][3];
+          pb4[tt][7] = pb4[tt][1] ^ pb4[tt][2] ^ pb4[tt][3];
+        }
+      }
+      // coordinate 8 col + j, j = 0..7: the MFMAs of j are issued before the
+      // recombination of j - 1 (two accumulator sets), and the scheduler is
+      // kept from mixing more iterations (their operands would not fit)
+      i32x4 pacc[2][NPL];
+      auto products = [&](int j, i32x4 (&acc)[NPL]) {
+        const unsigned msk = 0x01010101u << j;
+#pragma unroll
+        for (int pl = 0; pl < NPL; ++pl) {
+          const u32x4 b0 = pb4[0][pl] & msk, b1 = pb4[1][pl] & msk;
+          acc[pl] = mfma8(Aw[0], i32x4{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3]}, i32x4{0, 0, 0, 0});
+          acc[pl] = mfma8(Aw[1], i32x4{(int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]}, acc[pl]);
+        }
+      };
+      // sum_P A_P (2 V_P - W): digit pairs (d0 * 128 + d1, d2 * 128 + d3) of
+      // every plane are exact in int32; the byte value 2^j (-128 for j = 7)
+      // is divided out here
+      auto recombine = [&](int j, const i32x4 (&acc)[NPL]) {
         float sh = 0.f, sl = 0.f;
 #pragma unroll
         for (int pl = 0; pl < NPL; ++pl) {
-          sh = fmaf(a.vbasis[pl], (float)(pacc[pl][0] * 128 + pacc[pl][1]), sh);
-          sl = fmaf(a.vbasis[pl], (float)(pacc[pl][2] * 128 + pacc[pl][3]), sl);
+          sh = fmaf(a.vbasis[pl], (float)(acc[pl][0] * 128 + acc[pl][1]), sh);
+          sl = fmaf(a.vbasis[pl], (float)(acc[pl][2] * 128 + acc[pl][3]), sl);
         }
-        const float v = fmaf(fmaf(2.f, sl, -KWl), 0x1.0p-21f, fmaf(2.f, sh, -KWh) * 0x1.0p-7f);
-        vac[16 * ct] = fmaf(v, invS, vac[16 * ct] * fg);
+        const float tj = j == 7 ? -0x1.0p-6f : 2.f / (float)(1 << j);   // 2 / byte value
+        const float v = fmaf(fmaf(tj, sl, -KWl), 0x1.0p-21f, fmaf(tj, sh, -KWh) * 0x1.0p-7f);
+        vac[j] = fmaf(v, invS, vac[j] * fg);
+        // (an empty asm keeps the recombination here: unpinned, the compiler
+        // defers every recombination past all 64 products, whose results
+        // then no longer fit in registers)
+        __asm__ volatile("" : "+v"(vac[j]));
+      };
+      if constexpr (NPL <= 4) {
+        products(0, pacc[0]);
+#pragma unroll
+        for (int j = 1; j < 8; ++j) {
+          products(j, pacc[j & 1]);
+          recombine(j - 1, pacc[(j - 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        recombine(7, pacc[1]);
+      } else {          // 4-bit values: one set (two would spill)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          products(j, pacc[0]);
+          recombine(j, pacc[0]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-    wave_sync();          // the wave's zt, vrec, tpl and ufix are rewritten for its next tokens
+    __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): the slot's reads are done
+    wave_sync();          // the wave's zt, vrec and ufix are rewritten for its next tokens
+    if constexpr (!DB) {
+      if (c + 1 < c_end) stage_values(c + 1, 0);
+    }
   }
+  wave_sync();            // the slots' last reads are done: vacc reuses them
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (8 * col + j < d) L.vacc[grp][8 * col + j] = vac[j];
 
   // ---- D: merge the four waves' softmax states: every wave's sums are
   // rescaled to the block max of each head
@@ -534,20 +529,21 @@ __global__ void __launch_bounds__(256) attend_probs_kernel(const float *logits, 
     probs[row * T + t] = __expf(scale * logits[row * T + t] - M) * invL;
 }
 
-// Key geometries d <= 128 produces (one sign word per lane group) x value
+// Key geometries of d = 64 and 128 (one sign word per lane group) x value
 // code widths 1..4.
 int dispatch(const AttArgs &a, dim3 grid, int cb16, int sb16, int w, int vw, hipStream_t s) {
-#define TQ_CASE_V(C, S, W_, V)                                         \
+#define TQ_CASE_V(D_, C, S, W_, V)                                     \
   if (vw == V) {                                                       \
-    attend_partial_kernel<C, S, W_, V><<<grid, NT, 0, s>>>(a);         \
+    attend_partial_kernel<D_, C, S, W_, V><<<grid, NT, 0, s>>>(a);     \
     return hip_status();                                               \
   }
-#define TQ_CASE(C, S, W_)                                              \
-  if (cb16 == C && sb16 == S && w == W_) {                             \
-    TQ_CASE_V(C, S, W_, 1) TQ_CASE_V(C, S, W_, 2) TQ_CASE_V(C, S, W_, 3) TQ_CASE_V(C, S, W_, 4) \
+#define TQ_CASE(D_, C, S, W_)                                          \
+  if (a.d == D_ && cb16 == C && sb16 == S && w == W_) {                \
+    TQ_CASE_V(D_, C, S, W_, 1) TQ_CASE_V(D_, C, S, W_, 2) TQ_CASE_V(D_, C, S, W_, 3) TQ_CASE_V(D_, C, S, W_, 4) \
     return TQ_ENOTSUP;                                                 \
   }
-  TQ_CASE(1, 1, 1) TQ_CASE(1, 1, 2) TQ_CASE(2, 1, 2) TQ_CASE(1, 1, 3) TQ_CASE(2, 1, 3) TQ_CASE(3, 1, 3)
+  TQ_CASE(64, 1, 1, 1) TQ_CASE(64, 1, 1, 2) TQ_CASE(64, 2, 1, 3)
+  TQ_CASE(128, 1, 1, 1) TQ_CASE(128, 2, 1, 2) TQ_CASE(128, 3, 1, 3)
 #undef TQ_CASE
 #undef TQ_CASE_V
   return TQ_ENOTSUP;
@@ -555,14 +551,14 @@ int dispatch(const AttArgs &a, dim3 grid, int cb16, int sb16, int w, int vw, hip
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
-// ------------------------------------------------------------ d > 128
-// Vectors longer than 128 coordinates take three steps: the logits by the
+// ------------------------------------------------------------ other d
+// Vectors of other lengths than 64 and 128 take three steps: the logits by the
 // scores kernels (into the logits output, or the workspace), a value-sum
 // kernel that reads them back with the same online softmax per run of chunks
 // and accumulates sum_t exp(z_t - M) nu_t c_v[idx_t] on the VALU, and the
 // combine (and probs) kernels above.  Block = (query group of 4 heads, run of
-// chunks); thread = (token lane, 4 consecutive coordinates), so that the
-// codes of its coordinates are one bit field of a record word pair.
+// chunks); thread = (token lane, 4 consecutive coordinates), so that each
+// bit plane of a value record holds the thread's coordinates as one nibble.
 constexpr int VT = 64;             // tokens per value tile
 
 struct VsumArgs {
@@ -602,7 +598,6 @@ __global__ void __launch_bounds__(256) attend_vsum_kernel(VsumArgs a) {
   for (int e = 0; e < 4; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
   const int64_t t_begin = (int64_t)blockIdx.x * a.cps * CH;
   const int64_t t_end = min(t_begin + (int64_t)a.cps * CH, a.T);
-  const uint32_t cmask = (1u << vw) - 1u;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += VT) {
     const int ntok = (int)min((int64_t)VT, t_end - t0);
     for (int i = tid; i < VT * vcw; i += 256) {
@@ -629,16 +624,23 @@ __global__ void __launch_bounds__(256) attend_vsum_kernel(VsumArgs a) {
       acc[e].w *= fs.w;
     }
     if (act) {
-      const int bit = 4 * qi * vw, wi = bit >> 5, sh = bit & 31;
+      // bit planes: plane pl holds the 4 coordinates' bits as one nibble at
+      // record bit pl d + 4 qi (never across a word)
       for (int tok = tl; tok < ntok; tok += nl) {
         const float4 w4 = wt[tok];
         const uint32_t *rw = vrec + tok * vcw;
-        uint32_t bits = rw[wi] >> sh;
-        // the field's bits lie inside the record, so word wi + 1 exists here
-        if (sh + 4 * vw > 32) bits |= rw[wi + 1] << (32 - sh);
+        uint32_t nib[4];
+#pragma unroll
+        for (int pl = 0; pl < 4; ++pl) {
+          const int bit = pl * d + 4 * qi;
+          nib[pl] = pl < vw ? (rw[bit >> 5] >> (bit & 31)) & 0xfu : 0u;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float c = cbk[(bits >> (e * vw)) & cmask];
+          uint32_t code = 0;
+#pragma unroll
+          for (int pl = 0; pl < 4; ++pl) code |= ((nib[pl] >> e) & 1u) << pl;
+          const float c = cbk[code];
           acc[e].x = fmaf(c, w4.x, acc[e].x);
           acc[e].y = fmaf(c, w4.y, acc[e].y);
           acc[e].z = fmaf(c, w4.z, acc[e].z);
@@ -685,8 +687,8 @@ size_t attend_ws_bytes(const tq_ctx *k, int64_t G, int qpg, int64_t T) {
   const int nm = mfma_count(k->cw16, k->sign_bytes / 16, k->hp.w);
   const int64_t nchunk = (T + CH - 1) / CH;
   const int d = k->hp.d;
-  // d > 128: the logits of the three-step path as well
-  const int64_t lg = d > 128 ? align256(G * qpg * T * 4) : 0;
+  // the three-step path (d other than 64 and 128): the logits as well
+  const int64_t lg = !attend_fused(d) ? align256(G * qpg * T * 4) : 0;
   return (size_t)(align256(G * hg * prep_stride(nm)) + align256(G * hg * nchunk * 4 * (d + 2) * 4) +
                   align256(G * qpg * 2 * 4) + lg);
 }
@@ -695,8 +697,8 @@ int check_attend(const tq_ctx *kc, const tq_ctx *vc, int64_t G, int qpg, int64_t
                  bool want_probs) {
   const int d = kc->hp.d;
   if (vc->hp.w < 1 || vc->hp.w > 4) return TQ_ENOTSUP;
-  // the fused kernel (d <= 128) holds a value record in 16 w bytes
-  if (d <= 128 && vc->code_bytes > 16 * vc->hp.w) return TQ_ENOTSUP;
+  // the fused kernel holds a value record in 16 w bytes
+  if (attend_fused(d) && vc->code_bytes > 16 * vc->hp.w) return TQ_ENOTSUP;
   const int64_t groups = G * ((qpg + 3) / 4);
   if (groups > 65535 || T > 0x7fffffff - CH || G * qpg > 0x7fffffff) return TQ_ENOTSUP;
   const int64_t rec_max = std::max<int64_t>(std::max(kc->code_bytes, kc->sign_bytes), vc->code_bytes);
@@ -734,7 +736,7 @@ int launch_attend(const tq_ctx *kc, const tq_ctx *vc, const float *q, int64_t G,
   if (want < 1) want = 1;
   const int cps = (int)((nchunk + want - 1) / want);
   const int nsplit = (int)((nchunk + cps - 1) / cps);
-  if (d > 128) {
+  if (!attend_fused(d)) {
     float *lg = logits ? logits
                        : reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(mstat) + align256(G * qpg * 2 * 4));
     st = launch_scores_prepared(kc, prep, G, qpg, T, ldk, kcodes, ksigns, knorms, krnorms, lg, stream);

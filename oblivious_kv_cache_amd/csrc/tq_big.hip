@@ -34,6 +34,7 @@ struct QBigArgs {
   // cpos2), and the codes are stored as bit planes per coordinate quarter
   int frac, w2;
   float tpos2[8], cpos2[8];
+  int planes;          // MSE-only records: codes as bit planes of d bits
 };
 
 template <bool BF16IN>
@@ -159,6 +160,12 @@ __global__ void __launch_bounds__(256) quantize_big_kernel(QBigArgs a) {
           const int base = g < 2 ? g * a.w * wpp : 2 * a.w * wpp + (g - 2) * a.w2 * wpp;
           for (int pl = 0; pl < cw; ++pl)
             if ((idx >> pl) & 1u) atomicOr(&cwl[col * cwn + base + pl * wpp + (jq >> 5)], 1u << (jq & 31));
+        } else if (a.planes) {
+          // MSE-only records: bit pl of code i at record bit pl d + i
+          for (int pl = 0; pl < a.w; ++pl) {
+            const int bit = pl * a.d + i;
+            if ((idx >> pl) & 1u) atomicOr(&cwl[col * cwn + (bit >> 5)], 1u << (bit & 31));
+          }
         } else {
           const int bit = i * a.w;
           if (idx) {
@@ -487,6 +494,7 @@ int launch_quantize_big(const tq_ctx *ctx, const void *x, int dtype, int64_t n, 
   }
   a.frac = ctx->frac;
   a.w2 = ctx->hp.w2;
+  a.planes = ctx->hp.mode == TQ_MODE_MSE;
   const bool bf16 = dtype == TQ_BF16;
   const int NK = a.dpad / 32;
   const size_t frag_bytes = sizeof(Frag) * 64 * (size_t)NK * ((bf16 ? 1 : 2) + 2);

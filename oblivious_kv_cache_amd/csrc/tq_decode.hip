@@ -28,7 +28,8 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_prep_kernel(QArgs qk, int 
   if (b < kb) {
     quantize_body<128, BF16IN, true, 1, WK, true, DEC_THREADS>(qk, sm.lds, b, kb);
   } else if (WV > 0 && b < kb + vb) {
-    quantize_body<128, BF16IN, true, 1, (WV > 0 ? WV : 1), false, DEC_THREADS>(qv, sm.lds, b - kb, vb);
+    // values: MSE-only records (bit planes)
+    quantize_body<128, BF16IN, true, 1, (WV > 0 ? WV : 1), false, DEC_THREADS, true>(qv, sm.lds, b - kb, vb);
   } else {
     const int half = threadIdx.x >> 8;
     const int g = 2 * (b - kb - vb) + half;

@@ -30,6 +30,7 @@ struct DqArgs {
   int nlev;           // polar mode: L = log2 d
   int frac, w2;       // fractional widths: second-half code bits and centroids
   float c2[16];
+  int planes;         // MSE-only records: bit pl of code i at record bit pl d + i
 };
 
 // Record slot of the angle of node j at level l (polar layout: slots
@@ -75,6 +76,13 @@ __global__ void __launch_bounds__(256) dequant_kernel(DqArgs a) {
           code |= (uint32_t)((rec[bit >> 3] >> (bit & 7)) & 1) << pl;
         }
         cv[j] = g < 2 ? a.c[code] : a.c2[code];
+      } else if (a.planes) {
+        uint32_t code = 0;
+        for (int pl = 0; pl < a.w; ++pl) {
+          const int bit = pl * a.d + j;
+          code |= (uint32_t)((rec[bit >> 3] >> (bit & 7)) & 1) << pl;
+        }
+        cv[j] = a.c[code];
       } else {
         cv[j] = a.c[code_at(j)];
       }
@@ -126,6 +134,7 @@ int launch_dequant(const tq_ctx *ctx, const uint8_t *codes, const uint8_t *signs
   }
   a.frac = ctx->frac;
   a.w2 = ctx->hp.w2;
+  a.planes = ctx->hp.mode == TQ_MODE_MSE;
   a.pcs = ctx->hp.mode == TQ_MODE_POLAR ? ctx->polar_cs : nullptr;
   a.nlev = 0;
   while ((1 << a.nlev) < a.d) ++a.nlev;

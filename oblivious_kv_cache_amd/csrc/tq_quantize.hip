@@ -11,22 +11,24 @@ __host__ __device__ constexpr int quant_threads(bool use_lds, int w, bool bf16in
   return use_lds ? (w == 3 && bf16in ? 768 : 512) : 256;
 }
 
-template <int DPAD, bool BF16IN, bool USE_LDS, int NTL, int W, bool FULL>
+template <int DPAD, bool BF16IN, bool USE_LDS, int NTL, int W, bool FULL, bool PLANES>
 __global__ void __launch_bounds__(quant_threads(USE_LDS, W, BF16IN)) quantize_kernel(QArgs a) {
   constexpr int FR = (DPAD / 16) * (DPAD / 32);
   __shared__ Frag lds[USE_LDS ? 4 * FR * 64 : 1];
-  quantize_body<DPAD, BF16IN, USE_LDS, NTL, W, FULL, quant_threads(USE_LDS, W, BF16IN)>(a, lds, blockIdx.x,
-                                                                                     gridDim.x);
+  quantize_body<DPAD, BF16IN, USE_LDS, NTL, W, FULL, quant_threads(USE_LDS, W, BF16IN), PLANES>(
+      a, lds, blockIdx.x, gridDim.x);
 }
 
-template <int DPAD, bool BF16IN, bool USE_LDS, int NTL, bool FULL>
+// PLANES: MSE-only records (bit planes); W = 1 takes the stream form, which is
+// the same bytes
+template <int DPAD, bool BF16IN, bool USE_LDS, int NTL, bool FULL, bool PLANES>
 int launch_w(const QArgs &a, int w, int blocks, hipStream_t s) {
   switch (w) {
-#define TQ_W(W_)                                                                                      \
+#define TQ_W(W_, P_)                                                                                  \
     case W_:                                                                                          \
-      quantize_kernel<DPAD, BF16IN, USE_LDS, NTL, W_, FULL><<<blocks, quant_threads(USE_LDS, W_, BF16IN), 0, s>>>(a); \
+      quantize_kernel<DPAD, BF16IN, USE_LDS, NTL, W_, FULL, P_><<<blocks, quant_threads(USE_LDS, W_, BF16IN), 0, s>>>(a); \
       break;
-    TQ_W(1) TQ_W(2) TQ_W(3) TQ_W(4)
+    TQ_W(1, false) TQ_W(2, PLANES) TQ_W(3, PLANES) TQ_W(4, PLANES)
 #undef TQ_W
     default: return TQ_ENOTSUP;
   }
@@ -41,10 +43,13 @@ int launch_d(const QArgs &a, int w, bool bf16, int cus, hipStream_t s) {
   const int blocks = (int)(want < cap ? (want > 0 ? want : 1) : cap);
   const bool full = a.d == DPAD && a.m == (a.prod ? DPAD : 0);
   if (full && a.prod)
-    return bf16 ? launch_w<DPAD, true, USE_LDS, NTL, true>(a, w, blocks, s)
-                : launch_w<DPAD, false, USE_LDS, NTL, true>(a, w, blocks, s);
-  return bf16 ? launch_w<DPAD, true, USE_LDS, NTL, false>(a, w, blocks, s)
-              : launch_w<DPAD, false, USE_LDS, NTL, false>(a, w, blocks, s);
+    return bf16 ? launch_w<DPAD, true, USE_LDS, NTL, true, false>(a, w, blocks, s)
+                : launch_w<DPAD, false, USE_LDS, NTL, true, false>(a, w, blocks, s);
+  if (!a.prod)
+    return bf16 ? launch_w<DPAD, true, USE_LDS, NTL, false, true>(a, w, blocks, s)
+                : launch_w<DPAD, false, USE_LDS, NTL, false, true>(a, w, blocks, s);
+  return bf16 ? launch_w<DPAD, true, USE_LDS, NTL, false, false>(a, w, blocks, s)
+              : launch_w<DPAD, false, USE_LDS, NTL, false, false>(a, w, blocks, s);
 }
 
 }  // namespace

@@ -82,14 +82,21 @@ __device__ __forceinline__ void zero_bytes(uint8_t *dst, int nb) {
 // `block` of `nblocks` blocks of NTHR threads working on this quantize job;
 // `lds` holds the operand fragments (USE_LDS: 4 FR x 64 Frags, filled here by
 // the block's NTHR threads).
-template <int DPAD, bool BF16IN, bool USE_LDS, int NTL, int W, bool FULL, int NTHR>
+//
+// PLANES (MSE-only contexts): the codes are stored as W bit planes of d bits
+// (plane p in record bytes [p d/8, (p+1) d/8), bit p of code i at bit i), so
+// a lane holds PW words per plane for its PER coordinates and stores PER/8
+// bytes into each plane.  (With W = 1 both layouts are the same.)
+template <int DPAD, bool BF16IN, bool USE_LDS, int NTL, int W, bool FULL, int NTHR, bool PLANES = false>
 __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int block, int nblocks) {
   constexpr int NT = DPAD / 16;       // 16-row output tiles (coordinates)
   constexpr int NK = DPAD / 32;       // 32-deep k blocks
   constexpr int FR = NT * NK;         // operand fragments per matrix
   constexpr int PER = DPAD / 4;       // coordinates (and sketch rows) per lane
   constexpr int HALF = (1 << W) / 2;  // L / 2
-  constexpr int CW = (PER * W + 31) / 32;   // code words per lane
+  constexpr bool PL = PLANES && W > 1;
+  constexpr int PW = (PER + 31) / 32;       // words per bit plane (PL)
+  constexpr int CW = PL ? W * PW : (PER * W + 31) / 32;   // code words per lane
   constexpr int SW = (PER + 31) / 32;       // sign words per lane
   constexpr int CBYTES = PER * W / 8;       // code bytes per lane (whole bytes: PER % 8 == 0)
   constexpr int SBYTES = PER / 8;
@@ -316,14 +323,22 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
             if constexpr (!FULL) {
               if (li >= nval) idx = 0u;      // padding coordinates
             }
-            const int bit = li * W;
-            cw[t][bit >> 5] |= idx << (bit & 31);
-            if (((bit & 31) + W) > 32) cw[t][(bit >> 5) + 1] |= idx >> (32 - (bit & 31));
-            // packed here and now (an empty asm reads the word): otherwise the
-            // search results of many coordinates stay live, as lane masks in
-            // scalar registers, until the compiler's chosen packing spot, and
-            // spill
-            __asm__ volatile("" : "+v"(cw[t][bit >> 5]));
+            if constexpr (PL) {
+#pragma unroll
+              for (int pl = 0; pl < W; ++pl) {
+                cw[t][pl * PW + (li >> 5)] |= ((idx >> pl) & 1u) << (li & 31);
+                __asm__ volatile("" : "+v"(cw[t][pl * PW + (li >> 5)]));
+              }
+            } else {
+              const int bit = li * W;
+              cw[t][bit >> 5] |= idx << (bit & 31);
+              if (((bit & 31) + W) > 32) cw[t][(bit >> 5) + 1] |= idx >> (32 - (bit & 31));
+              // packed here and now (an empty asm reads the word): otherwise the
+              // search results of many coordinates stay live, as lane masks in
+              // scalar registers, until the compiler's chosen packing spot, and
+              // spill
+              __asm__ volatile("" : "+v"(cw[t][bit >> 5]));
+            }
           }
           if constexpr (!FULL) {
             if (li >= nval) r = 0.f;
@@ -376,7 +391,16 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
       if (valid[t]) {
         uint8_t *rec = a.codes + vi[t] * a.ldr * a.code_bytes;
         const int off = grp * CBYTES;
-        if constexpr (CEXACT) {
+        if constexpr (PL) {
+          // plane pl: this lane group's PER bits at record bit pl d + grp PER
+          // (the bytes of real coordinates only; d is a multiple of 8)
+          const int pb = a.d >> 3, nb = min(PER / 8, max(0, pb - grp * (PER / 8)));
+#pragma unroll
+          for (int pl = 0; pl < W; ++pl)
+            store_bytes<PW>(rec + pl * pb + grp * (PER / 8),
+                            *reinterpret_cast<const uint32_t(*)[PW]>(&cw[t][pl * PW]), nb);
+          if (grp == 3 && W * pb < a.code_bytes) zero_bytes(rec + W * pb, a.code_bytes - W * pb);
+        } else if constexpr (CEXACT) {
           // the 4 lane groups' byte runs tile the record exactly, dword-aligned
 #pragma unroll
           for (int i = 0; i < CBYTES / 4; ++i) reinterpret_cast<uint32_t *>(rec + off)[i] = cw[t][i];

@@ -45,6 +45,10 @@ from .quant import (
     record_sizes,
     pack_bits,
     unpack_bits,
+    pack_planes,
+    unpack_planes,
+    pack_codes,
+    unpack_codes,
     quantize_one,
     quantize,
     stage2_from_codes,
@@ -64,7 +68,8 @@ from .estimate import (
 __all__ = [
     "splitmix64_stream", "gaussian_stream", "haar_rotation", "jl_matrix",
     "lloyd_max_gaussian", "gaussian_distortion", "codebook", "TQParams",
-    "make_params", "record_sizes", "pack_bits", "unpack_bits", "quantize_one",
+    "make_params", "record_sizes", "pack_bits", "unpack_bits", "pack_planes", "unpack_planes",
+    "pack_codes", "unpack_codes", "quantize_one",
     "quantize", "stage2_from_codes", "dequant", "prep_query", "scores_one", "scores", "softmax",
     "attend", "topk", "exact_top1", "recall_at_k",
 ]

@@ -15,7 +15,7 @@ scale).
 
 import numpy as np
 
-from .quant import unpack_bits
+from .quant import unpack_bits, unpack_codes
 
 
 def prep_query(p, q):
@@ -29,7 +29,7 @@ def prep_query(p, q):
 def scores_one(p, q, code_rec, sign_rec, norm, rnorm):
     """Logit of one query against one packed key, written out term by term."""
     q = np.asarray(q, np.float64)
-    idx = unpack_bits(code_rec[None, :], p.w, p.d)[0]
+    idx = unpack_codes(p, code_rec[None, :])[0]
     approx = float(np.dot(p.Pi @ q, p.c[idx]))
     if p.mode != "prod":
         return float(norm) * approx
@@ -41,7 +41,7 @@ def scores_one(p, q, code_rec, sign_rec, norm, rnorm):
 def scores(p, Q, codes, signs, norms, rnorms):
     """Logits [nq, n] of queries Q[nq, d] against n packed keys."""
     q_rot, q_s = prep_query(p, Q)
-    idx = unpack_bits(codes, p.w, p.d)
+    idx = unpack_codes(p, codes)
     approx = q_rot @ p.c[idx].T                      # [nq, n]
     nu = np.asarray(norms, np.float64)[None, :]
     if p.mode != "prod":

@@ -14,11 +14,13 @@ Steps, in the pages' order:
     189244, "第二步：QJL"; suzuke blog, "第三步"); sign(0) counts as +1.
 
 Packed record layout (the pages fix none; this is the library's layout):
-  codes[n][code_bytes]: little-endian bit stream, code i in bits
-  [i*w, (i+1)*w), LSB first; signs[n][sign_bytes]: bit j = (byte j>>3, bit
-  j&7), 1 <=> +1; norms[n], rnorms[n] float32.  Record byte counts are rounded
-  up to a multiple of 16 and the padding is zero.  A zero vector encodes as
-  all-zero codes and signs with norm 0 and residual norm 0.
+  codes[n][code_bytes]: prod mode (keys): little-endian bit stream, code i in
+  bits [i*w, (i+1)*w), LSB first; MSE-only mode (values): w bit planes of d
+  bits each, plane p in bytes [p d/8, (p+1) d/8) holding bit p of code i at
+  bit i of the plane (d is a multiple of 8); signs[n][sign_bytes]: bit j =
+  (byte j>>3, bit j&7), 1 <=> +1; norms[n], rnorms[n] float32.  Record byte
+  counts are rounded up to a multiple of 16 and the padding is zero.  A zero
+  vector encodes as all-zero codes and signs with norm 0 and residual norm 0.
 """
 
 import numpy as np
@@ -52,6 +54,41 @@ def unpack_bits(packed, width, k):
     bits = np.unpackbits(packed, axis=1, bitorder="little")[:, : k * width]
     bits = bits.reshape(packed.shape[0], k, width).astype(np.int64)
     return (bits << np.arange(width, dtype=np.int64)).sum(axis=2)
+
+
+def pack_planes(values, width, d, nbytes):
+    """Bit planes of rows ``values[n, d]``: plane p (bit p of every value) as d
+    bits, value i at bit i, planes one after another; ``nbytes`` per row."""
+    values = np.asarray(values, dtype=np.int64)
+    n = values.shape[0]
+    out = np.zeros((n, nbytes * 8), dtype=np.uint8)
+    for plane in range(width):
+        out[:, plane * d:(plane + 1) * d] = (values >> plane) & 1
+    return np.packbits(out, axis=1, bitorder="little")
+
+
+def unpack_planes(packed, width, d):
+    """Inverse of :func:`pack_planes`: [n, d] values of ``width`` bits."""
+    bits = np.unpackbits(np.asarray(packed, dtype=np.uint8), axis=1, bitorder="little").astype(np.int64)
+    out = np.zeros((bits.shape[0], d), dtype=np.int64)
+    for plane in range(width):
+        out |= bits[:, plane * d:(plane + 1) * d] << plane
+    return out
+
+
+def pack_codes(p, idx):
+    """Code records of a context: bit stream (prod) or bit planes (MSE-only)."""
+    cb = record_sizes(p.d, p.w, p.m)[0]
+    if p.mode == "mse":
+        return pack_planes(idx, p.w, p.d, cb)
+    return pack_bits(idx, p.w, cb)
+
+
+def unpack_codes(p, codes):
+    """Code indices [n, d] from a context's code records."""
+    if p.mode == "mse":
+        return unpack_planes(codes, p.w, p.d)
+    return unpack_bits(codes, p.w, p.d)
 
 
 def quantize_one(p, x):
@@ -117,7 +154,7 @@ def quantize(p, X, chunk=65536, return_unpacked=False):
         y = u @ p.Pi.T
         idx = np.searchsorted(p.t, y, side="left")   # = #{k : t_k < y}
         idx[zero] = 0
-        codes[s:s + chunk] = pack_bits(idx, p.w, cb)
+        codes[s:s + chunk] = pack_codes(p, idx)
         norms[s:s + chunk] = nu.astype(np.float32)
         if p.mode == "prod":
             r = y - p.c[idx]
@@ -149,7 +186,7 @@ def dequant(p, codes, signs, norms, rnorms):
     mse:  x_hat = nu Pi^T c[idx]
     (suzuke blog, "第三步": approximation plus residual correction).
     """
-    idx = unpack_bits(codes, p.w, p.d)
+    idx = unpack_codes(p, codes)
     nu = np.asarray(norms, np.float64)[:, None]
     xhat = p.c[idx] @ p.Pi
     if p.mode == "prod":

@@ -40,7 +40,7 @@ def check_quantized(p, gpu, ref, X=None, allow_frac=MAX_FRAC):
     sign bits and gamma are then checked against the oracle's stage-2 result
     for the other valid code choice (needs the input rows ``X``).
     """
-    g_idx = O.unpack_bits(gpu["codes"], p.w, p.d)
+    g_idx = O.unpack_codes(p, gpu["codes"])
     r_idx = ref["idx"]
     assert np.array_equal(gpu["codes"].shape, ref["codes"].shape)
     # norms: within one float32 ulp of the float64 length

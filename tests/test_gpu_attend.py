@@ -29,6 +29,12 @@ def _dev(rec, keys):
 @pytest.mark.parametrize("d,kbits,vbits,G,qpg,T", [
     (128, 3, 3, 3, 4, 1000), (128, 3, 3, 1, 4, 512), (128, 3, 3, 2, 4, 513), (128, 2, 4, 2, 2, 777),
     (128, 4, 2, 1, 5, 300), (64, 3, 3, 2, 4, 1200), (128, 3, 3, 1, 4, 1), (96, 3, 1, 1, 8, 700),
+    # every value width of the fused kernel at d = 128 and 64, and key widths at d = 64
+    (128, 2, 1, 1, 4, 2000), (64, 4, 4, 2, 4, 700), (64, 2, 2, 1, 3, 1025), (64, 3, 1, 1, 4, 90),
+    # several chunks per block (the value-record slots are refilled while a chunk is scored)
+    (128, 3, 3, 64, 4, 8192), (128, 3, 4, 128, 4, 4096), (64, 3, 2, 64, 4, 8192),
+    # lengths the fused kernel does not take (three steps)
+    (32, 3, 3, 2, 4, 600),
 ])
 def test_attend_matches_oracle(tq, d, kbits, vbits, G, qpg, T):
     pk = O.make_params(d, kbits, 0)

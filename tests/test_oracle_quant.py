@@ -59,6 +59,48 @@ def test_pack_unpack_roundtrip():
         assert np.array_equal(O.unpack_bits(O.pack_bits(v, w, cb), w, d), v)
 
 
+def test_pack_planes_hand_example():
+    # d = 16 at 3 bits: codes 5 (101), 2 (010), 7 (111), 0 at coordinates 0..3
+    # and 6 (110) at coordinate 15.  Plane p holds bit p of code i at bit i:
+    # plane 0 = 1,0,1,0,...,0 -> bytes 0x05 0x00; plane 1 = 0,1,1,0,...,1 ->
+    # 0x06 0x80; plane 2 = 1,0,1,0,...,1 -> 0x05 0x80
+    v = np.zeros((1, 16), np.int64)
+    v[0, :4] = [5, 2, 7, 0]
+    v[0, 15] = 6
+    packed = O.pack_planes(v, 3, 16, 16)
+    assert packed[0].tolist() == [0x05, 0x00, 0x06, 0x80, 0x05, 0x80] + [0] * 10
+    assert np.array_equal(O.unpack_planes(packed, 3, 16), v)
+
+
+def test_planes_are_the_stream_transposed():
+    # bit p of code i: stream bit i w + p, plane bit p d + i
+    rng = np.random.default_rng(1)
+    for w, d in [(1, 24), (2, 64), (3, 128), (4, 40)]:
+        v = rng.integers(0, 2 ** w, (20, d))
+        cb, _ = O.record_sizes(d, w, 0)
+        st = np.unpackbits(O.pack_bits(v, w, cb), axis=1, bitorder="little")
+        pl = np.unpackbits(O.pack_planes(v, w, d, cb), axis=1, bitorder="little")
+        assert pl.shape == st.shape
+        for p in range(w):
+            assert np.array_equal(pl[:, p * d:(p + 1) * d], st[:, p:w * d:w])
+        assert not pl[:, w * d:].any()
+        assert np.array_equal(O.unpack_planes(O.pack_planes(v, w, d, cb), w, d), v)
+
+
+def test_records_by_mode():
+    # prod records (keys) keep the bit stream, MSE-only records (values) the planes
+    X = np.random.default_rng(2).standard_normal((30, 64))
+    for mode, packer in (("prod", lambda p, i: O.pack_bits(i, p.w, O.record_sizes(p.d, p.w, p.m)[0])),
+                         ("mse", lambda p, i: O.pack_planes(i, p.w, p.d, O.record_sizes(p.d, p.w, p.m)[0]))):
+        p = O.make_params(64, 3, 5, mode)
+        r = O.quantize(p, X, return_unpacked=True)
+        assert np.array_equal(r["codes"], packer(p, r["idx"]))
+        assert np.array_equal(O.unpack_codes(p, r["codes"]), r["idx"])
+        xh = O.dequant(p, r["codes"], r["signs"], r["norms"], r["rnorms"])
+        assert np.allclose(xh[:, :], (p.c[r["idx"]] @ p.Pi) * r["norms"][:, None].astype(np.float64)
+                           + (0 if mode == "mse" else xh - (p.c[r["idx"]] @ p.Pi) * r["norms"][:, None]))
+
+
 def test_record_sizes():
     assert O.record_sizes(128, 2, 128) == (32, 16)
     assert O.record_sizes(128, 1, 128) == (16, 16)
