@@ -233,7 +233,6 @@ attend_partial_kernel(AttArgs a) {
   issue(c_begin);
   stage_values(c_begin, 0);
   for (int c = c_begin; c < c_end; ++c) {
-    const int64_t tbeg = (int64_t)c * CH;
     const int slot = DB ? (c - c_begin) & 1 : 0;
     // ---- A: logits of the wave's tokens into LDS
     float lg[2][4];
@@ -249,19 +248,21 @@ attend_partial_kernel(AttArgs a) {
         lg[tt][s] = tile_logit<CB16, SB16, W>(A, kw[tt][s], nu, ga, a.alpha, hc, pm);
         __asm__ volatile("" : "+v"(lg[tt][s]));
       }
+    // (token indexes fit in 32 bits: the host limits T to 2^31 - CH)
+    const int Ti = (int)T, tb32 = c * CH;
     float mz = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int64_t t = tbeg + (wv + 4 * tt) * 64 + 16 * s + col;
-        const float z = t < T ? a.scale * lg[tt][s] : -INFINITY;
+        const int t = tb32 + (wv + 4 * tt) * 64 + 16 * s + col;
+        const float z = t < Ti ? a.scale * lg[tt][s] : -INFINITY;
         L.zt[tt * 64 + 16 * s + col][grp] = z;
         mz = fmaxf(mz, z);
-        if (a.logits && head < a.qpg && t < T) a.logits[(kg * a.qpg + head) * T + t] = lg[tt][s];
+        if (a.logits && head < a.qpg && t < Ti) a.logits[(kg * a.qpg + head) * T + t] = lg[tt][s];
       }
     const float vnl0 = vn[0], vnl1 = vn[1];
-    const bool v0 = tbeg + wv * 64 + lane < T, v1 = tbeg + (wv + 4) * 64 + lane < T;
+    const bool v0 = tb32 + wv * 64 + lane < Ti, v1 = tb32 + (wv + 4) * 64 + lane < Ti;
     if (c + 1 < c_end) {
       issue(c + 1);
       if constexpr (DB) stage_values(c + 1, slot ^ 1);
@@ -283,8 +284,10 @@ attend_partial_kernel(AttArgs a) {
     // weights w = exp(z - M) nu <= numax, in units of numax / 127: u = w S,
     // S = 127 / numax, so u <= 127; the A operand carries the four base-128
     // digits of U = u 2^21, an integer below 2^28
+    // (S from the hardware reciprocal, 2^-20 below 127 / numax so that u stays
+    // below 127 whatever its rounding; S only has to be that bound)
     const float numax = wave_max(fmaxf(v0 ? vnl0 : 0.f, v1 ? vnl1 : 0.f));
-    const float S = numax > 0.f ? 127.f / numax : 1.f;
+    const float S = numax > 0.f ? (127.f * (1.f - 0x1.0p-20f)) * __builtin_amdgcn_rcpf(numax) : 1.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t = tt * 64 + lane;
@@ -305,7 +308,7 @@ attend_partial_kernel(AttArgs a) {
     // ---- C: the value sum of the wave's 128 tokens on int8 MFMA
     {
       const float fg = grp == 0 ? f[0] : grp == 1 ? f[1] : grp == 2 ? f[2] : f[3];
-      const float invS = 1.f / S;
+      const float invS = __builtin_amdgcn_rcpf(S);
       i32x4 Aw[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -509,11 +512,24 @@ __global__ void __launch_bounds__(CT) attend_combine_kernel(CombArgs a) {
     y[tid] = s / L;
   }
   __syncthreads();
-  for (int jx = tid; jx < d; jx += CT) {      // out = Pi_v^T y
+  // out = Pi_v^T y: thread (row lane ri, column jx) sums rows ri, ri + nr, ...
+  // (short chains of coalesced row reads; d <= TQ_MAX_D = CT), then the row
+  // lanes are added
+  {
+    const int nr = CT / d;
+    const int ri = tid / d, jx = tid - ri * d;
     float o = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < d; ++r) o = fmaf(a.Piv[(int64_t)r * d + jx], y[r], o);
-    a.out[gq * d + jx] = o;
+    if (ri < nr) {
+#pragma unroll 4
+      for (int r = ri; r < d; r += nr) o = fmaf(a.Piv[(int64_t)r * d + jx], y[r], o);
+    }
+    if (ri < nr) part_acc[tid] = o;             // (its last reads were before the barrier above)
+    __syncthreads();
+    if (tid < d) {
+      float sum = 0.f;
+      for (int k = 0; k < nr; ++k) sum += part_acc[k * d + tid];
+      a.out[gq * d + tid] = sum;
+    }
   }
   if (a.mstat && tid == 0) {
     a.mstat[2 * gq] = M;
