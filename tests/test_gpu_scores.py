@@ -87,7 +87,7 @@ def test_scores_random_records(tq, d, bits, G, qpg, T, ldk):
     # b = 2, 3, 4, d = 64 and 128, with a partial last head group
     (128, 3, 2, 2048, 100, 100), (64, 2, 4, 1024, 70, 70), (128, 4, 1, 4096, 40, 40),
     (128, 3, 1, 4099, 33, 33),
-    # d + m > 256: the prep GEMM takes 32 queries per block
+    # d > 128: the projection GEMM runs 8-wave blocks (twice the A fragments per wave)
     (200, 2, 1, 4100, 50, 50), (256, 4, 2, 2048, 40, 40), (96, 3, 3, 1366, 30, 31),
 ])
 def test_scores_many_queries_per_group(tq, d, bits, G, qpg, T, ldk):
@@ -99,6 +99,26 @@ def test_scores_many_queries_per_group(tq, d, bits, G, qpg, T, ldk):
     print(f"scores many queries d={d} b={bits} G={G} qpg={qpg} T={T} ldk={ldk}", flush=True)
     got = _score(tq, ctx, Q, rec, G, T, ldk)
     assert_close(got, _oracle_grouped(p, Q, rec, G, T, ldk), what="logits")
+
+
+@pytest.mark.parametrize("d", [128, 200])
+def test_scores_many_queries_unaligned_queries(tq, d):
+    # queries 4 bytes past a 16-byte boundary: the projection GEMM's query
+    # loads take the one-float path (4096 head groups)
+    G, qpg, T = 1024, 16, 40
+    ctx = tq.Context(d, 3, 0)
+    p = O.make_params(d, 3, 0)
+    codes, signs, norms, rnorms = wl.random_records(G * T, ctx.code_bytes, ctx.sign_bytes, seed=d)
+    rec = {"codes": codes, "signs": signs, "norms": norms, "rnorms": rnorms}
+    Q = wl.gaussian((G, qpg, d), 27)
+    buf = torch.zeros(G * qpg * d + 1, dtype=torch.float32, device="cuda")
+    q = buf[1:].view(G, qpg, d)
+    q.copy_(torch.from_numpy(np.ascontiguousarray(Q, dtype=np.float32)))
+    assert q.data_ptr() % 16 == 4
+    print(f"scores many queries, unaligned q: d={d} G={G} qpg={qpg}", flush=True)
+    got = tq.tq_scores(ctx, q, _dev(rec), T=T, ldk=T)
+    torch.cuda.synchronize()
+    assert_close(got.cpu().numpy(), _oracle_grouped(p, Q, rec, G, T, T), what="logits")
 
 
 def test_scores_query_count_limits(tq):
