@@ -145,23 +145,51 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
 
 constexpr int FRAG_PAD = 16;
 
+// Wave-wide sum (a float) and maximum (of non-negative floats, compared as
+// integers) with DPP alone: row reductions, then row_bcast:15 / :31 carry
+// rows 0-2 into row 3, whose lane 63 ends with the result.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_rows(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ float wave_sum63(float v) {
+  v = row_sum(v);
+  v += __builtin_bit_cast(float, dpp_rows<0x142, 0xa>(__builtin_bit_cast(int, v)));   // row_bcast:15
+  v += __builtin_bit_cast(float, dpp_rows<0x143, 0xc>(__builtin_bit_cast(int, v)));   // row_bcast:31
+  return lane_f(v, 63);
+}
+__device__ __forceinline__ float wave_max63_nonneg(float v) {
+  unsigned u = __float_as_uint(v);
+  u = max(u, (unsigned)dpp_rows<0xb1, 0xf>((int)u));    // quad_perm [1,0,3,2]
+  u = max(u, (unsigned)dpp_rows<0x4e, 0xf>((int)u));    // quad_perm [2,3,0,1]
+  u = max(u, (unsigned)dpp_rows<0x141, 0xf>((int)u));   // row_half_mirror
+  u = max(u, (unsigned)dpp_rows<0x140, 0xf>((int)u));   // row_mirror
+  u = max(u, (unsigned)dpp_rows<0x142, 0xa>((int)u));   // row_bcast:15
+  u = max(u, (unsigned)dpp_rows<0x143, 0xc>((int)u));   // row_bcast:31
+  return __uint_as_float((unsigned)__builtin_amdgcn_readlane((int)u, 63));
+}
+
 // W (code bits) is a template parameter: the bit position -> coordinate
 // arithmetic of every coefficient then folds to shifts and constants, with
 // only the lane's group g and byte t left at run time.
 template <int W>
 __global__ void __launch_bounds__(256) prep_frag_kernel(PrepGemmArgs a) {
-  // per wave: 4 heads x (d + m) projections, each head's row padded by
-  // FRAG_PAD floats (spreads the LDS banks); sized at launch
+  // per wave: 4 heads x one row each: the dP rotated coordinates any code
+  // bit of the record words can name (zero past d), then the mP sketch rows
+  // (zero past m), then FRAG_PAD floats (spreads the LDS banks); sized at launch
   extern __shared__ float prs[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t gx = (int64_t)blockIdx.x * 4 + wv;
   if (gx >= a.groups) return;                       // no block-wide synchronisation below
-  const int d = a.d, m = a.m, dm = d + m, ps = dm + FRAG_PAD;
+  const int cwpl = a.cb16, swpl = a.sb16;
+  const int d = a.d, m = a.m, dm = d + m;
+  const int dP = (128 * cwpl + W - 1) / W, mP = 128 * swpl, ps = dP + mP + FRAG_PAD;
   float *pr = prs + wv * 4 * ps;
   uint8_t *out = a.ws + gx * prep_stride(a.nm);
   const float4 *proj = reinterpret_cast<const float4 *>(out);   // [column][head]
-  for (int c = lane; c < dm; c += 64) {
-    const float4 v = proj[c];
+  for (int c = lane; c < dP + mP; c += 64) {
+    const int src = c < dP ? (c < d ? c : -1) : (c - dP < m ? d + c - dP : -1);
+    const float4 v = src >= 0 ? proj[src] : make_float4(0.f, 0.f, 0.f, 0.f);
     pr[c] = v.x;
     pr[ps + c] = v.y;
     pr[2 * ps + c] = v.z;
@@ -182,40 +210,42 @@ __global__ void __launch_bounds__(256) prep_frag_kernel(PrepGemmArgs a) {
   // per head: sums of the projections; largest |coefficient| 2^-j over the
   // code (and parity) bits and over the sign bits (j = the bit's place in its byte)
   float sP[4] = {0.f, 0.f, 0.f, 0.f}, sQ[4] = {0.f, 0.f, 0.f, 0.f};
-  float mP[4] = {0.f, 0.f, 0.f, 0.f}, mQ[4] = {0.f, 0.f, 0.f, 0.f};
+  float mP4[4] = {0.f, 0.f, 0.f, 0.f}, mQ4[4] = {0.f, 0.f, 0.f, 0.f};
   for (int i = lane; i < d; i += 64) {
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
       const float v = pr[hh * ps + i], av = fabsf(v);
       sP[hh] += v;
 #pragma unroll
-      for (int p = 0; p < W; ++p) mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(cb2[p]) * av, -((i * W + p) & 7)));
-      if constexpr (W == 3) mP[hh] = fmaxf(mP[hh], ldexpf(fabsf(cb2[3]) * av, -((3 * i) & 7)));
+      for (int p = 0; p < W; ++p) mP4[hh] = fmaxf(mP4[hh], ldexpf(fabsf(cb2[p]) * av, -((i * W + p) & 7)));
+      if constexpr (W == 3) mP4[hh] = fmaxf(mP4[hh], ldexpf(fabsf(cb2[3]) * av, -((3 * i) & 7)));
     }
   }
   for (int jj = lane; jj < m; jj += 64) {
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
-      const float v = pr[hh * ps + d + jj];
+      const float v = pr[hh * ps + dP + jj];
       sQ[hh] += v;
-      mQ[hh] = fmaxf(mQ[hh], ldexpf(2.f * fabsf(v), -(jj & 7)));
+      mQ4[hh] = fmaxf(mQ4[hh], ldexpf(2.f * fabsf(v), -(jj & 7)));
     }
   }
 #pragma unroll
   for (int hh = 0; hh < 4; ++hh) {
-    sP[hh] = wave_sum(sP[hh]);
-    sQ[hh] = wave_sum(sQ[hh]);
-    mP[hh] = wave_max(mP[hh]);
-    mQ[hh] = wave_max(mQ[hh]);
+    sP[hh] = wave_sum63(sP[hh]);
+    sQ[hh] = wave_sum63(sQ[hh]);
+    mP4[hh] = wave_max63_nonneg(mP4[hh]);
+    mQ4[hh] = wave_max63_nonneg(mQ4[hh]);
   }
   // lane: fragment row r = 4 head + t of lane group g; it computes the
   // coefficients of byte t of its four dwords
   const int r = lane & 15, g = lane >> 4, hr = r >> 2, t = r & 3;
-  const float mx0 = hr == 0 ? mP[0] : hr == 1 ? mP[1] : hr == 2 ? mP[2] : mP[3];
-  const float mx1 = hr == 0 ? mQ[0] : hr == 1 ? mQ[1] : hr == 2 ? mQ[2] : mQ[3];
-  const float sc0 = mx0 > 0.f ? 127.f / mx0 : 1.f, sc1 = mx1 > 0.f ? 127.f / mx1 : 1.f;
-  const float *qr = pr + hr * ps, *qs = qr + d;
-  const int cwpl = a.cb16, swpl = a.sb16;
+  const float mx0 = hr == 0 ? mP4[0] : hr == 1 ? mP4[1] : hr == 2 ? mP4[2] : mP4[3];
+  const float mx1 = hr == 0 ? mQ4[0] : hr == 1 ? mQ4[1] : hr == 2 ? mQ4[2] : mQ4[3];
+  // scales 127 / max from the hardware reciprocal (1 ulp: |U| stays below
+  // 127.5 2^21, so the top digit stays within int8)
+  const float sc0 = mx0 > 0.f ? 127.f * __builtin_amdgcn_rcpf(mx0) : 1.f;
+  const float sc1 = mx1 > 0.f ? 127.f * __builtin_amdgcn_rcpf(mx1) : 1.f;
+  const float *qr = pr + hr * ps, *qs = qr + dP;
   const int nmc = 2 * cwpl, nmp = 2 * parity_words(cwpl, W);
   // byte selector: byte t of the low operand, byte t of the high operand
   const uint32_t psel = (uint32_t)t | ((uint32_t)(4 + t) << 8) | 0x0c0c0000u;
@@ -231,19 +261,18 @@ __global__ void __launch_bounds__(256) prep_frag_kernel(PrepGemmArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int j = 4 * half + e, q = 8 * t + j;
       float v = 0.f;
+      // (the rows are zero past d and m, so no range checks)
       if (kind == 2) {
         const int bitpos = 32 * (g * wpl + pair) + q;
-        if (bitpos < m) v = 2.f * qs[bitpos];
+        v = 2.f * qs[bitpos];
       } else if (kind == 0) {
-        if (pair < wpl) {
-          const int bitpos = 32 * (g * wpl + pair) + q;
-          // bitpos / W: a shift, or (W = 3) exact below 2^15 by multiply
-          const int i = W == 1 ? bitpos : W == 2 ? bitpos >> 1 : (bitpos * 43691) >> 17;
-          // the code bit's plane: j's parity for W = 2 (32 (...) + 8 t is even)
-          const float cf = W == 1 ? cb2[0] : W == 2 ? ((e & 1) ? cb2[1] : cb2[0])
-                                         : (bitpos - 3 * i == 0 ? cb2[0] : bitpos - 3 * i == 1 ? cb2[1] : cb2[2]);
-          if (i < d) v = cf * qr[i];
-        }
+        const int bitpos = 32 * (g * wpl + pair) + q;
+        // bitpos / W: a shift, or (W = 3) exact below 2^15 by multiply
+        const int i = W == 1 ? bitpos : W == 2 ? bitpos >> 1 : (bitpos * 43691) >> 17;
+        // the code bit's plane: j's parity for W = 2 (32 (...) + 8 t is even)
+        const float cf = W == 1 ? cb2[0] : W == 2 ? ((e & 1) ? cb2[1] : cb2[0])
+                                       : (bitpos - 3 * i == 0 ? cb2[0] : bitpos - 3 * i == 1 ? cb2[1] : cb2[2]);
+        v = cf * qr[i];
       } else if constexpr (W == 3) {
         // merged parity word `pair`: bit q belongs to the code starting at bit
         // q of record word g*wpl + p, p = 3 pair + ((q - g*wpl) mod 3)
@@ -251,7 +280,7 @@ __global__ void __launch_bounds__(256) prep_frag_kernel(PrepGemmArgs a) {
         if (p < wpl) {
           const int bitpos = 32 * (g * wpl + p) + q;
           const int i = (bitpos * 43691) >> 17;
-          if (bitpos - 3 * i == 0 && i < d) v = cb2[3] * qr[i];
+          if (bitpos - 3 * i == 0) v = cb2[3] * qr[i];
         }
       }
       // U = u 2^21 rounded, u = v S 2^-j (negated for j = 7: the B byte value
@@ -282,14 +311,14 @@ __global__ void __launch_bounds__(256) prep_frag_kernel(PrepGemmArgs a) {
     *reinterpret_cast<uint4 *>(out + ((int64_t)mu * 64 + lane) * 16) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
   }
   if (lane < 4) {
-    const float xp = lane == 0 ? mP[0] : lane == 1 ? mP[1] : lane == 2 ? mP[2] : mP[3];
-    const float xq = lane == 0 ? mQ[0] : lane == 1 ? mQ[1] : lane == 2 ? mQ[2] : mQ[3];
+    const float xp = lane == 0 ? mP4[0] : lane == 1 ? mP4[1] : lane == 2 ? mP4[2] : mP4[3];
+    const float xq = lane == 0 ? mQ4[0] : lane == 1 ? mQ4[1] : lane == 2 ? mQ4[2] : mQ4[3];
     const float s0 = lane == 0 ? sP[0] : lane == 1 ? sP[1] : lane == 2 ? sP[2] : sP[3];
     const float s1 = lane == 0 ? sQ[0] : lane == 1 ? sQ[1] : lane == 2 ? sQ[2] : sQ[3];
     const float bsum = a.basis[0] + (W >= 2 ? a.basis[1] : 0.f) + (W >= 3 ? a.basis[2] + a.basis[3] : 0.f);
     float *cst = reinterpret_cast<float *>(out + (int64_t)a.nm * 1024);
-    cst[lane * 4 + 0] = xp > 0.f ? 1.f / (127.f / xp) : 1.f;
-    cst[lane * 4 + 1] = xq > 0.f ? 1.f / (127.f / xq) : 1.f;
+    cst[lane * 4 + 0] = xp > 0.f ? xp * (1.f / 127.f) : 1.f;   // 1 / S, as the scales above
+    cst[lane * 4 + 1] = xq > 0.f ? xq * (1.f / 127.f) : 1.f;
     cst[lane * 4 + 2] = bsum * s0;
     cst[lane * 4 + 3] = s1;
   }
@@ -334,7 +363,9 @@ int launch_prep_gemm(const tq_ctx *ctx, const float *q, int64_t groups, int qpg,
   else
     return TQ_ENOTSUP;
   if (hip_status() != TQ_OK) return TQ_EHIP;
-  const size_t flds = sizeof(float) * 4 * 4 * (size_t)(a.d + a.m + FRAG_PAD);   // <= 33 KB
+  // (one row per head and wave: dP + mP <= 256 + 256 floats at d <= 256)
+  const size_t flds = sizeof(float) * 4 * 4 *
+                      (size_t)((128 * a.cb16 + a.w - 1) / a.w + 128 * a.sb16 + FRAG_PAD);   // <= 33 KB
   if (a.w == 1)
     prep_frag_kernel<1><<<(unsigned)fblocks, 256, flds, stream>>>(a);
   else if (a.w == 2)
