@@ -232,6 +232,11 @@ attend_partial_kernel(AttArgs a) {
 
   issue(c_begin);
   stage_values(c_begin, 0);
+  // every load of a chunk (key words, norms, the next chunk's value copies)
+  // lands before the chunk is processed: an explicit wait here and at the
+  // end of each iteration (the compiler does not order the LDS copies before
+  // the slot's reads)
+  wait_vm<0>();
   for (int c = c_begin; c < c_end; ++c) {
     const int slot = DB ? (c - c_begin) & 1 : 0;
     // ---- A: logits of the wave's tokens into LDS
@@ -401,6 +406,7 @@ attend_partial_kernel(AttArgs a) {
     if constexpr (!DB) {
       if (c + 1 < c_end) stage_values(c + 1, 0);
     }
+    wait_vm<0>();
   }
   wave_sync();            // the slots' last reads are done: vacc reuses them
 #pragma unroll

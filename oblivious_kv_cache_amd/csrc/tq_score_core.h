@@ -215,6 +215,17 @@ __device__ __forceinline__ float tile_logit(const i32x4 *A, const KeyWords<CB16,
   return l;
 }
 
+// s_waitcnt vmcnt(N): at most N vector memory instructions of this wave still
+// outstanding (loads complete in issue order, so every load issued more than
+// N loads ago has landed).  The copies into LDS (global_load_lds) are waited
+// for this way, explicitly: the compiler does not order them before later
+// LDS reads of the same slot.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Wave-wide sum / max with DPP row permutes (quad swaps, half-row and row
 // mirrors make every lane of a 16-lane row hold the row result) and four
 // readlanes; much shorter latency than a chain of ds_bpermute shuffles.

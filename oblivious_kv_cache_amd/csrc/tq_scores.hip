@@ -70,8 +70,17 @@ constexpr int kScoresSPB = 4;
 // FRAC: fractional-width records (24 to 80 code bytes, the two halves' bit
 // planes by quarter); the tile copies into LDS end with a partial 1 KB
 // instruction where the tile's bytes are not a multiple of 1 KB.
+// LATE (3-bit codes, one head group): a tile's words are read from its LDS
+// slot subtile by subtile while it is scored, and the slot is refilled
+// afterwards; without the words of four subtiles held in registers the
+// kernel fits four waves per SIMD.
+template <int CB16, int SB16, int W, int NQ, bool FRAC>
+__host__ __device__ constexpr bool scores_late_refill() { return W == 3 && NQ == 1 && !FRAC; }
+
 template <int CB16, int SB16, int W, int NQ, bool FRAC = false>
-__global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(scores_late_refill<CB16, SB16, W, NQ, FRAC>() ? 4 : 1)))
+scores_kernel(ScoreArgs a) {
   constexpr int NM = ScoreShape<CB16, SB16, W>::NM;
   constexpr int SPB = kScoresSPB, KT = 16 * SPB;
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
@@ -248,6 +257,42 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
       }
     }
   };
+  // LATE: the words of subtile s of a slot, read right before it is scored
+  auto score_dma_slot = [&](uint8_t (&kb)[4][TB], float nub, float gab, int t0) {
+#pragma unroll
+    for (int s = 0; s < SPB; ++s) {
+      KeyWords<CB16, SB16, W> kw1;
+      const int k = 16 * s + col;
+      const uint8_t *rc = kb[wv] + k * CBY + grp * (CB16 * 4);
+      const uint8_t *rsg = kb[wv] + KT * CBY + k * SBY + grp * (SB16 * 4);
+#pragma unroll
+      for (int i = 0; i < CB16; ++i) kw1.cw[i] = *reinterpret_cast<const uint32_t *>(rc + 4 * i);
+      if constexpr (W == 3) {
+        const uint32_t nxt = *reinterpret_cast<const uint32_t *>(rc + 4 * CB16);
+        kw1.cw[CB16] = grp < 3 ? nxt : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < SB16; ++i) kw1.sw[i] = *reinterpret_cast<const uint32_t *>(rsg + 4 * i);
+      const float nu = __shfl(nub, 16 * s + col), ga = __shfl(gab, 16 * s + col);
+      float l[NQ];
+      tile_logits<CB16, SB16, W, NQ, FRAC>(A, kw1, nu, ga, a.alpha, hc, pm, l);
+#pragma unroll
+      for (int g = 0; g < NQ; ++g) lt[wv][g][grp][16 * s + col] = l[g];
+    }
+#pragma unroll
+    for (int g = 0; g < NQ; ++g) {
+      const fvec v = *reinterpret_cast<const fvec *>(&lt[wv][g][grp][SPB * col]);
+      float *dst = lrow[g] + (uint32_t)(t0 + SPB * col);
+      if (head_ok[g]) {
+        if (a.wide) {
+          *reinterpret_cast<fvec *>(dst) = v;
+        } else {
+#pragma unroll
+          for (int i = 0; i < SPB; ++i) dst[i] = v[i];
+        }
+      }
+    }
+  };
   if (ntile <= 0) return;
   // first key of this wave's i-th tile
   auto key0 = [&](int i) { return (tile0 + i) * KT; };
@@ -261,13 +306,37 @@ __global__ void __launch_bounds__(256) scores_kernel(ScoreArgs a) {
   KeyWords<CB16, SB16, W> kw[SPB];
   if (nfull > 0) load_dma(kbA, nA, gA, key0(0));
   if (nfull > 1) load_dma(kbB, nB, gB, key0(1));
+  // Before a slot is read, its copy has landed: the only loads issued after
+  // it are the other slot's copy (NLD instructions) when that was issued.
+  constexpr int NLD = (KT * CBY + 1023) / 1024 + (KT * SBY + 1023) / 1024 + 2;
+  auto wait_slot = [](bool other_issued) {
+    if (other_issued)
+      wait_vm<NLD>();
+    else
+      wait_vm<0>();
+  };
+  if constexpr (scores_late_refill<CB16, SB16, W, NQ, FRAC>()) {
+    for (int it = 0; it < nfull; it += 2) {
+      wait_slot(it + 1 < nfull);                  // A(it) landed (B(it+1) was copied after it)
+      score_dma_slot(kbA, nA, gA, key0(it));
+      __builtin_amdgcn_s_waitcnt(0xc07f);         // lgkmcnt(0): the slot's reads are done
+      if (it + 2 < nfull) load_dma(kbA, nA, gA, key0(it + 2));
+      if (it + 1 >= nfull) break;
+      wait_slot(it + 2 < nfull);                  // B(it+1) landed (A(it+2) was copied after it)
+      score_dma_slot(kbB, nB, gB, key0(it + 1));
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      if (it + 3 < nfull) load_dma(kbB, nB, gB, key0(it + 3));
+    }
+  } else
   for (int it = 0; it < nfull; it += 2) {
+    wait_slot(it + 1 < nfull);
     read_dma(kbA, kw);
     float nu = nA, ga = gA;
     __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): the slot's reads are done
     if (it + 2 < nfull) load_dma(kbA, nA, gA, key0(it + 2));
     score_dma(kw, nu, ga, key0(it));
     if (it + 1 >= nfull) break;
+    wait_slot(it + 2 < nfull);
     read_dma(kbB, kw);
     nu = nB;
     ga = gB;
