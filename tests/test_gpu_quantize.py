@@ -115,6 +115,41 @@ def test_quantize_dimensions(tq, d, bits, n):
     check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
 
 
+# MSE-only records hold bit planes of d bits: lengths whose planes end inside
+# a lane group's bytes, padded lengths, both input types, and the generic
+# kernel (d > 256)
+@pytest.mark.parametrize("d,bits,n,dtype", [(8, 3, 100, torch.float32), (40, 2, 97, torch.bfloat16),
+                                            (96, 4, 515, torch.float32), (200, 3, 333, torch.bfloat16),
+                                            (256, 2, 300, torch.float32), (136, 4, 129, torch.float32),
+                                            (64, 1, 257, torch.bfloat16), (520, 3, 70, torch.float32)])
+def test_quantize_mse_dimensions(tq, d, bits, n, dtype):
+    X = wl.power_law(n, d, seed=6, unit=True)
+    X[3] = 0.0
+    if dtype == torch.bfloat16:
+        X = wl.bf16_round(X)
+    print(f"quantize mse n={n} d={d} b={bits} {dtype}", flush=True)
+    ctx, g, xin = _run(tq, d, bits, X, mode="mse", seed=2, dtype=dtype)
+    p = O.make_params(d, bits, 2, "mse")
+    check_quantized(p, g, O.quantize(p, xin, return_unpacked=True), xin)
+    # the planes themselves: plane p of a record is bit p of its codes
+    idx = O.unpack_codes(p, g["codes"])
+    assert np.array_equal(O.pack_planes(idx, p.w, d, ctx.code_bytes), g["codes"])
+
+
+@pytest.mark.parametrize("d,bits", [(96, 3), (40, 4), (200, 2), (520, 3)])
+def test_dequant_mse_dimensions(tq, d, bits):
+    dev = torch.device("cuda")
+    p = O.make_params(d, bits, 4, "mse")
+    ref = O.quantize(p, wl.gaussian((150, d), 14, np.float64))
+    ctx = tq.Context(d, bits, 4, tq.TQ_MODE_MSE)
+    rec = {k: torch.from_numpy(np.ascontiguousarray(ref[k])).to(dev) for k in ("codes", "norms")}
+    print(f"dequant mse b={bits} d={d}", flush=True)
+    out = tq.tq_dequant(ctx, rec).cpu().numpy()
+    want = O.dequant(p, ref["codes"], None, ref["norms"], None)
+    scale = np.linalg.norm(want, axis=1, keepdims=True)
+    assert (np.abs(out - want) <= 1e-5 * scale + 1e-6).all()
+
+
 def test_quantize_zero_rows_ragged_and_strided(tq):
     dev = torch.device("cuda")
     d, bits = 128, 3
