@@ -274,11 +274,12 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
       for (int i = 0; i < CW; ++i) cw[t][i] = 0u;
     }
 
-    // GEMM 1, one 16-coordinate output tile at a time, each tile consumed at
-    // once by the codebook search (its accumulator is the only live state).
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      f32x4 acc[NTL];
+    // GEMM 1, one 16-coordinate output tile at a time, each tile consumed by
+    // the codebook search while the MFMAs of the next tile run: the search's
+    // VALU instructions are interleaved with those MFMAs (one MFMA, then a
+    // few VALU instructions), so the matrix cores and the VALU work at once
+    // within the wave.
+    auto gemm1 = [&](int u, f32x4 (&acc)[NTL]) {
 #pragma unroll
       for (int t = 0; t < NTL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -291,6 +292,15 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
           if constexpr (!BF16IN) acc[t] = mfma(ah, bxl[t][k], acc[t]);
         }
       }
+    };
+    constexpr int G1_MFMA = NK * NTL * (BF16IN ? 2 : 3);   // MFMAs per output tile
+    f32x4 accs[2][NTL];
+    gemm1(0, accs[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      f32x4 (&acc)[NTL] = accs[u & 1];
+      if (u + 1 < NT) gemm1(u + 1, accs[(u + 1) & 1]);
 #pragma unroll
       for (int t = 0; t < NTL; ++t) {
         float rr[4];
@@ -356,6 +366,15 @@ __device__ __forceinline__ void quantize_body(const QArgs &a, Frag *lds, int blo
                                                  __builtin_convertvector(f32x2{rr[jj] - h0, rr[jj + 1] - h1}, bf16x2));
           rh[t][li >> 3][(li & 7) >> 1] = hw;
           rl[t][li >> 3][(li & 7) >> 1] = lw;
+        }
+      }
+      if (u + 1 < NT) {
+        // the next tile's fragment reads first, then MFMA / VALU alternating
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NK, 0);    // DS reads
+#pragma unroll
+        for (int i = 0; i < G1_MFMA; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);       // VALU
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // keep fragment loads from piling up
