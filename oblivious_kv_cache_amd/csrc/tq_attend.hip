@@ -83,6 +83,27 @@ __device__ __forceinline__ i32x2 lds_tr8(const uint8_t *p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2 *)(p));
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (reads at or beyond
+// `bytes` return zero), and one non-temporal 32-bit read at byte offset
+// off + imm (imm an instruction constant).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t buf_word(__amdgpu_buffer_rsrc_t r, uint32_t off, int imm) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + (uint32_t)imm), 0, 2 /* nt */);
+}
+// Units I .. N-1 of 1 KB (16 bytes per lane) from byte offset vo + 1024 unit
+// into LDS at dst + 1024 unit, non-temporal (the instruction's constant
+// offset moves the source and the LDS destination alike).
+template <int I, int N>
+__device__ __forceinline__ void buf_copy_lds(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t vo) {
+  if constexpr (I < N) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, (int)vo, 0,
+                                             I * 1024, 2 /* nt */);
+    buf_copy_lds<I + 1, N>(r, dst, vo);
+  }
+}
+
 // One block = one query group x one split (a run of `cps` chunks of CH
 // tokens).  Wave wv owns the 64-token blocks wv and wv + 4 of every chunk and
 // everything computed from them: their logits, staged value records,
@@ -129,7 +150,10 @@ attend_partial_kernel(AttArgs a) {
   __shared__ __align__(16) WaveLds wl[NT / 64];
   __shared__ float fin[NT / 64][4][2];            // per wave and head: running max, sum of exp
 
-  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  // wave index as a scalar: the wave's LDS and token offsets are then
+  // scalar arithmetic
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   WaveLds &L = wl[wv];
   const int64_t gidx = blockIdx.y, kg = gidx / a.hg;
   const int hgi = (int)(gidx - kg * a.hg);
@@ -158,47 +182,52 @@ attend_partial_kernel(AttArgs a) {
   // norms of tokens lane and lane + 64
   KW kw[2][4];
   float knu[2], kga[2], vn[2];
+  // The group's records are read through buffer resources whose size is the
+  // T records of the group: reads past the cache end (the last, partial
+  // chunk) return zeros instead of faulting, so no token index is clamped;
+  // those tokens get logit -inf and weight 0.  Offsets are 32-bit (the host
+  // checks that a group's records span less than 4 GB): one lane offset per
+  // 64-token block, the subtile and word offsets immediate.
+  const uint32_t Tu = (uint32_t)T;
+  const __amdgpu_buffer_rsrc_t rkc = buf_rsrc(kcb, Tu * (CB16 * 16)), rks = buf_rsrc(ksb, Tu * (SB16 * 16));
+  const __amdgpu_buffer_rsrc_t rkn = buf_rsrc(knb, Tu * 4), rkr = buf_rsrc(krb, Tu * 4);
+  const __amdgpu_buffer_rsrc_t rvc = buf_rsrc(vcbp, Tu * VCB), rvn = buf_rsrc(vnb, Tu * 4);
+  // lane offsets within a 64-token block: key words of token col, lane
+  // group grp
+  const uint32_t kco = (uint32_t)col * (CB16 * 16) + (uint32_t)grp * (CB16 * 4);
+  const uint32_t kso = (uint32_t)col * (SB16 * 16) + (uint32_t)grp * (SB16 * 4);
   auto issue = [&](int c) {
-    // 32-bit offsets from the group's base pointers (the host checks that a
-    // group's records span less than 4 GB) keep the address math short
-    const int tlast = (int)T - 1;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int tb = c * CH + (wv + 4 * tt) * 64;   // first token of the block
+      const uint32_t tb = (uint32_t)(c * CH + (wv + 4 * tt) * 64);   // first token of the block
+      uint32_t co = tb * (CB16 * 16) + kco, so = tb * (SB16 * 16) + kso, no = (tb + (uint32_t)lane) * 4;
+      // (opaque, so that each load's offset is this value plus an immediate
+      // and not a register of its own derived across iterations)
+      __asm__ volatile("" : "+v"(co), "+v"(so), "+v"(no));
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t t = (uint32_t)min(tb + 16 * s + col, tlast);
-        const uint8_t *cp = kcb + (t * (CB16 * 16) + (uint32_t)grp * (CB16 * 4));
-        const uint8_t *sp = ksb + (t * (SB16 * 16) + (uint32_t)grp * (SB16 * 4));
 #pragma unroll
-        for (int i = 0; i < CB16; ++i) kw[tt][s].cw[i] = key_word<true>(reinterpret_cast<const uint32_t *>(cp + 4 * i));
+        for (int i = 0; i < CB16; ++i) kw[tt][s].cw[i] = buf_word(rkc, co, s * 16 * (CB16 * 16) + 4 * i);
 #pragma unroll
-        for (int i = 0; i < SB16; ++i) kw[tt][s].sw[i] = key_word<true>(reinterpret_cast<const uint32_t *>(sp + 4 * i));
+        for (int i = 0; i < SB16; ++i) kw[tt][s].sw[i] = buf_word(rks, so, s * 16 * (SB16 * 16) + 4 * i);
       }
-      const uint32_t tl = (uint32_t)min(tb + lane, tlast);
-      knu[tt] = load_f32(knb, tl);
-      kga[tt] = load_f32(krb, tl);
-      vn[tt] = vnb[tl];
+      knu[tt] = __uint_as_float(buf_word(rkn, no, 0));
+      kga[tt] = __uint_as_float(buf_word(rkr, no, 0));
+      vn[tt] = __uint_as_float(buf_word(rvn, no, 0));
     }
   };
   // the value records of the wave's two 64-token blocks of chunk c into its
   // LDS slot: each block is one contiguous run of 64 VCB bytes, moved as
-  // 16-byte units (units past the cache end repeat the last real one; their
-  // tokens get zero weight)
+  // 16-byte units by the memory system (units past the cache end arrive as
+  // zeros; their tokens get zero weight)
   auto stage_values = [&](int c, int slot) {
-    const int tlast = (int)T - 1;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int tb = c * CH + (wv + 4 * tt) * 64;
-      const int tbc = min(tb, tlast);              // a block past the cache end reads its last token
-      const uint32_t lim = (uint32_t)(min(64, (int)T - tbc) * NU16) - 1u;
-      const uint8_t *src = vcbp + (uint32_t)tbc * VCB;
+      const uint32_t tb = (uint32_t)(c * CH + (wv + 4 * tt) * 64);
+      uint32_t vo = tb * VCB + 16 * (uint32_t)lane;
+      __asm__ volatile("" : "+v"(vo));
       uint8_t *dst = L.vrec[slot] + tt * 64 * VCB;
-#pragma unroll
-      for (int i = 0; i < NU16; ++i)
-        __builtin_amdgcn_global_load_lds(src + 16 * min((uint32_t)(i * 64 + lane), lim),
-                                         (__attribute__((address_space(3))) void *)(dst + i * 1024), 16, 0,
-                                         2 /* nt */);
+      buf_copy_lds<0, NU16>(rvc, dst, vo);
     }
   };
 

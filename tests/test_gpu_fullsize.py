@@ -75,6 +75,10 @@ def test_decode_32k_sampled(tq, bits):
         got = L[grp][:, toks]
         keep = same[sl]
         assert_close(got[:, keep], want[:, keep], what=f"logits group {grp}")
+        # every sampled key, band cases included: the oracle scores the
+        # GPU's own records
+        want_g = O.scores(p, Q[grp], g["codes"][sl], g["signs"][sl], g["norms"][sl], g["rnorms"][sl])
+        assert_close(got, want_g, what=f"logits group {grp} (GPU records)")
     # every sampled key, band cases included: the sampled records are replaced
     # by the oracle's own and the whole cache is scored again in the same
     # launch configuration
@@ -176,6 +180,9 @@ def test_many_queries_2k_sampled(tq):
         keep = same[sl]
         assert_close(L[grp][qs][:, keep], want[:, keep], what=f"logits group {grp}")
         assert_close(L2[grp][qs], want, what=f"logits group {grp} (oracle records)")
+        want_g = O.scores(p, Q[grp][qs].astype(np.float64), g["codes"][sl], g["signs"][sl],
+                          g["norms"][sl], g["rnorms"][sl])
+        assert_close(L[grp][qs], want_g, what=f"logits group {grp} (GPU records)")
 
 
 def _oracle_topk_chunked(p, Q, rec, k, chunk=50000):
