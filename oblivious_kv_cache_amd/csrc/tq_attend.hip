@@ -83,27 +83,6 @@ __device__ __forceinline__ i32x2 lds_tr8(const uint8_t *p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2 *)(p));
 }
 
-// Raw buffer resource over `bytes` bytes from `base` (reads at or beyond
-// `bytes` return zero), and one non-temporal 32-bit read at byte offset
-// off + imm (imm an instruction constant).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint32_t buf_word(__amdgpu_buffer_rsrc_t r, uint32_t off, int imm) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + (uint32_t)imm), 0, 2 /* nt */);
-}
-// Units I .. N-1 of 1 KB (16 bytes per lane) from byte offset vo + 1024 unit
-// into LDS at dst + 1024 unit, non-temporal (the instruction's constant
-// offset moves the source and the LDS destination alike).
-template <int I, int N>
-__device__ __forceinline__ void buf_copy_lds(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t vo) {
-  if constexpr (I < N) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, (int)vo, 0,
-                                             I * 1024, 2 /* nt */);
-    buf_copy_lds<I + 1, N>(r, dst, vo);
-  }
-}
-
 // One block = one query group x one split (a run of `cps` chunks of CH
 // tokens).  Wave wv owns the 64-token blocks wv and wv + 4 of every chunk and
 // everything computed from them: their logits, staged value records,
