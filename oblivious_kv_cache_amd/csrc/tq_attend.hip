@@ -83,6 +83,30 @@ __device__ __forceinline__ i32x2 lds_tr8(const uint8_t *p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2 *)(p));
 }
 
+// Raw buffer resource over `bytes` bytes from `base`: reads at or beyond
+// `bytes` return zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// One non-temporal 32-bit read at byte offset off + imm (imm a constant,
+// which the instruction carries).
+__device__ __forceinline__ uint32_t buf_word(__amdgpu_buffer_rsrc_t r, uint32_t off, int imm) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + (uint32_t)imm), 0, 2 /* nt */);
+}
+// 1 KB units I .. N-1 (16 bytes per lane, lane offset included in vo) from
+// byte offset vo + 1024 I into LDS at dst + 1024 I, non-temporal.  The
+// instruction's constant offset moves the source and the LDS destination
+// alike; it stays below 4 KB, so every fourth unit advances both bases.
+template <int I, int N>
+__device__ __forceinline__ void buf_copy_lds(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t vo) {
+  if constexpr (I < N) {
+    constexpr int HI = (I >> 2) * 4096, LO = (I & 3) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + HI), 16,
+                                             (int)(vo + (uint32_t)HI), 0, LO, 2 /* nt */);
+    buf_copy_lds<I + 1, N>(r, dst, vo);
+  }
+}
+
 // One block = one query group x one split (a run of `cps` chunks of CH
 // tokens).  Wave wv owns the 64-token blocks wv and wv + 4 of every chunk and
 // everything computed from them: their logits, staged value records,
@@ -301,6 +325,12 @@ attend_partial_kernel(AttArgs a) {
     // below 127 whatever its rounding; S only has to be that bound)
     const float numax = wave_max(fmaxf(v0 ? vnl0 : 0.f, v1 ? vnl1 : 0.f));
     const float S = numax > 0.f ? (127.f * (1.f - 0x1.0p-20f)) * __builtin_amdgcn_rcpf(numax) : 1.f;
+    // the running max floored to a finite value: masked tokens (z = -inf)
+    // then get exp(-inf) = 0 also while none of the wave's tokens has been
+    // real (M = -inf), with no compare
+    float Mf[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) Mf[h] = fmaxf(M[h], -FLT_MAX);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t = tt * 64 + lane;
@@ -309,11 +339,11 @@ attend_partial_kernel(AttArgs a) {
       const float sc = (tt ? vnl1 : vnl0) * S * 0x1.0p21f;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        // 0 for masked tokens (z = -inf; M is -inf too while none of the
-        // wave's tokens has been real)
-        const float pz = zz[h] == -INFINITY ? 0.f : __expf(zz[h] - M[h]);
+        const float pz = __expf(zz[h] - Mf[h]);
         lsum[h] += pz;
-        L.ufix[h * UST + uidx(t)] = (uint32_t)rintf(pz * sc);
+        // rounded to the nearest integer (the sum stays below 2^28, and the
+        // conversion truncates)
+        L.ufix[h * UST + uidx(t)] = (uint32_t)fmaf(pz, sc, 0.5f);
       }
     }
     wave_sync();

@@ -215,30 +215,6 @@ __device__ __forceinline__ float tile_logit(const i32x4 *A, const KeyWords<CB16,
   return l;
 }
 
-// Raw buffer resource over `bytes` bytes from `base`: reads at or beyond
-// `bytes` return zero instead of faulting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-// One non-temporal 32-bit read at byte offset off + imm (imm a constant,
-// which the instruction carries).
-__device__ __forceinline__ uint32_t buf_word(__amdgpu_buffer_rsrc_t r, uint32_t off, int imm) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + (uint32_t)imm), 0, 2 /* nt */);
-}
-// 1 KB units I .. N-1 (16 bytes per lane, lane offset included in vo) from
-// byte offset vo + 1024 I into LDS at dst + 1024 I, non-temporal.  The
-// instruction's constant offset moves the source and the LDS destination
-// alike; it stays below 4 KB, so every fourth unit advances both bases.
-template <int I, int N>
-__device__ __forceinline__ void buf_copy_lds(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t vo) {
-  if constexpr (I < N) {
-    constexpr int HI = (I >> 2) * 4096, LO = (I & 3) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + HI), 16,
-                                             (int)(vo + (uint32_t)HI), 0, LO, 2 /* nt */);
-    buf_copy_lds<I + 1, N>(r, dst, vo);
-  }
-}
-
 // s_waitcnt vmcnt(N): at most N vector memory instructions of this wave still
 // outstanding (loads complete in issue order, so every load issued more than
 // N loads ago has landed).  The copies into LDS (global_load_lds) are waited
