@@ -167,8 +167,8 @@ def cpu_softmax_baseline(rows=1024, T=32768):
             "sample": f"{rows} rows x {T}, {el:.2f} s"}
 
 
-def _time(torch, fn, reps):
-    for _ in range(2):
+def _time(torch, fn, reps, warmup=2):
+    for _ in range(warmup):
         fn()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -198,7 +198,8 @@ def bench_attend(tq, wl, dev):
     q = wl.gaussian_torch((B, Hq, d), 45, dev).view(G, qpg, d).contiguous()
     ws = kctx.workspace(tq.TQ_OP_ATTEND, G, qpg, T, device=dev)
     scale = 1.0 / math.sqrt(d)
-    ms = _time(torch, lambda: tq.tq_attend(kctx, vctx, q, krec, vrec, scale, ws=ws), 10)
+    # steady state: the first calls after setup run measurably slower
+    ms = _time(torch, lambda: tq.tq_attend(kctx, vctx, q, krec, vrec, scale, ws=ws), 50, warmup=20)
     kv_bytes = G * T * (kctx.code_bytes + kctx.sign_bytes + 8 + vctx.code_bytes + 4)
     # the value sum is 4 heads x d fp32 FMAs per token and group; non-packed
     # fp32 VALU peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz FMAs
@@ -215,7 +216,7 @@ def bench_attend(tq, wl, dev):
     nk = wl.gaussian_torch((G, d), 46, dev, torch.bfloat16)
     nv = wl.gaussian_torch((G, d), 47, dev, torch.bfloat16)
     ms_step = _time(torch, lambda: tq.tq_decode_step(kctx, vctx, q, nk, nv, krec, vrec, T - 1, scale,
-                                                     ldk=T, ws=ws), 10)
+                                                     ldk=T, ws=ws), 50, warmup=20)
     r["decode_step_ms"] = ms_step
     r["decode_step_tokens_per_s"] = G * T / (ms_step / 1e3)
     log(f"  decode step (append K and V + attend): {ms_step:.3f} ms")
