@@ -603,11 +603,11 @@ def main():
         for b in (2, 3, 4):
             c2 = tq.Context(d, b, seed=0)
             out = c2.empty_records(1 << 20, dev)
-            for i in range(3):
+            for i in range(10):
                 tq.tq_quantize(c2, Xs[i % 2], out=out)
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
-            reps = 10
+            reps = 30
             for i in range(reps):
                 tq.tq_quantize(c2, Xs[i % 2], out=out)
             e.record()
@@ -633,7 +633,7 @@ def main():
                               ("frac_2.5", tq.TQ_MODE_FRAC, 5), ("frac_3.5", tq.TQ_MODE_FRAC, 7)):
             c2 = tq.Context(d, b, 0, mode)
             out = c2.empty_records(1 << 20, dev)
-            ms = _time(torch, lambda: tq.tq_quantize(c2, Xs[0], out=out), 5)
+            ms = _time(torch, lambda: tq.tq_quantize(c2, Xs[0], out=out), 10, warmup=5)
             vps = (1 << 20) / (ms / 1000.0)
             rec_b = c2.code_bytes + c2.sign_bytes + (8 if c2.sign_bytes else 4)
             io_gbs = (1 << 20) * (2 * d + rec_b) / (ms / 1000.0) / 1e9
