@@ -274,30 +274,47 @@ attend_partial_kernel(AttArgs a) {
     // ---- A: logits of the wave's tokens into LDS
     float lg[2][4];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt) {
+      const float aga = a.alpha * kga[tt];        // alpha gamma, once per token
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         if constexpr (W == 3) {   // first code word of the next lane group (lane + 16), none for the last
           const uint32_t nxt = (uint32_t)__shfl((int)kw[tt][s].cw[0], (lane + 16) & 63);
           kw[tt][s].cw[CB16] = grp < 3 ? nxt : 0u;
         }
-        const float nu = __shfl(knu[tt], 16 * s + col), ga = __shfl(kga[tt], 16 * s + col);
-        lg[tt][s] = tile_logit<CB16, SB16, W>(A, kw[tt][s], nu, ga, a.alpha, hc, pm);
+        const float nu = __shfl(knu[tt], 16 * s + col), ga = __shfl(aga, 16 * s + col);
+        lg[tt][s] = tile_logit<CB16, SB16, W>(A, kw[tt][s], nu, ga, 1.f, hc, pm);
         __asm__ volatile("" : "+v"(lg[tt][s]));
       }
+    }
     // (token indexes fit in 32 bits: the host limits T to 2^31 - CH)
     const int Ti = (int)T, tb32 = c * CH;
     float mz = -INFINITY;
+    if ((c + 1) * CH <= Ti) {
+      // a whole chunk: every token is real
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int t = tb32 + (wv + 4 * tt) * 64 + 16 * s + col;
-        const float z = t < Ti ? a.scale * lg[tt][s] : -INFINITY;
-        L.zt[tt * 64 + 16 * s + col][grp] = z;
-        mz = fmaxf(mz, z);
-        if (a.logits && head < a.qpg && t < Ti) a.logits[(kg * a.qpg + head) * T + t] = lg[tt][s];
-      }
+        for (int s = 0; s < 4; ++s) {
+          const float z = a.scale * lg[tt][s];
+          L.zt[tt * 64 + 16 * s + col][grp] = z;
+          mz = fmaxf(mz, z);
+          if (a.logits && head < a.qpg)
+            a.logits[(kg * a.qpg + head) * T + tb32 + (wv + 4 * tt) * 64 + 16 * s + col] = lg[tt][s];
+        }
+    } else {
+      // the last, partial chunk: tokens past the cache end get -inf
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int t = tb32 + (wv + 4 * tt) * 64 + 16 * s + col;
+          const float z = t < Ti ? a.scale * lg[tt][s] : -INFINITY;
+          L.zt[tt * 64 + 16 * s + col][grp] = z;
+          mz = fmaxf(mz, z);
+          if (a.logits && head < a.qpg && t < Ti) a.logits[(kg * a.qpg + head) * T + t] = lg[tt][s];
+        }
+    }
     const float vnl0 = vn[0], vnl1 = vn[1];
     const bool v0 = tb32 + wv * 64 + lane < Ti, v1 = tb32 + (wv + 4) * 64 + lane < Ti;
     if (c + 1 < c_end) {
