@@ -117,7 +117,7 @@ __device__ __forceinline__ void buf_copy_lds(__amdgpu_buffer_rsrc_t r, uint8_t *
 // states are merged once at the end.  The key words and norms of the wave's
 // next tokens are loaded into registers while the current ones are scored,
 // and the next value records are copied into the wave's LDS slot by the
-// memory system (global_load_lds, 16 bytes per lane) during the next logits.
+// memory system (buffer loads into LDS, 16 bytes per lane) during the next logits.
 #ifndef TQ_ATT_WAVES_PER_EU
 #define TQ_ATT_WAVES_PER_EU 2
 #endif
