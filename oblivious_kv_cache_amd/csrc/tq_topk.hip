@@ -40,7 +40,7 @@ struct TopkGeom {
   int64_t ncand;       // candidates per query
 };
 
-TopkGeom topk_geom(int64_t nq, int64_t n, int k, int nm) {
+TopkGeom topk_geom(int64_t nq, int64_t n, int k, int nm, int cus) {
   TopkGeom g{};
   g.groups = (nq + 3) / 4;
   g.kp = k <= 16 ? 16 : 64;
@@ -51,6 +51,19 @@ TopkGeom topk_geom(int64_t nq, int64_t n, int k, int nm) {
   if (want > tiles) want = tiles;
   if (want > MAX_CHUNKS) want = MAX_CHUNKS;
   if (want < 1) want = 1;
+  // A scan block fills its CU (8 waves at two per SIMD, or 4 at one), so the
+  // blocks run in rounds of `cus`.  From want up to MAX_CHUNKS chunks, take
+  // the count with the fewest rounds per unit of work (the fullest last
+  // round; ties: fewer chunks, less to merge).
+  int64_t best = want, best_rounds = (g.qblocks * want + cus - 1) / cus;
+  for (int64_t nc = want + 1; nc <= MAX_CHUNKS && nc <= tiles; ++nc) {
+    const int64_t rounds = (g.qblocks * nc + cus - 1) / cus;
+    if (rounds * best < best_rounds * nc) {
+      best = nc;
+      best_rounds = rounds;
+    }
+  }
+  want = best;
   g.nchunk = (int)want;
   g.chunk = (tiles + g.nchunk - 1) / g.nchunk * 64;
   g.ncand = (int64_t)g.nchunk * 16 * g.kp;
@@ -458,7 +471,7 @@ TopkGeom topk_block_geom(const tq_ctx *ctx, int64_t nq, int64_t n, int k) {
 
 size_t topk_ws_bytes(const tq_ctx *ctx, int64_t nq, int64_t n, int k) {
   const int nm = mfma_count(ctx->cw16, ctx->sign_bytes / 16, ctx->hp.w);
-  const TopkGeom g = topk_block_path(ctx, k) ? topk_block_geom(ctx, nq, n, k) : topk_geom(nq, n, k, nm);
+  const TopkGeom g = topk_block_path(ctx, k) ? topk_block_geom(ctx, nq, n, k) : topk_geom(nq, n, k, nm, ctx->cus);
   return (size_t)(align256(g.groups * prep_stride(nm)) + 2 * align256(nq * g.ncand * 4));
 }
 
@@ -468,7 +481,7 @@ int launch_topk(const tq_ctx *ctx, const float *q, int64_t nq, int64_t n, const 
   const int cb16 = ctx->cw16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
   const int nm = mfma_count(cb16, sb16, w);
   const bool blk = topk_block_path(ctx, k);
-  const TopkGeom g = blk ? topk_block_geom(ctx, nq, n, k) : topk_geom(nq, n, k, nm);
+  const TopkGeom g = blk ? topk_block_geom(ctx, nq, n, k) : topk_geom(nq, n, k, nm, ctx->cus);
   uint8_t *base = reinterpret_cast<uint8_t *>(ws);
   uint8_t *prep = base;
   float *cand_s = reinterpret_cast<float *>(base + align256(g.groups * prep_stride(nm)));
