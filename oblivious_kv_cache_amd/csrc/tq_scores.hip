@@ -353,8 +353,12 @@ scores_kernel(ScoreArgs a) {
 }
 
 // Two head groups per wave where both groups' operand fragments fit in
-// registers beside the rest (up to 12 MFMAs per 16 keys).
+// registers beside the rest (up to 12 MFMAs per 16 keys); four where the
+// records take at most 6 (codes of 1 or 2 bits at d <= 128): each bit-plane
+// operand then serves four MFMAs (8 groups x 8192 queries x 2048 keys, b=3:
+// 306 -> 275 us, at two waves per SIMD instead of three).
 constexpr int kScoresNQ2MaxNM = 12;
+constexpr int kScoresNQ4MaxNM = 6;
 
 // With events, the dispatch itself records them (hipExtLaunchKernel): they
 // bracket exactly this kernel's execution.
@@ -369,6 +373,9 @@ int launch_one(const ScoreArgs &a, dim3 grid, hipStream_t s, hipEvent_t e0, hipE
 
 template <int C, int S, int W_, bool FRAC = false>
 int launch_geometry(const ScoreArgs &a, dim3 grid, int nq, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if constexpr (ScoreShape<C, S, W_>::NM <= kScoresNQ4MaxNM && !FRAC) {
+    if (nq == 4) return launch_one<C, S, W_, 4, FRAC>(a, grid, s, e0, e1);
+  }
   if constexpr (ScoreShape<C, S, W_>::NM <= kScoresNQ2MaxNM) {
     if (nq == 2) return launch_one<C, S, W_, 2, FRAC>(a, grid, s, e0, e1);
   }
@@ -547,7 +554,8 @@ int launch_scores_prepared(const tq_ctx *ctx, const void *ws, int64_t G, int qpg
   const int hg = (qpg + 3) / 4;
   const int cb16 = ctx->cw16, sb16 = ctx->sign_bytes / 16, w = ctx->hp.w;
   // NQ head groups per wave (2 where it fits); blocks along y: key group x NQ-group block
-  const int nq = hg >= 2 && mfma_count(cb16, sb16, w) <= kScoresNQ2MaxNM ? 2 : 1;
+  const int nmc = mfma_count(cb16, sb16, w);
+  const int nq = hg >= 4 && nmc <= kScoresNQ4MaxNM && !ctx->frac ? 4 : hg >= 2 && nmc <= kScoresNQ2MaxNM ? 2 : 1;
   const int hq = (hg + nq - 1) / nq;
   const int64_t groups = G * hq;
   ScoreArgs sa{};
