@@ -77,10 +77,12 @@ def test_scores_random_records(tq, d, bits, G, qpg, T, ldk):
 
 @pytest.mark.parametrize("d,bits,G,qpg,T,ldk", [
     # many queries per key group (every position of a prefill against one key
-    # set): two head groups per wave, odd head-group counts (the last wave's
-    # second group repeats the first and is not stored), ragged T
+    # set): two or four head groups per wave, head-group counts that leave 1,
+    # 2 or 3 groups in the last wave (its other slots repeat a group and are
+    # not stored), ragged T
     (128, 3, 2, 100, 300, 300), (128, 2, 1, 257, 129, 130), (64, 3, 3, 36, 1000, 1000),
-    (128, 4, 1, 12, 64, 64), (128, 3, 1, 1024, 70, 70),
+    (128, 4, 1, 12, 64, 64), (128, 3, 1, 1024, 70, 70), (128, 2, 2, 28, 257, 260),
+    (64, 3, 1, 40, 190, 190),
     # geometry with more than 12 MFMAs per 16 keys: one head group per wave
     (200, 4, 1, 72, 200, 200),
     # 1024 head groups or more (query prep over many blocks per CU), at
